@@ -1,0 +1,242 @@
+"""Python binding of the dattn C ABI (include/dattn.h).
+
+Argument marshalling only: every computation happens in the HIP kernels of
+``libdattn.so``.  Torch supplies device memory (outputs, workspace) and the
+current HIP stream.  There is no fallback: if the library is missing or a call
+fails, this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdattn.so")
+
+DATTN_F32, DATTN_BF16 = 0, 1
+STATUS = {0: "OK", -1: "EINVAL", -2: "EUNSUPPORTED", -3: "EWORKSPACE", -4: "EHIP"}
+
+EXPORTS = (
+    "decode_attn_gqa", "decode_attn_gqa_workspace",
+    "decode_attn_mla", "decode_attn_mla_workspace",
+    "dsa_indexer_topk", "dsa_indexer_topk_workspace",
+    "dsa_topk", "dsa_topk_workspace",
+    "sparse_mla_attn", "sparse_mla_attn_workspace",
+    "dattn_last_error", "dattn_version",
+    "dattn_profile_enable", "dattn_profile_read", "dattn_profile_reset",
+)
+
+_lib = None
+
+
+class DattnError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"dattn {STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+def lib() -> ctypes.CDLL:
+    """Load libdattn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m decode_attention_kv_flash_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, SZ, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
+    L.decode_attn_gqa.argtypes = [P, P, P, P, P, I32, I32, P, P, I32, I32, I32, I32, I32, I32,
+                                  I32, F, I32, P, SZ, P]
+    L.decode_attn_gqa_workspace.argtypes = [I32] * 9
+    L.decode_attn_mla.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, I32, F, I32,
+                                  P, SZ, P]
+    L.decode_attn_mla_workspace.argtypes = [I32] * 5
+    L.dsa_indexer_topk.argtypes = [P, P, P, P, I32, P, P, I32, I32, I32, I32, I32, P, SZ, P]
+    L.dsa_indexer_topk_workspace.argtypes = [I32] * 3
+    L.dsa_topk.argtypes = [P, P, I32, P, I32, I32, P, SZ, P]
+    L.dsa_topk_workspace.argtypes = [I32] * 3
+    L.sparse_mla_attn.argtypes = [P, P, P, I32, P, P, I32, I32, I32, I32, I32, I32, F, I32, P, SZ, P]
+    L.sparse_mla_attn_workspace.argtypes = [I32] * 5
+    for name in ("decode_attn_gqa_workspace", "decode_attn_mla_workspace",
+                 "dsa_indexer_topk_workspace", "dsa_topk_workspace", "sparse_mla_attn_workspace"):
+        getattr(L, name).restype = SZ
+    for name in ("decode_attn_gqa", "decode_attn_mla", "dsa_indexer_topk", "dsa_topk",
+                 "sparse_mla_attn", "dattn_profile_enable", "dattn_profile_read",
+                 "dattn_profile_reset"):
+        getattr(L, name).restype = ctypes.c_int
+    L.dattn_last_error.restype = ctypes.c_char_p
+    L.dattn_last_error.argtypes = []
+    L.dattn_version.restype = I32
+    L.dattn_profile_enable.argtypes = [I32]
+    L.dattn_profile_read.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
+                                     ctypes.POINTER(ctypes.c_int64)]
+    _lib = L
+    return L
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise DattnError(rc, lib().dattn_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t: torch.Tensor, name: str):
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return DATTN_F32
+    if t.dtype == torch.bfloat16:
+        return DATTN_BF16
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _workspace(nbytes: int, device) -> Optional[torch.Tensor]:
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def decode_attn_gqa(q, k_cache, v_cache, seq_lens, page_table=None, window=0, n_sink=0, *,
+                    scale=None, num_splits=0, out=None, lse=None, want_lse=True, stream=None):
+    """GQA / sliding-window + sinks decode attention.  Returns (out, lse)."""
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (seq_lens, "seq_lens")):
+        _dev(t, n)
+    B, Hq, D = q.shape
+    Hkv = k_cache.shape[1]
+    page_size = k_cache.shape[2]
+    if page_table is not None:
+        _dev(page_table, "page_table")
+        max_pages = page_table.shape[1]
+    else:
+        max_pages = 1
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty(B, Hq, dtype=torch.float32, device=q.device)
+    nbytes = lib().decode_attn_gqa_workspace(B, Hq, Hkv, D, page_size, max_pages, int(window),
+                                             int(n_sink), int(num_splits))
+    ws = _workspace(nbytes, q.device)
+    _check(lib().decode_attn_gqa(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), _ptr(page_table),
+        int(window), int(n_sink), _ptr(out), _ptr(lse), B, Hq, Hkv, D, page_size, max_pages,
+        _dtype_code(q), float(scale or 0.0), int(num_splits), _ptr(ws), nbytes, _stream(stream)))
+    return out, lse
+
+
+def decode_attn_mla(q_absorbed, latent_cache, seq_lens, page_table=None, *, d_latent=512,
+                    scale=None, num_splits=0, out=None, lse=None, want_lse=True, stream=None):
+    """Absorbed MLA decode attention.  latent_cache [B, S_max, 576] (contiguous)
+    or [num_pages, page_size, 576] with page_table.  Returns (out [B,H,512], lse)."""
+    for t, n in ((q_absorbed, "q_absorbed"), (latent_cache, "latent_cache"), (seq_lens, "seq_lens")):
+        _dev(t, n)
+    B, H, Dq = q_absorbed.shape
+    d_rope = Dq - d_latent
+    if page_table is not None:
+        _dev(page_table, "page_table")
+        page_size, max_pages = latent_cache.shape[1], page_table.shape[1]
+        S_max = page_size * max_pages
+    else:
+        S_max, page_size, max_pages = latent_cache.shape[1], latent_cache.shape[1], 1
+    if out is None:
+        out = torch.empty(B, H, d_latent, dtype=q_absorbed.dtype, device=q_absorbed.device)
+    if lse is None and want_lse:
+        lse = torch.empty(B, H, dtype=torch.float32, device=q_absorbed.device)
+    nbytes = lib().decode_attn_mla_workspace(B, H, d_latent, S_max, int(num_splits))
+    ws = _workspace(nbytes, q_absorbed.device)
+    _check(lib().decode_attn_mla(
+        _ptr(q_absorbed), _ptr(latent_cache), _ptr(seq_lens), _ptr(page_table), _ptr(out),
+        _ptr(lse), B, H, d_latent, d_rope, S_max, page_size, max_pages, _dtype_code(q_absorbed),
+        float(scale or 0.0), int(num_splits), _ptr(ws), nbytes, _stream(stream)))
+    return out, lse
+
+
+def dsa_indexer_topk(q_i, w, k_i_cache, seq_lens, k, *, topk_idx=None, return_scores=False,
+                     stream=None):
+    """Indexer scores + top-k.  Returns topk_idx [B,k] (and scores [B,S_max])."""
+    for t, n in ((q_i, "q_i"), (w, "w"), (k_i_cache, "k_i_cache"), (seq_lens, "seq_lens")):
+        _dev(t, n)
+    if w.dtype != torch.float32:
+        raise ValueError("w must be fp32")
+    B, Hi, Di = q_i.shape
+    S_max = k_i_cache.shape[1]
+    if topk_idx is None:
+        topk_idx = torch.empty(B, k, dtype=torch.int32, device=q_i.device)
+    scores = torch.empty(B, S_max, dtype=torch.float32, device=q_i.device) if return_scores else None
+    nbytes = 0 if return_scores else lib().dsa_indexer_topk_workspace(B, S_max, k)
+    ws = _workspace(nbytes, q_i.device)
+    _check(lib().dsa_indexer_topk(
+        _ptr(q_i), _ptr(w), _ptr(k_i_cache), _ptr(seq_lens), int(k), _ptr(topk_idx), _ptr(scores),
+        B, Hi, Di, S_max, _dtype_code(q_i), _ptr(ws), nbytes, _stream(stream)))
+    return (topk_idx, scores) if return_scores else topk_idx
+
+
+def dsa_topk(scores, seq_lens, k, *, topk_idx=None, stream=None):
+    """Top-k of fp32 scores [B, S_max]; ties to the lower index; ascending; -1 padded."""
+    _dev(scores, "scores")
+    _dev(seq_lens, "seq_lens")
+    if scores.dtype != torch.float32:
+        raise ValueError("scores must be fp32")
+    B, S_max = scores.shape
+    if topk_idx is None:
+        topk_idx = torch.empty(B, k, dtype=torch.int32, device=scores.device)
+    nbytes = lib().dsa_topk_workspace(B, S_max, k)
+    ws = _workspace(nbytes, scores.device)
+    _check(lib().dsa_topk(_ptr(scores), _ptr(seq_lens), int(k), _ptr(topk_idx), B, S_max,
+                          _ptr(ws), nbytes, _stream(stream)))
+    return topk_idx
+
+
+def sparse_mla_attn(q, latent_cache, topk_idx, *, d_latent=512, scale=None, num_splits=0,
+                    out=None, lse=None, want_lse=True, stream=None):
+    """MLA over the rows listed in topk_idx [B,k] (-1 = skip).  Returns (out, lse)."""
+    for t, n in ((q, "q"), (latent_cache, "latent_cache"), (topk_idx, "topk_idx")):
+        _dev(t, n)
+    B, H, Dq = q.shape
+    S_max = latent_cache.shape[1]
+    k = topk_idx.shape[1]
+    if out is None:
+        out = torch.empty(B, H, d_latent, dtype=q.dtype, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty(B, H, dtype=torch.float32, device=q.device)
+    nbytes = lib().sparse_mla_attn_workspace(B, H, d_latent, k, int(num_splits))
+    ws = _workspace(nbytes, q.device)
+    _check(lib().sparse_mla_attn(
+        _ptr(q), _ptr(latent_cache), _ptr(topk_idx), k, _ptr(out), _ptr(lse), B, H, d_latent,
+        Dq - d_latent, S_max, _dtype_code(q), float(scale or 0.0), int(num_splits), _ptr(ws),
+        nbytes, _stream(stream)))
+    return out, lse
+
+
+# ---- per-kernel timing (HIP events recorded inside the library) -------------
+
+def profile_enable(on: bool = True):
+    _check(lib().dattn_profile_enable(1 if on else 0))
+
+
+def profile_reset():
+    _check(lib().dattn_profile_reset())
+
+
+def profile_read(name: str = ""):
+    """(total milliseconds, launch count) of kernels whose name contains ``name``."""
+    tot, cnt = ctypes.c_double(0.0), ctypes.c_int64(0)
+    _check(lib().dattn_profile_read(name.encode() if name else None, ctypes.byref(tot),
+                                    ctypes.byref(cnt)))
+    return tot.value, cnt.value

@@ -1,0 +1,444 @@
+// C ABI of the dattn library: argument validation, split planning, workspace
+// carving and kernel launches on the caller's stream.  See include/dattn.h.
+#include "../../include/dattn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "internal.hpp"
+
+namespace {
+
+constexpr int kMaxSplits = 64;
+constexpr int kTopkMax = 16384;
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return DATTN_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(DATTN_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool pow2(int32_t x) { return x > 0 && (x & (x - 1)) == 0; }
+int ilog2(int32_t x) {
+  int r = 0;
+  while ((1 << r) < x) ++r;
+  return r;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// ---------------------------------------------------------------- profiling
+struct ProfRec {
+  const char* name;
+  hipEvent_t start, stop;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRec> g_recs;
+std::vector<hipEvent_t> g_pool;
+
+hipEvent_t pool_get() {
+  if (!g_pool.empty()) {
+    hipEvent_t e = g_pool.back();
+    g_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// ---------------------------------------------------------------- planning
+// Token splits per (sequence, KV head): enough workgroups for 8 per CU on
+// 256 CUs, but no split shorter than 256 tokens.
+int plan_gqa_splits(int32_t B, int32_t Hkv, int64_t max_tokens, int32_t req) {
+  if (req > 0) return req < kMaxSplits ? req : kMaxSplits;
+  const int64_t units = (int64_t)B * Hkv;
+  int64_t want = (2048 + units - 1) / units;
+  int64_t cap = (max_tokens + 255) / 256;
+  if (cap < 1) cap = 1;
+  int64_t n = want < cap ? want : cap;
+  if (n > kMaxSplits) n = kMaxSplits;
+  return n < 1 ? 1 : (int)n;
+}
+
+// MLA workgroups (64 heads each) run one per CU: aim for one full wave of
+// 256 workgroups, splits of at least 128 tokens.
+int plan_mla_splits(int32_t B, int32_t H, int64_t max_tokens, int32_t req) {
+  if (req > 0) return req < kMaxSplits ? req : kMaxSplits;
+  const int64_t units = (int64_t)B * (H / 64);
+  int64_t want = (256 + units - 1) / units;
+  int64_t cap = (max_tokens + 127) / 128;
+  if (cap < 1) cap = 1;
+  int64_t n = want < cap ? want : cap;
+  if (n > kMaxSplits) n = kMaxSplits;
+  return n < 1 ? 1 : (int)n;
+}
+
+// Upper bound on the tokens one sequence attends: the cache capacity
+// page_size * max_pages (contiguous: max_pages = 1), cut by window + sinks.
+int64_t gqa_max_tokens(int32_t page_size, int32_t max_pages, int32_t window, int32_t n_sink) {
+  int64_t cap = (int64_t)page_size * (max_pages < 1 ? 1 : max_pages);
+  if (window > 0 && (int64_t)window + n_sink < cap) cap = (int64_t)window + n_sink;
+  return cap;
+}
+
+size_t split_workspace(int64_t rows, int splits, int D) {
+  if (splits <= 1) return 0;
+  return align256((size_t)rows * splits * D * sizeof(float)) +
+         align256((size_t)rows * splits * sizeof(float));
+}
+
+}  // namespace
+
+namespace dattn {
+
+void prof_begin(const char* name, hipStream_t s) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (!g_prof_on) return;
+  hipEvent_t e = pool_get();
+  if (!e) return;
+  hipEventRecord(e, s);
+  g_recs.push_back({name, e, nullptr});
+}
+
+void prof_end(hipStream_t s) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (!g_prof_on || g_recs.empty() || g_recs.back().stop) return;
+  hipEvent_t e = pool_get();
+  if (!e) return;
+  hipEventRecord(e, s);
+  g_recs.back().stop = e;
+}
+
+}  // namespace dattn
+
+namespace {
+
+template <typename F>
+int launch(const char* name, hipStream_t s, F&& f) {
+  dattn::prof_begin(name, s);
+  hipError_t e = f();
+  dattn::prof_end(s);
+  if (e != hipSuccess) return hip_fail(e, name);
+  return DATTN_OK;
+}
+
+int check_workspace(void* ws, size_t have, size_t need) {
+  if (need == 0) return DATTN_OK;
+  if (!ws) return fail(DATTN_EWORKSPACE, "workspace is NULL but %zu bytes are needed", need);
+  if (have < need)
+    return fail(DATTN_EWORKSPACE, "workspace has %zu bytes, %zu are needed", have, need);
+  if ((uintptr_t)ws % 256 != 0) return fail(DATTN_EWORKSPACE, "workspace must be 256-byte aligned");
+  return DATTN_OK;
+}
+
+int validate_gqa(const void* q, const void* k, const void* v, const int32_t* seq_lens,
+                 const int32_t* page_table, int32_t n_sink, const void* out, int32_t B,
+                 int32_t Hq, int32_t Hkv, int32_t D, int32_t page_size, int32_t max_pages,
+                 int32_t dtype, float scale, int32_t num_splits) {
+  if (!q || !k || !v || !seq_lens || !out) return fail(DATTN_EINVAL, "decode_attn_gqa: NULL pointer argument");
+  if (B < 1 || Hq < 1 || Hkv < 1) return fail(DATTN_EINVAL, "decode_attn_gqa: B, Hq, Hkv must be >= 1");
+  if (B > 65535 || Hkv > 65535) return fail(DATTN_EINVAL, "decode_attn_gqa: B and Hkv must be <= 65535");
+  if (Hq % Hkv != 0) return fail(DATTN_EINVAL, "decode_attn_gqa: Hq (%d) is not a multiple of Hkv (%d)", Hq, Hkv);
+  const int G = Hq / Hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(DATTN_EUNSUPPORTED, "decode_attn_gqa: group size Hq/Hkv = %d not in {1,2,4,8}", G);
+  if (D != 64 && D != 128) return fail(DATTN_EUNSUPPORTED, "decode_attn_gqa: head dim %d not in {64,128}", D);
+  if (dtype != DATTN_F32 && dtype != DATTN_BF16) return fail(DATTN_EUNSUPPORTED, "decode_attn_gqa: dtype %d", dtype);
+  if (page_size < 1) return fail(DATTN_EINVAL, "decode_attn_gqa: page_size must be >= 1");
+  if (page_table) {
+    if (!pow2(page_size)) return fail(DATTN_EUNSUPPORTED, "decode_attn_gqa: paged cache needs a power-of-two page_size, got %d", page_size);
+    if (max_pages < 1) return fail(DATTN_EINVAL, "decode_attn_gqa: max_pages must be >= 1");
+  }
+  if (n_sink < 0) return fail(DATTN_EINVAL, "decode_attn_gqa: n_sink must be >= 0");
+  if (num_splits < 0) return fail(DATTN_EINVAL, "decode_attn_gqa: num_splits must be >= 0");
+  if (std::isnan(scale) || std::isinf(scale)) return fail(DATTN_EINVAL, "decode_attn_gqa: scale is not finite");
+  return DATTN_OK;
+}
+
+int validate_mla_common(const char* fn, const void* q, const void* latent, const void* out, int32_t B,
+                        int32_t H, int32_t d_latent, int32_t d_rope, int32_t S_max, int32_t dtype,
+                        float scale, int32_t num_splits) {
+  if (!q || !latent || !out) return fail(DATTN_EINVAL, "%s: NULL pointer argument", fn);
+  if (B < 1 || H < 1 || S_max < 1) return fail(DATTN_EINVAL, "%s: B, H, S_max must be >= 1", fn);
+  if (B > 65535) return fail(DATTN_EINVAL, "%s: B must be <= 65535", fn);
+  if (d_latent != 512 || d_rope != 64)
+    return fail(DATTN_EUNSUPPORTED, "%s: latent %d + rope %d; only 512 + 64 is built", fn, d_latent, d_rope);
+  if (H % 64 != 0) return fail(DATTN_EUNSUPPORTED, "%s: H = %d is not a multiple of 64", fn, H);
+  if (H / 64 > 65535) return fail(DATTN_EINVAL, "%s: H too large", fn);
+  if (dtype != DATTN_BF16) return fail(DATTN_EUNSUPPORTED, "%s: only bf16 is built", fn);
+  if (num_splits < 0) return fail(DATTN_EINVAL, "%s: num_splits must be >= 0", fn);
+  if (std::isnan(scale) || std::isinf(scale)) return fail(DATTN_EINVAL, "%s: scale is not finite", fn);
+  return DATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dattn_last_error(void) { return g_err.c_str(); }
+
+int32_t dattn_version(void) { return 1; }
+
+int dattn_profile_enable(int32_t on) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_on = on != 0;
+  return ok();
+}
+
+int dattn_profile_reset(void) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  for (auto& r : g_recs) {
+    if (r.start) g_pool.push_back(r.start);
+    if (r.stop) g_pool.push_back(r.stop);
+  }
+  g_recs.clear();
+  return ok();
+}
+
+int dattn_profile_read(const char* name, double* total_ms, int64_t* count) {
+  if (!total_ms || !count) return fail(DATTN_EINVAL, "dattn_profile_read: NULL output");
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  double tot = 0.0;
+  int64_t n = 0;
+  for (auto& r : g_recs) {
+    if (!r.stop || (name && !strstr(r.name, name))) continue;
+    hipError_t e = hipEventSynchronize(r.stop);
+    if (e != hipSuccess) return hip_fail(e, "dattn_profile_read");
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, r.start, r.stop);
+    if (e != hipSuccess) return hip_fail(e, "dattn_profile_read");
+    tot += ms;
+    ++n;
+  }
+  *total_ms = tot;
+  *count = n;
+  return ok();
+}
+
+// ------------------------------------------------------------------- GQA
+
+size_t decode_attn_gqa_workspace(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t page_size,
+                                 int32_t max_pages, int32_t window, int32_t n_sink,
+                                 int32_t num_splits) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || D < 1 || page_size < 1 || num_splits < 0) return 0;
+  const int splits =
+      plan_gqa_splits(B, Hkv, gqa_max_tokens(page_size, max_pages, window, n_sink), num_splits);
+  return split_workspace((int64_t)B * Hq, splits, D);
+}
+
+int decode_attn_gqa(const void* q, const void* k_cache, const void* v_cache, const int32_t* seq_lens,
+                    const int32_t* page_table, int32_t window, int32_t n_sink, void* out, float* lse,
+                    int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t page_size, int32_t max_pages,
+                    int32_t dtype, float scale, int32_t num_splits, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  int rc = validate_gqa(q, k_cache, v_cache, seq_lens, page_table, n_sink, out, B, Hq, Hkv, D,
+                        page_size, max_pages, dtype, scale, num_splits);
+  if (rc) return rc;
+  const bool paged = page_table != nullptr;
+  const int splits = plan_gqa_splits(
+      B, Hkv, gqa_max_tokens(page_size, paged ? max_pages : 1, window, n_sink), num_splits);
+  const size_t need = split_workspace((int64_t)B * Hq, splits, D);
+  if ((rc = check_workspace(workspace, workspace_bytes, need))) return rc;
+
+  dattn::GqaArgs a{};
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.seq_lens = seq_lens;
+  a.page_table = page_table;
+  a.window = window;
+  a.n_sink = n_sink;
+  a.out = out;
+  a.lse = lse;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.D = D;
+  a.G = Hq / Hkv;
+  a.page_size = page_size;
+  a.log2_page = paged ? ilog2(page_size) : 0;
+  a.max_pages = paged ? max_pages : 1;
+  a.num_splits = splits;
+  a.bf16 = dtype == DATTN_BF16;
+  const float sc = scale > 0.f ? scale : 1.0f / std::sqrt((float)D);
+  a.scale_log2 = sc * 1.4426950408889634f;
+  if (splits > 1) {
+    a.part_o = (float*)workspace;
+    a.part_lse = (float*)((char*)workspace + align256((size_t)B * Hq * splits * D * sizeof(float)));
+  }
+  hipStream_t s = (hipStream_t)stream;
+  if ((rc = launch("gqa_split", s, [&] { return dattn::launch_gqa(a, s); }))) return rc;
+  if (splits > 1) {
+    dattn::CombineArgs c{a.part_o, a.part_lse, out, lse, B * Hq, splits, D, a.bf16};
+    if ((rc = launch("lse_combine", s, [&] { return dattn::launch_combine(c, s); }))) return rc;
+  }
+  return ok();
+}
+
+// ------------------------------------------------------------------- MLA
+
+size_t decode_attn_mla_workspace(int32_t B, int32_t H, int32_t d_latent, int32_t S_max,
+                                 int32_t num_splits) {
+  if (B < 1 || H < 64 || d_latent < 1 || S_max < 1 || num_splits < 0) return 0;
+  const int splits = plan_mla_splits(B, H, S_max, num_splits);
+  return split_workspace((int64_t)B * H, splits, d_latent);
+}
+
+static int run_mla(dattn::MlaArgs& a, int splits, float* lse, uint16_t* out, void* workspace,
+                   hipStream_t s, const char* name) {
+  a.num_splits = splits;
+  a.out = out;
+  a.lse = lse;
+  if (splits > 1) {
+    a.part_o = (float*)workspace;
+    a.part_lse = (float*)((char*)workspace + align256((size_t)a.B * a.H * splits * 512 * sizeof(float)));
+  }
+  int rc = launch(name, s, [&] { return dattn::launch_mla(a, s); });
+  if (rc) return rc;
+  if (splits > 1) {
+    dattn::CombineArgs c{a.part_o, a.part_lse, out, lse, a.B * a.H, splits, 512, 1};
+    if ((rc = launch("lse_combine", s, [&] { return dattn::launch_combine(c, s); }))) return rc;
+  }
+  return ok();
+}
+
+int decode_attn_mla(const void* q_absorbed, const void* latent_cache, const int32_t* seq_lens,
+                    const int32_t* page_table, void* out, float* lse, int32_t B, int32_t H,
+                    int32_t d_latent, int32_t d_rope, int32_t S_max, int32_t page_size,
+                    int32_t max_pages, int32_t dtype, float scale, int32_t num_splits,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = validate_mla_common("decode_attn_mla", q_absorbed, latent_cache, out, B, H, d_latent,
+                               d_rope, S_max, dtype, scale, num_splits);
+  if (rc) return rc;
+  if (!seq_lens) return fail(DATTN_EINVAL, "decode_attn_mla: seq_lens is NULL");
+  if (page_table) {
+    if (!pow2(page_size)) return fail(DATTN_EUNSUPPORTED, "decode_attn_mla: paged cache needs a power-of-two page_size");
+    if (max_pages < 1) return fail(DATTN_EINVAL, "decode_attn_mla: max_pages must be >= 1");
+  }
+  const int splits = plan_mla_splits(B, H, S_max, num_splits);
+  if ((rc = check_workspace(workspace, workspace_bytes, split_workspace((int64_t)B * H, splits, 512))))
+    return rc;
+  dattn::MlaArgs a{};
+  a.q = (const uint16_t*)q_absorbed;
+  a.latent = (const uint16_t*)latent_cache;
+  a.seq_lens = seq_lens;
+  a.page_table = page_table;
+  a.B = B;
+  a.H = H;
+  a.S_max = S_max;
+  a.page_size = page_table ? page_size : S_max;
+  a.log2_page = page_table ? ilog2(page_size) : 0;
+  a.max_pages = page_table ? max_pages : 1;
+  const float sc = scale > 0.f ? scale : 1.0f / std::sqrt(192.0f);
+  a.scale_log2 = sc * 1.4426950408889634f;
+  return run_mla(a, splits, lse, (uint16_t*)out, workspace, (hipStream_t)stream, "mla_split");
+}
+
+size_t sparse_mla_attn_workspace(int32_t B, int32_t H, int32_t d_latent, int32_t k, int32_t num_splits) {
+  if (B < 1 || H < 64 || d_latent < 1 || k < 1 || num_splits < 0) return 0;
+  const int splits = plan_mla_splits(B, H, k, num_splits);
+  return split_workspace((int64_t)B * H, splits, d_latent);
+}
+
+int sparse_mla_attn(const void* q, const void* latent_cache, const int32_t* topk_idx, int32_t k,
+                    void* out, float* lse, int32_t B, int32_t H, int32_t d_latent, int32_t d_rope,
+                    int32_t S_max, int32_t dtype, float scale, int32_t num_splits, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  int rc = validate_mla_common("sparse_mla_attn", q, latent_cache, out, B, H, d_latent, d_rope,
+                               S_max, dtype, scale, num_splits);
+  if (rc) return rc;
+  if (!topk_idx) return fail(DATTN_EINVAL, "sparse_mla_attn: topk_idx is NULL");
+  if (k < 1) return fail(DATTN_EINVAL, "sparse_mla_attn: k must be >= 1");
+  const int splits = plan_mla_splits(B, H, k, num_splits);
+  if ((rc = check_workspace(workspace, workspace_bytes, split_workspace((int64_t)B * H, splits, 512))))
+    return rc;
+  dattn::MlaArgs a{};
+  a.q = (const uint16_t*)q;
+  a.latent = (const uint16_t*)latent_cache;
+  a.idx = topk_idx;
+  a.k_sel = k;
+  a.B = B;
+  a.H = H;
+  a.S_max = S_max;
+  a.page_size = S_max;
+  a.max_pages = 1;
+  const float sc = scale > 0.f ? scale : 1.0f / std::sqrt(192.0f);
+  a.scale_log2 = sc * 1.4426950408889634f;
+  return run_mla(a, splits, lse, (uint16_t*)out, workspace, (hipStream_t)stream, "sparse_mla_split");
+}
+
+// ------------------------------------------------------------------- DSA
+
+size_t dsa_topk_workspace(int32_t, int32_t, int32_t) { return 0; }
+
+int dsa_topk(const float* scores, const int32_t* seq_lens, int32_t k, int32_t* topk_idx, int32_t B,
+             int32_t S_max, void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (!scores || !seq_lens || !topk_idx) return fail(DATTN_EINVAL, "dsa_topk: NULL pointer argument");
+  if (B < 1 || S_max < 1) return fail(DATTN_EINVAL, "dsa_topk: B and S_max must be >= 1");
+  if (k < 1 || k > kTopkMax) return fail(DATTN_EINVAL, "dsa_topk: k = %d outside [1, %d]", k, kTopkMax);
+  dattn::TopkArgs t{scores, seq_lens, topk_idx, B, S_max, k};
+  hipStream_t s = (hipStream_t)stream;
+  int rc = launch("topk_select", s, [&] { return dattn::launch_topk(t, s); });
+  return rc ? rc : ok();
+}
+
+size_t dsa_indexer_topk_workspace(int32_t B, int32_t S_max, int32_t k) {
+  (void)k;
+  if (B < 1 || S_max < 1) return 0;
+  return align256((size_t)B * S_max * sizeof(float));
+}
+
+int dsa_indexer_topk(const void* q_i, const float* w, const void* k_i_cache, const int32_t* seq_lens,
+                     int32_t k, int32_t* topk_idx, float* scores_out, int32_t B, int32_t Hi,
+                     int32_t Di, int32_t S_max, int32_t dtype, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  if (!q_i || !w || !k_i_cache || !seq_lens || !topk_idx)
+    return fail(DATTN_EINVAL, "dsa_indexer_topk: NULL pointer argument");
+  if (B < 1 || S_max < 1) return fail(DATTN_EINVAL, "dsa_indexer_topk: B and S_max must be >= 1");
+  if (B > 65535) return fail(DATTN_EINVAL, "dsa_indexer_topk: B must be <= 65535");
+  if (k < 1 || k > kTopkMax) return fail(DATTN_EINVAL, "dsa_indexer_topk: k = %d outside [1, %d]", k, kTopkMax);
+  if (Di != 128) return fail(DATTN_EUNSUPPORTED, "dsa_indexer_topk: Di = %d; only 128 is built", Di);
+  if (Hi != 32 && Hi != 64 && Hi != 96 && Hi != 128)
+    return fail(DATTN_EUNSUPPORTED, "dsa_indexer_topk: Hi = %d not in {32,64,96,128}", Hi);
+  if (dtype != DATTN_BF16) return fail(DATTN_EUNSUPPORTED, "dsa_indexer_topk: only bf16 is built");
+  float* scores = scores_out;
+  if (!scores) {
+    int rc = check_workspace(workspace, workspace_bytes, dsa_indexer_topk_workspace(B, S_max, k));
+    if (rc) return rc;
+    scores = (float*)workspace;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  dattn::IndexerArgs ia{(const uint16_t*)q_i, w, (const uint16_t*)k_i_cache, seq_lens, scores, B, Hi, S_max};
+  int rc = launch("indexer_scores", s, [&] { return dattn::launch_indexer(ia, s); });
+  if (rc) return rc;
+  dattn::TopkArgs t{scores, seq_lens, topk_idx, B, S_max, k};
+  rc = launch("topk_select", s, [&] { return dattn::launch_topk(t, s); });
+  return rc ? rc : ok();
+}
+
+}  // extern "C"

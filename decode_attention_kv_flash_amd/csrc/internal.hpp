@@ -1,0 +1,81 @@
+// Host-side launch interfaces between the C ABI (api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dattn {
+
+// Kernel launch bracketing for per-kernel timing (api.cpp).
+void prof_begin(const char* name, hipStream_t s);
+void prof_end(hipStream_t s);
+
+struct GqaArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* seq_lens;
+  const int32_t* page_table;  // nullptr: contiguous
+  int32_t window, n_sink;
+  void* out;
+  float* lse;
+  float* part_o;    // [B*Hq, num_splits, D]  (num_splits > 1)
+  float* part_lse;  // [B*Hq, num_splits]    (log2 units)
+  int32_t B, Hq, Hkv, D, G;
+  int32_t page_size, log2_page, max_pages, num_splits;
+  int32_t bf16;
+  float scale_log2;  // softmax scale * log2(e)
+};
+
+hipError_t launch_gqa(const GqaArgs& a, hipStream_t s);
+
+struct CombineArgs {
+  const float* part_o;    // [rows, splits, D]
+  const float* part_lse;  // [rows, splits] (log2 units)
+  void* out;              // [rows, D]
+  float* lse;             // [rows] natural log, or nullptr
+  int32_t rows, splits, D;
+  int32_t bf16;
+};
+
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+
+struct MlaArgs {
+  const uint16_t* q;        // [B, H, Dq] bf16
+  const uint16_t* latent;   // paged [pages, P, Dq] or contiguous [B, S_max, Dq]
+  const int32_t* seq_lens;  // dense mode
+  const int32_t* page_table;
+  const int32_t* idx;       // sparse mode: [B, k_sel]
+  int32_t k_sel;
+  uint16_t* out;            // [B, H, Dc] (num_splits == 1)
+  float* lse;
+  float* part_o;
+  float* part_lse;
+  int32_t B, H, S_max, page_size, log2_page, max_pages, num_splits;
+  float scale_log2;
+};
+
+hipError_t launch_mla(const MlaArgs& a, hipStream_t s);
+
+struct IndexerArgs {
+  const uint16_t* q;       // [B, Hi, 128] bf16
+  const float* w;          // [B, Hi]
+  const uint16_t* k;       // [B, S_max, 128] bf16
+  const int32_t* seq_lens;
+  float* scores;           // [B, S_max]
+  int32_t B, Hi, S_max;
+};
+
+hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s);
+
+struct TopkArgs {
+  const float* scores;     // [B, S_max]
+  const int32_t* seq_lens;
+  int32_t* idx;            // [B, k]
+  int32_t B, S_max, k;
+};
+
+hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
+
+}  // namespace dattn

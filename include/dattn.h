@@ -1,0 +1,224 @@
+/*
+ * dattn -- single-token decode attention over a KV cache, for AMD MI355X (gfx950).
+ *
+ * C ABI.  Every entry point takes plain pointers and sizes; device pointers
+ * are HIP device addresses, `stream` is a hipStream_t passed as void*
+ * (NULL = the null stream).  The library:
+ *   - never allocates or frees device memory and keeps no pointer past return:
+ *     the caller owns every buffer, including the workspace;
+ *   - validates the host-side arguments before launching anything; a failure
+ *     returns a negative dattn_status and dattn_last_error() explains it
+ *     (thread-local message); nothing is printed and nothing is launched;
+ *   - launches its kernels asynchronously on `stream` and never synchronises;
+ *     outputs are valid once the stream reaches that point;
+ *   - fully overwrites every output (never accumulates into it).
+ * Contents of device-resident index arrays (seq_lens, page_table, topk_idx)
+ * are a caller contract: they are not read on the host, so calls can be
+ * captured into graphs.
+ *
+ * Layouts (all row-major, no strides):
+ *   KV page:     [num_pages, n_kv_heads, page_size, head_dim]  (K and V alike)
+ *   page table:  int32 [B, max_pages], logical page j of sequence b at
+ *                physical page page_table[b*max_pages + j]; token t lives in
+ *                slot t % page_size of logical page t / page_size.
+ *   contiguous:  page_table == NULL means one page per sequence:
+ *                [B, n_kv_heads, page_size, head_dim] with page_size = S_max.
+ *   latent row:  [c_KV (d_latent) | k_pe (d_rope)], 576 values for DeepSeek-V3.
+ *
+ * Numerics: scores, softmax and accumulation in fp32; bf16 outputs are rounded
+ * to nearest even; lse is the natural-log log-sum-exp of the scaled scores.
+ * An empty token set yields a zero output row and lse = -inf.
+ */
+#ifndef DATTN_H
+#define DATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define DATTN_EXPORT __attribute__((visibility("default")))
+#else
+#define DATTN_EXPORT
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { DATTN_F32 = 0, DATTN_BF16 = 1 } dattn_dtype;
+
+typedef enum {
+  DATTN_OK = 0,
+  DATTN_EINVAL = -1,        /* malformed argument (null pointer, bad size, bad ratio) */
+  DATTN_EUNSUPPORTED = -2,  /* well-formed but not built: head dim, dtype, group size */
+  DATTN_EWORKSPACE = -3,    /* workspace missing or smaller than the *_workspace() size */
+  DATTN_EHIP = -4           /* a HIP call or kernel launch failed */
+} dattn_status;
+
+/* ------------------------------------------------------------------------ */
+/* Grouped-query decode attention, with optional sliding window and sinks.
+ *
+ * Computes, for every sequence b and query head h, softmax(scale * q K^T) V
+ * over the token set T_b of the one new query token, where query head h
+ * reads KV head h / (Hq / Hkv) -- the head sharing of GQA ("All the
+ * attentions", section 2 GQA; "Overview of Attention Mechanism", GQA, 分组机制:
+ * one KV head is MQA, Hkv = Hq is MHA).  L_b = seq_lens[b] counts the cached
+ * tokens, the current one included.
+ *   window <= 0:  T_b = [0, L_b)  (full attention).
+ *   window  > 0:  T_b = [0, min(n_sink, L_b)) u [L_b - window, L_b): the last
+ *                 `window` tokens ("All the attentions", section 4, Sliding
+ *                 Window) plus the first n_sink attention sinks ("Attention
+ *                 Optimizations", "Attention sinks"); a union, never counted
+ *                 twice; window >= L_b is full attention.
+ * Tokens outside T_b are skipped, not masked: they are never loaded.
+ * The cache is paged as described above (PagedAttention block table, "All
+ * the attentions", section 8); physical pages may be shared between
+ * sequences (read-only aliasing is allowed).
+ *
+ *   q          [B, Hq, D]                   dtype
+ *   k_cache    [num_pages, Hkv, page_size, D] dtype
+ *   v_cache    same layout as k_cache
+ *   seq_lens   int32 [B], 0 <= L_b <= page_size * max_pages
+ *   page_table int32 [B, max_pages] or NULL (contiguous, page_size = S_max)
+ *   out        [B, Hq, D] dtype (written)
+ *   lse        fp32 [B, Hq] or NULL
+ *   dtype      DATTN_F32 or DATTN_BF16; D in {64, 128}; Hq / Hkv in {1,2,4,8}
+ *   page_size  paged: a power of two >= 1; contiguous: S_max
+ *   scale      softmax scale; <= 0 means 1/sqrt(D)
+ *   num_splits token-range splits per (sequence, KV head); 0 = automatic.
+ *              Partial results are merged by log-sum-exp in a second kernel.
+ *   workspace  device memory of at least decode_attn_gqa_workspace(...) bytes
+ *              (may be NULL when that size is 0)
+ */
+DATTN_EXPORT int decode_attn_gqa(const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* seq_lens, const int32_t* page_table,
+                    int32_t window, int32_t n_sink,
+                    void* out, float* lse,
+                    int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                    int32_t page_size, int32_t max_pages, int32_t dtype, float scale,
+                    int32_t num_splits, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/* Workspace bytes decode_attn_gqa needs for these sizes (0 if none); pass
+ * max_pages = 1 for a contiguous cache. */
+DATTN_EXPORT size_t decode_attn_gqa_workspace(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                 int32_t page_size, int32_t max_pages, int32_t window,
+                                 int32_t n_sink, int32_t num_splits);
+
+/* ------------------------------------------------------------------------ */
+/* Absorbed MLA decode attention over a latent cache.
+ *
+ * For each sequence b and head h: s_t = scale * q_absorbed[b,h] . row_t over
+ * all d_latent + d_rope values of the cached row, softmax over t in
+ * [0, seq_lens[b]), output = sum_t p_t row_t[0:d_latent].  The query is the
+ * absorbed one, [W_UK^T q_nope ; q_pe] ("Overview of Attention Mechanism",
+ * MLA, Method: W_UK folds into the query and W_UV into the output
+ * projection), and the cached row is cat(c_KV, k_pe) ("Attention
+ * Optimizations", "DSA: DeepSeek Sparse Attention", "Computation Path").
+ *
+ *   q_absorbed   [B, H, d_latent + d_rope] bf16
+ *   latent_cache [num_pages, page_size, d_latent + d_rope] bf16, or contiguous
+ *                [B, S_max, d_latent + d_rope] when page_table == NULL
+ *   seq_lens     int32 [B], 0 <= L_b <= S_max
+ *   page_table   int32 [B, max_pages] or NULL
+ *   out          [B, H, d_latent] bf16 (written);  lse fp32 [B, H] or NULL
+ *   d_latent 512, d_rope 64, H a multiple of 64, dtype DATTN_BF16 only
+ *   S_max        contiguous: rows per sequence; paged: page_size * max_pages
+ *   page_size    paged: a power of two; ignored when page_table == NULL
+ *   scale        <= 0 means 1/sqrt(192) (DeepSeek-V3: 128 + 64 qk dims)
+ *   num_splits   0 = automatic
+ */
+DATTN_EXPORT int decode_attn_mla(const void* q_absorbed, const void* latent_cache,
+                    const int32_t* seq_lens, const int32_t* page_table,
+                    void* out, float* lse,
+                    int32_t B, int32_t H, int32_t d_latent, int32_t d_rope,
+                    int32_t S_max, int32_t page_size, int32_t max_pages,
+                    int32_t dtype, float scale, int32_t num_splits,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+DATTN_EXPORT size_t decode_attn_mla_workspace(int32_t B, int32_t H, int32_t d_latent, int32_t S_max,
+                                 int32_t num_splits);
+
+/* ------------------------------------------------------------------------ */
+/* DSA lightning indexer followed by top-k selection.
+ *
+ * scores[b,t] = sum_h w[b,h] * ReLU(q_i[b,h] . k_i[b,t]) for t < seq_lens[b]
+ * ("Attention Optimizations", "DSA: DeepSeek Sparse Attention", "Computation
+ * Path": per-head indexer products mixed by a per-head weight; the ReLU and
+ * the sum over heads are the reading this library implements), then the k
+ * largest scores of each sequence, ties to the lower token index, written in
+ * ascending index order; when k > seq_lens[b] the tail is -1.  The caller
+ * folds any positive constant (such as n_heads^-0.5) into w.
+ *
+ *   q_i        [B, Hi, Di] bf16;  w fp32 [B, Hi];  k_i_cache [B, S_max, Di] bf16
+ *   seq_lens   int32 [B], 0 <= L_b <= S_max
+ *   k          1 <= k <= 16384
+ *   topk_idx   int32 [B, k] (written)
+ *   scores_out fp32 [B, S_max] or NULL; when given, receives the scores
+ *              (entries t >= seq_lens[b] are -inf)
+ *   Hi a multiple of 32 (<= 128), Di = 128, dtype DATTN_BF16
+ * Integer-valued inputs with |sum| < 2^24 give exact scores and therefore an
+ * exact, reproducible selection.
+ */
+DATTN_EXPORT int dsa_indexer_topk(const void* q_i, const float* w, const void* k_i_cache,
+                     const int32_t* seq_lens, int32_t k, int32_t* topk_idx, float* scores_out,
+                     int32_t B, int32_t Hi, int32_t Di, int32_t S_max, int32_t dtype,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+DATTN_EXPORT size_t dsa_indexer_topk_workspace(int32_t B, int32_t S_max, int32_t k);
+
+/* The selection step alone, on caller-provided fp32 scores [B, S_max]:
+ * the k largest of scores[b, 0:seq_lens[b]], ties to the lower index,
+ * ascending, -1 padded.  -0.0 and +0.0 are equal; NaN scores are not
+ * supported (their position in the order is unspecified).  1 <= k <= 16384. */
+DATTN_EXPORT int dsa_topk(const float* scores, const int32_t* seq_lens, int32_t k, int32_t* topk_idx,
+             int32_t B, int32_t S_max, void* workspace, size_t workspace_bytes, void* stream);
+
+DATTN_EXPORT size_t dsa_topk_workspace(int32_t B, int32_t S_max, int32_t k);
+
+/* ------------------------------------------------------------------------ */
+/* Sparse MLA: absorbed MLA decode attention over only the selected rows.
+ *
+ * Same arithmetic as decode_attn_mla, over the token set
+ * { topk_idx[b, j] : 0 <= j < k, topk_idx[b, j] >= 0 } (gather of the
+ * selected latent rows, "Attention Optimizations", "Computation Path");
+ * entries equal to -1 are skipped; an index listed twice counts twice.
+ *
+ *   q            [B, H, d_latent + d_rope] bf16
+ *   latent_cache [B, S_max, d_latent + d_rope] bf16
+ *   topk_idx     int32 [B, k], each entry -1 or in [0, S_max)
+ *   out          [B, H, d_latent] bf16;  lse fp32 [B, H] or NULL
+ */
+DATTN_EXPORT int sparse_mla_attn(const void* q, const void* latent_cache, const int32_t* topk_idx, int32_t k,
+                    void* out, float* lse,
+                    int32_t B, int32_t H, int32_t d_latent, int32_t d_rope, int32_t S_max,
+                    int32_t dtype, float scale, int32_t num_splits,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+DATTN_EXPORT size_t sparse_mla_attn_workspace(int32_t B, int32_t H, int32_t d_latent, int32_t k,
+                                 int32_t num_splits);
+
+/* ------------------------------------------------------------------------ */
+/* Diagnostics. */
+
+/* Message describing the last failure on this thread ("" if none). */
+DATTN_EXPORT const char* dattn_last_error(void);
+
+/* ABI version of this library. */
+DATTN_EXPORT int32_t dattn_version(void);
+
+/* Per-kernel timing.  While enabled, every kernel the library launches is
+ * bracketed by HIP events recorded on the launch stream.  dattn_profile_read
+ * waits for the recorded events and reports, for kernels whose name contains
+ * `name`, the summed duration in milliseconds and the launch count.
+ * dattn_profile_reset drops all records.  Timing adds two event records per
+ * launch and is meant for benchmarks, not production. */
+DATTN_EXPORT int dattn_profile_enable(int32_t on);
+DATTN_EXPORT int dattn_profile_read(const char* name, double* total_ms, int64_t* count);
+DATTN_EXPORT int dattn_profile_reset(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DATTN_H */

@@ -1,0 +1,128 @@
+"""The C-ABI library: it loads, exports what include/dattn.h declares, and
+rejects malformed arguments on the host before any HIP call (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from decode_attention_kv_flash_amd import api
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    with open(os.path.join(ROOT, "include", "dattn.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"DATTN_EXPORT\s+[\w\s\*]+?\b(\w+)\s*\(", text)))
+
+
+def test_header_declares_the_four_entry_points():
+    syms = declared_symbols()
+    for name in ("decode_attn_gqa", "decode_attn_mla", "dsa_indexer_topk", "sparse_mla_attn"):
+        assert name in syms
+
+
+def test_library_exports_every_declared_symbol():
+    L = api.lib()
+    for name in declared_symbols():
+        assert hasattr(L, name), name
+    assert set(declared_symbols()) == set(api.EXPORTS)
+    assert L.dattn_version() == 1
+
+
+def _gqa(**kw):
+    args = dict(q=1, k=1, v=1, seq_lens=1, page_table=None, window=0, n_sink=0, out=1, lse=None,
+                B=2, Hq=8, Hkv=2, D=128, page_size=16, max_pages=4, dtype=1, scale=0.0,
+                num_splits=0, ws=None, ws_bytes=0)
+    args.update(kw)
+    P = lambda x: None if x is None else ctypes.c_void_p(x)
+    return api.lib().decode_attn_gqa(
+        P(args["q"]), P(args["k"]), P(args["v"]), P(args["seq_lens"]), P(args["page_table"]),
+        args["window"], args["n_sink"], P(args["out"]), P(args["lse"]), args["B"], args["Hq"],
+        args["Hkv"], args["D"], args["page_size"], args["max_pages"], args["dtype"],
+        args["scale"], args["num_splits"], P(args["ws"]), args["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1),
+    (dict(seq_lens=None), -1),
+    (dict(out=None), -1),
+    (dict(B=0), -1),
+    (dict(Hq=6, Hkv=4), -1),          # not a multiple
+    (dict(Hq=48, Hkv=2), -2),         # group 24 not built
+    (dict(D=96), -2),
+    (dict(dtype=7), -2),
+    (dict(page_table=1, page_size=24), -2),  # paged needs power-of-two pages
+    (dict(page_table=1, max_pages=0), -1),
+    (dict(n_sink=-1), -1),
+    (dict(num_splits=-3), -1),
+    (dict(scale=float("nan")), -1),
+    (dict(page_table=1, num_splits=8), -3),  # 8 splits need a workspace
+])
+def test_gqa_validation(kw, code):
+    rc = _gqa(**kw)
+    assert rc == code, api.lib().dattn_last_error()
+    assert api.lib().dattn_last_error()
+
+
+def test_gqa_workspace_sizes():
+    L = api.lib()
+    # one split: no workspace
+    assert L.decode_attn_gqa_workspace(2, 4, 2, 64, 256, 1, 0, 0, 1) == 0
+    # explicit 8 splits on 16 x 32 heads x 128: o and lse partials, 256-aligned
+    n = L.decode_attn_gqa_workspace(16, 32, 8, 128, 16, 512, 0, 0, 8)
+    assert n == 16 * 32 * 8 * 128 * 4 + 16 * 32 * 8 * 4
+    # window + sinks cap the planned splits below the cache capacity
+    full = L.decode_attn_gqa_workspace(32, 32, 8, 128, 16, 2048, 0, 0, 0)
+    win = L.decode_attn_gqa_workspace(32, 32, 8, 128, 16, 2048, 64, 4, 0)
+    assert win <= full
+
+
+def test_mla_and_sparse_validation():
+    L = api.lib()
+    P = ctypes.c_void_p
+    # bad latent width
+    rc = L.decode_attn_mla(P(1), P(1), P(1), None, P(1), None, 2, 128, 256, 64, 100, 100, 1, 1,
+                           0.0, 0, None, 0, None)
+    assert rc == -2
+    # fp32 MLA is not built
+    rc = L.decode_attn_mla(P(1), P(1), P(1), None, P(1), None, 2, 128, 512, 64, 100, 100, 1, 0,
+                           0.0, 0, None, 0, None)
+    assert rc == -2
+    # heads not a multiple of 64
+    rc = L.decode_attn_mla(P(1), P(1), P(1), None, P(1), None, 2, 96, 512, 64, 100, 100, 1, 1,
+                           0.0, 0, None, 0, None)
+    assert rc == -2
+    # sparse: k must be >= 1 and idx non-null
+    rc = L.sparse_mla_attn(P(1), P(1), None, 16, P(1), None, 2, 128, 512, 64, 100, 1, 0.0, 0,
+                           None, 0, None)
+    assert rc == -1
+    rc = L.sparse_mla_attn(P(1), P(1), P(1), 0, P(1), None, 2, 128, 512, 64, 100, 1, 0.0, 0,
+                           None, 0, None)
+    assert rc == -1
+
+
+def test_dsa_validation():
+    L = api.lib()
+    P = ctypes.c_void_p
+    args = lambda **kw: dict(dict(k=2048, Hi=64, Di=128, dt=1), **kw)
+    def call(a, scores=None, ws=None, ws_bytes=0):
+        return L.dsa_indexer_topk(P(1), P(1), P(1), P(1), a["k"], P(1), scores, 8, a["Hi"],
+                                  a["Di"], 65536, a["dt"], ws, ws_bytes, None)
+    assert call(args(k=0)) == -1
+    assert call(args(k=20000)) == -1
+    assert call(args(Di=64)) == -2
+    assert call(args(Hi=48)) == -2
+    assert call(args(dt=0)) == -2
+    assert call(args()) == -3                     # no scores buffer, no workspace
+    assert L.dsa_indexer_topk_workspace(8, 65536, 2048) == 8 * 65536 * 4
+    assert L.dsa_topk(P(1), P(1), 0, P(1), 8, 100, None, 0, None) == -1
+    assert L.dsa_topk(None, P(1), 4, P(1), 8, 100, None, 0, None) == -1
+
+
+def test_profile_calls_without_gpu():
+    api.profile_enable(True)
+    api.profile_reset()
+    assert api.profile_read("gqa") == (0.0, 0)
+    api.profile_enable(False)

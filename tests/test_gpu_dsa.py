@@ -1,0 +1,123 @@
+"""DSA indexer, top-k select and sparse MLA on the GPU against the oracle.
+
+Indexer inputs are integer-valued, so scores are exact on both sides and the
+selected index sets must match bit for bit (ties to the lower index).
+"""
+import pytest
+import torch
+
+import oracle
+from decode_attention_kv_flash_amd import api
+from decode_attention_kv_flash_amd import workloads as wl
+from _helpers import TOL_BF16, assert_lse_close, assert_rows_close, dev, rows_sample, say
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_indexer(x, k):
+    idx, scores = api.dsa_indexer_topk(dev(x.q_i), dev(x.w), dev(x.k_i), dev(x.seq_lens), k,
+                                       return_scores=True)
+    torch.cuda.synchronize()
+    return idx.cpu(), scores.cpu()
+
+
+def check_indexer(x, k):
+    say(f"[dsa] indexer B={x.B} Hi={x.q_i.shape[1]} lens={x.seq_lens.tolist()[:4]} k={k}")
+    idx, scores = gpu_indexer(x, k)
+    want = oracle.indexer(x.q_i, x.w, x.k_i, x.seq_lens)
+    for b, L in enumerate(x.seq_lens.tolist()):
+        assert torch.equal(scores[b, :L].double(), want[b, :L].double()), f"scores row {b}"
+        assert torch.all(torch.isinf(scores[b, L:]))
+    want_idx = oracle.topk(want, x.seq_lens, k)
+    assert torch.equal(idx, want_idx)
+    return idx, want_idx
+
+
+@pytest.mark.parametrize("Hi", [32, 64, 128])
+def test_indexer_small(Hi):
+    x = wl.make_dsa(B=3, seq_lens=[5, 700, 3001], Hi=Hi, topk=64, H=64, seed=51)
+    check_indexer(x, 64)
+
+
+@pytest.mark.parametrize("k", [1, 16, 2048, 5000])
+def test_indexer_topk_sizes(k):
+    x = wl.make_dsa(B=2, seq_lens=[4096, 2500], topk=k, H=64, seed=52)
+    check_indexer(x, k)
+
+
+def test_indexer_hand_worked_example():
+    """The golden tiny example, padded to the built head width (extra heads weigh 0)."""
+    import json, os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "indexer_tiny.json")))
+    q = torch.zeros(1, 32, 128, dtype=torch.bfloat16)
+    q[0, :2, :3] = torch.tensor(g["q_i"], dtype=torch.bfloat16)
+    w = torch.zeros(1, 32)
+    w[0, :2] = torch.tensor(g["w"], dtype=torch.float32)
+    k = torch.zeros(1, 5, 128, dtype=torch.bfloat16)
+    k[0, :, :3] = torch.tensor(g["k_i"], dtype=torch.bfloat16)
+    for kk, want in g["topk"].items():
+        idx, sc = api.dsa_indexer_topk(dev(q), dev(w), dev(k), dev(torch.tensor([5], dtype=torch.int32)),
+                                       int(kk), return_scores=True)
+        assert sc.cpu()[0].tolist() == g["scores"]
+        assert idx.cpu()[0].tolist() == want
+
+
+@pytest.mark.parametrize("n_distinct", [None, 3, 50])
+@pytest.mark.parametrize("k", [1, 100, 2048])
+def test_topk_alone(n_distinct, k):
+    lens = [0, 1, 99, 100, 2048, 2049, 65536]
+    s = wl.make_scores(B=len(lens), seq_lens=lens, n_distinct=n_distinct, seed=k)
+    sl = torch.tensor(lens, dtype=torch.int32)
+    got = api.dsa_topk(dev(s), dev(sl), k).cpu()
+    want = oracle.topk(s, sl, k)
+    assert torch.equal(got, want)
+
+
+def test_topk_run_to_run_identical():
+    s = wl.make_scores(B=4, seq_lens=[30000] * 4, n_distinct=7, seed=9)
+    sl = torch.tensor([30000] * 4, dtype=torch.int32)
+    a = api.dsa_topk(dev(s), dev(sl), 2048).cpu()
+    b = api.dsa_topk(dev(s), dev(sl), 2048).cpu()
+    assert torch.equal(a, b)
+
+
+def run_sparse(m, idx, num_splits=0):
+    out, lse = api.sparse_mla_attn(dev(m.q), dev(m.latent), dev(idx), scale=m.scale,
+                                   num_splits=num_splits)
+    torch.cuda.synchronize()
+    return out.float().cpu().reshape(-1, 512), lse.cpu().reshape(-1)
+
+
+@pytest.mark.parametrize("splits", [0, 1, 5])
+def test_sparse_mla_random_indices(splits):
+    m = wl.make_mla(B=3, H=128, seq_lens=[50, 4000, 3000], seed=53, name="sparse")
+    idx = wl.random_topk_indices(B=3, seq_lens=[50, 4000, 3000], k=256, seed=5, pad_fraction=0.1)
+    got, glse = run_sparse(m, idx, splits)
+    want, wlse = oracle.mla(m.q, m.latent, idx=idx, scale=m.scale)
+    assert_rows_close(got, want, TOL_BF16, "sparse")
+    assert_lse_close(glse, wlse, 1e-5, "sparse")
+
+
+def test_sparse_with_all_tokens_equals_dense():
+    m = wl.make_mla(B=2, H=64, seq_lens=[256, 256], seed=54)
+    idx = torch.arange(256, dtype=torch.int32).repeat(2, 1)
+    sp, _ = run_sparse(m, idx, 2)
+    de, _ = api.decode_attn_mla(dev(m.q), dev(m.latent), dev(m.seq_lens), scale=m.scale, num_splits=2)
+    assert oracle.rel_err_rows(sp, de.float().cpu().reshape(-1, 512)) <= 1e-6
+
+
+@pytest.fixture(scope="module")
+def cfg5():
+    say("[dsa] generating DSA decode: B8, 65536 tokens, indexer 64x128, top-2048, 128-head MLA")
+    return wl.config5_dsa()
+
+
+def test_config5_full_pipeline(cfg5):
+    x = cfg5
+    idx, want_idx = check_indexer(x, x.topk)
+    m = x.mla
+    got, glse = run_sparse(m, dev(idx))
+    rows = rows_sample(m.B * m.H, 48, seed=5)
+    want, wlse = oracle.mla(m.q, m.latent, idx=want_idx, scale=m.scale, rows=rows)
+    assert_rows_close(got[rows], want, TOL_BF16, "config5 sparse")
+    assert_lse_close(glse[rows], wlse, 1e-5, "config5 sparse")

@@ -1,0 +1,161 @@
+"""GQA and sliding-window + sinks decode attention on the GPU against the oracle."""
+import pytest
+import torch
+
+import oracle
+from decode_attention_kv_flash_amd import api
+from decode_attention_kv_flash_amd import workloads as wl
+from _helpers import (TOL_BF16, TOL_F32, assert_lse_close, assert_rows_close, dev, rows_sample,
+                      say, tol_for)
+
+pytestmark = pytest.mark.gpu
+
+
+def run_gpu(x, num_splits=0):
+    out, lse = api.decode_attn_gqa(dev(x.q), dev(x.k_cache), dev(x.v_cache), dev(x.seq_lens),
+                                   dev(x.page_table), x.window, x.n_sink, scale=x.scale,
+                                   num_splits=num_splits)
+    torch.cuda.synchronize()
+    return out.float().cpu().reshape(-1, x.D), lse.cpu().reshape(-1)
+
+
+def check_full(x, num_splits=0):
+    say(f"[gqa] {x.name or 'case'} B={x.B} Hq={x.Hq} Hkv={x.Hkv} D={x.D} lens={x.seq_lens.tolist()[:6]} "
+        f"window={x.window} sinks={x.n_sink} splits={num_splits}")
+    got, glse = run_gpu(x, num_splits)
+    want, wlse = oracle.gqa(x.q, x.k, x.v, x.seq_lens, window=x.window, n_sink=x.n_sink,
+                            scale=x.scale)
+    tol = tol_for(x.q.dtype)
+    err = assert_rows_close(got, want, tol, x.name)
+    assert_lse_close(glse, wlse, 1e-5, x.name)
+    return err
+
+
+def test_tiny_gqa_fp32_config():
+    """B2, 4 q heads / 2 KV heads, D64, 256 tokens, contiguous, fp32: tolerance 1e-5."""
+    x = wl.config1_tiny_gqa()
+    for splits in (0, 1, 2, 4, 7):
+        err = check_full(x, splits)
+        assert err <= TOL_F32
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,dtype,paged", [
+    (32, 8, 128, torch.bfloat16, True),
+    (8, 8, 64, torch.bfloat16, True),     # MHA
+    (8, 1, 128, torch.bfloat16, False),   # MQA
+    (16, 2, 64, torch.float32, True),     # G = 8
+    (4, 2, 128, torch.float32, False),
+    (6, 3, 64, torch.bfloat16, True),     # G = 2, odd head counts
+])
+@pytest.mark.parametrize("splits", [0, 1, 3])
+def test_gqa_ragged(Hq, Hkv, D, dtype, paged, splits):
+    x = wl.make_gqa(B=4, Hq=Hq, Hkv=Hkv, D=D, seq_lens=[1, 17, 300, 1029], dtype=dtype,
+                    page_size=16, paged=paged, seed=21, name=f"ragged_{Hq}_{Hkv}_{D}")
+    check_full(x, splits)
+
+
+@pytest.mark.parametrize("page_size", [1, 4, 32, 64])
+def test_gqa_page_sizes(page_size):
+    x = wl.make_gqa(B=3, Hq=8, Hkv=2, D=128, seq_lens=[5, 129, 700], page_size=page_size,
+                    seed=22, name=f"pages{page_size}")
+    check_full(x)
+
+
+@pytest.mark.parametrize("window,n_sink,lens", [
+    (64, 4, [1, 4, 60, 64, 65, 68, 69, 1000]),   # window >= L, sinks inside / overlapping / apart
+    (16, 0, [15, 16, 17, 500]),
+    (1, 3, [1, 2, 3, 4, 100]),
+    (100, 4, [2000, 3333]),
+])
+@pytest.mark.parametrize("splits", [0, 2])
+def test_window_and_sinks(window, n_sink, lens, splits):
+    x = wl.make_gqa(B=len(lens), Hq=8, Hkv=2, D=128, seq_lens=lens, window=window, n_sink=n_sink,
+                    sink_key_scale=4.0, seed=23, name=f"swa{window}_s{n_sink}")
+    check_full(x, splits)
+
+
+def test_empty_sequences():
+    x = wl.make_gqa(B=3, Hq=8, Hkv=2, D=64, seq_lens=[0, 7, 0], seed=24, name="empty")
+    got, lse = run_gpu(x)
+    got = got.view(3, 8, 64)
+    assert torch.all(got[0] == 0) and torch.all(got[2] == 0)
+    lse = lse.view(3, 8)
+    assert torch.all(torch.isinf(lse[0])) and torch.all(lse[0] < 0)
+    check_full(x)
+
+
+def test_window_of_whole_cache_equals_full_attention():
+    full = wl.make_gqa(B=2, Hq=8, Hkv=2, D=128, seq_lens=[300, 301], seed=25)
+    o_full, _ = run_gpu(full)
+    full.window, full.n_sink = 301, 4
+    o_win, _ = run_gpu(full)
+    assert torch.equal(o_full, o_win)
+
+
+def test_paged_equals_contiguous_bitwise():
+    """Paging does not change the output ("All the attentions", section 8)."""
+    p = wl.make_gqa(B=2, Hq=8, Hkv=2, D=128, seq_lens=[512, 512], page_size=16, paged=True, seed=26)
+    c = wl.make_gqa(B=2, Hq=8, Hkv=2, D=128, seq_lens=[512, 512], paged=False, seed=26)
+    assert torch.equal(p.k, c.k)
+    op, _ = run_gpu(p, 4)
+    oc, _ = run_gpu(c, 4)
+    assert torch.equal(op, oc)
+
+
+def test_aliased_pages():
+    """Several sequences may point at the same physical pages (copy-on-write prefixes)."""
+    x = wl.make_gqa(B=2, Hq=8, Hkv=2, D=128, seq_lens=[64, 64], page_size=16, seed=27)
+    x.page_table[1] = x.page_table[0]
+    x.k[1] = x.k[0]
+    x.v[1] = x.v[0]
+    got, _ = run_gpu(x)
+    got = got.view(2, 8, 128)
+    want, _ = oracle.gqa(x.q, x.k, x.v, x.seq_lens)
+    assert_rows_close(got.reshape(-1, 128), want, TOL_BF16)
+
+
+def test_deterministic():
+    x = wl.make_gqa(B=2, Hq=32, Hkv=8, D=128, seq_lens=[999, 2048], seed=28)
+    a, _ = run_gpu(x)
+    b, _ = run_gpu(x)
+    assert torch.equal(a, b)
+
+
+# --- full-size workloads, sampled rows, in the launch configuration the benchmark times ---
+
+@pytest.fixture(scope="module")
+def cfg2():
+    say("[gqa] generating Llama-3-8B-shaped layer: B16 32/8 heads D128 8192 tokens paged16")
+    return wl.config2_llama3_8b_gqa()
+
+
+def test_config2_full_size_sampled(cfg2):
+    x = cfg2
+    got, glse = run_gpu(x)
+    rows = rows_sample(x.B * x.Hq, 48, seed=2)
+    want, wlse = oracle.gqa(x.q, x.k, x.v, x.seq_lens, rows=rows)
+    assert_rows_close(got[rows], want, TOL_BF16, "config2")
+    assert_lse_close(glse[rows], wlse, 1e-5, "config2")
+
+
+def test_config2_split_invariance(cfg2):
+    x = cfg2
+    a, _ = run_gpu(x, 0)
+    b, _ = run_gpu(x, 3)
+    assert oracle.rel_err_rows(a, b) <= 2 * TOL_BF16
+
+
+@pytest.fixture(scope="module")
+def cfg3():
+    say("[swa] generating window 4096 + 4 sinks: B32 32/8 heads D128 lens U[4096,32768] paged16")
+    return wl.config3_swa_sinks()
+
+
+def test_config3_full_size_sampled(cfg3):
+    x = cfg3
+    got, glse = run_gpu(x)
+    rows = rows_sample(x.B * x.Hq, 48, seed=3)
+    want, wlse = oracle.gqa(x.q, x.k, x.v, x.seq_lens, window=x.window, n_sink=x.n_sink,
+                            scale=x.scale, rows=rows)
+    assert_rows_close(got[rows], want, TOL_BF16, "config3")
+    assert_lse_close(glse[rows], wlse, 1e-5, "config3")

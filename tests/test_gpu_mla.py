@@ -1,0 +1,82 @@
+"""Absorbed MLA decode attention on the GPU against the oracle."""
+import pytest
+import torch
+
+import oracle
+from decode_attention_kv_flash_amd import api
+from decode_attention_kv_flash_amd import workloads as wl
+from _helpers import TOL_BF16, assert_lse_close, assert_rows_close, dev, rows_sample, say
+
+pytestmark = pytest.mark.gpu
+
+
+def run_gpu(x, num_splits=0, page_table=None, latent=None):
+    out, lse = api.decode_attn_mla(dev(x.q), dev(latent if latent is not None else x.latent),
+                                   dev(x.seq_lens), dev(page_table), scale=x.scale,
+                                   num_splits=num_splits)
+    torch.cuda.synchronize()
+    return out.float().cpu().reshape(-1, 512), lse.cpu().reshape(-1)
+
+
+def check(x, num_splits=0, rows=None, **kw):
+    say(f"[mla] {x.name} B={x.B} H={x.H} lens={x.seq_lens.tolist()[:6]} splits={num_splits}")
+    got, glse = run_gpu(x, num_splits, **kw)
+    want, wlse = oracle.mla(x.q, x.latent, x.seq_lens, scale=x.scale, rows=rows)
+    if rows is not None:
+        got, glse = got[rows], glse[rows]
+    assert_rows_close(got, want, TOL_BF16, x.name)
+    assert_lse_close(glse, wlse, 1e-5, x.name)
+
+
+@pytest.mark.parametrize("splits", [0, 1, 3, 8])
+def test_mla_ragged(splits):
+    x = wl.make_mla(B=3, H=128, seq_lens=[1, 33, 517], seed=41, name="mla_ragged")
+    check(x, splits)
+
+
+def test_mla_64_heads_and_long():
+    x = wl.make_mla(B=2, H=64, seq_lens=[2048, 4000], seed=42, name="mla_h64")
+    check(x)
+
+
+def test_mla_empty_sequence():
+    x = wl.make_mla(B=2, H=64, seq_lens=[0, 40], seed=43, name="mla_empty")
+    got, lse = run_gpu(x)
+    assert torch.all(got[:64] == 0)
+    assert torch.all(torch.isinf(lse[:64]))
+    check(x)
+
+
+def test_mla_paged_equals_contiguous():
+    x = wl.make_mla(B=2, H=64, seq_lens=[300, 129], seed=44, name="mla_paged")
+    P = 16
+    n_pages = [(L + P - 1) // P for L in x.seq_lens.tolist()]
+    total = sum(n_pages)
+    g = torch.Generator().manual_seed(0)
+    perm = torch.randperm(total, generator=g)
+    pt = torch.zeros(2, max(n_pages), dtype=torch.int32)
+    cache = torch.zeros(total, P, 576, dtype=torch.bfloat16)
+    off = 0
+    for b, L in enumerate(x.seq_lens.tolist()):
+        for j in range(n_pages[b]):
+            phys = int(perm[off + j])
+            pt[b, j] = phys
+            t0, t1 = j * P, min(L, (j + 1) * P)
+            cache[phys, : t1 - t0] = x.latent[b, t0:t1]
+        off += n_pages[b]
+    cont, _ = run_gpu(x, 2)
+    paged, _ = run_gpu(x, 2, page_table=pt, latent=cache)
+    assert torch.equal(cont, paged)
+    check(x, 2, page_table=pt, latent=cache)
+
+
+@pytest.fixture(scope="module")
+def cfg4():
+    say("[mla] generating DeepSeek-V3-shaped MLA decode: B32 H128 576-wide latent 16384 tokens")
+    return wl.config4_mla()
+
+
+def test_config4_full_size_sampled(cfg4):
+    x = cfg4
+    rows = rows_sample(x.B * x.H, 48, seed=4)
+    check(x, 0, rows=rows)
