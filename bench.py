@@ -14,7 +14,8 @@ the 256 MB Infinity Cache.
 
 `roofline` covers the dominant kernel (gqa_split): algorithmic bytes per
 launch over its average duration, measured with HIP events the library
-records around each launch on the same stream.  `cpu_baseline` is the CPU
+records around each launch on the same stream, in a second pass of the same
+K steps (the first pass, without events, gives the step time).  `cpu_baseline` is the CPU
 oracle (plain fp64 C, OpenMP over rows) timed on this host on the same
 workload.
 """
@@ -71,15 +72,14 @@ class Timer:
         self.api, self.torch = api, torch
 
     def run(self, step, steps, warmup, kernels):
+        """K timed steps, twice: first plain (the step time), then with the
+        library's per-kernel HIP events enabled (kernel durations)."""
         torch, api = self.torch, self.api
         for i in range(warmup):
             step(i)
         torch.cuda.synchronize()
-        api.profile_reset()
-        api.profile_enable(True)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
         t0 = time.perf_counter()
         e0.record()
         for i in range(steps):
@@ -87,6 +87,11 @@ class Timer:
         e1.record()
         torch.cuda.synchronize()
         t1 = time.perf_counter()
+        api.profile_reset()
+        api.profile_enable(True)
+        for i in range(steps):
+            step(i)
+        torch.cuda.synchronize()
         api.profile_enable(False)
         per_kernel = {}
         for k in kernels:
@@ -200,6 +205,10 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--quick", action="store_true", help="headline workload only")
+    ap.add_argument("--only", choices=["gqa", "swa", "mla", "dsa"],
+                    help="time one workload and print its record (for profiling runs)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="time a plain 1 GiB device copy (reference for HBM byte counters)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -216,6 +225,12 @@ def main():
     torch.cuda.set_device(0)
     timer = Timer(api, torch)
     steps, warmup = args.steps, args.warmup
+    if args.calibrate_copy:
+        calibrate_copy(torch, steps)
+        return
+    if args.only:
+        only(args.only, timer, steps, warmup, torch, lib, wl)
+        return
 
     # ---- headline: Llama-3-8B-shaped GQA layer --------------------------------
     log("[bench] generating gqa config (B16, 32/8 heads, D128, 8192 tokens, paged 16, bf16)")
@@ -318,6 +333,44 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline()
     print(json.dumps(result), flush=True)
+
+
+def calibrate_copy(torch, steps):
+    """A plain device-to-device copy of 1 GiB: reads and writes exactly 1 GiB per
+    launch, the reference that scales rocprofv3's FETCH_SIZE / WRITE_SIZE."""
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    us = 1e6 * (time.perf_counter() - t0) / steps
+    print(json.dumps({"calibration": "device copy", "bytes_read_per_launch": n,
+                      "bytes_written_per_launch": n, "launches": steps, "avg_us": round(us, 2),
+                      "GB/s_read+write": round(2 * n / (us * 1e-6) / 1e9, 1)}), flush=True)
+
+
+def only(name, timer, steps, warmup, torch, lib, wl):
+    if name == "gqa":
+        x = wl.config2_llama3_8b_gqa()
+        r = bench_gqa(x, timer, steps, warmup, torch, lib)
+        r["kv_bytes_per_step"] = x.kv_bytes()
+    elif name == "swa":
+        x = wl.config3_swa_sinks()
+        r = bench_gqa(x, timer, steps, warmup, torch, lib)
+        r["kv_bytes_per_step"] = x.kv_bytes()
+    elif name == "mla":
+        m = wl.config4_mla()
+        r = bench_mla(m, timer, steps, warmup, torch, lib)
+        r["kv_bytes_per_step"], r["flops_per_step"] = m.kv_bytes(), m.flops()
+    else:
+        d = wl.config5_dsa()
+        r = bench_dsa(d, timer, steps, warmup, torch, lib)
+        r["indexer_bytes_per_step"] = d.indexer_bytes()
+    r["workload"] = name
+    print(json.dumps(r), flush=True)
 
 
 def cpu_baseline():

@@ -114,7 +114,8 @@ def _workspace(nbytes: int, device) -> Optional[torch.Tensor]:
 
 
 def decode_attn_gqa(q, k_cache, v_cache, seq_lens, page_table=None, window=0, n_sink=0, *,
-                    scale=None, num_splits=0, out=None, lse=None, want_lse=True, stream=None):
+                    scale=None, num_splits=0, out=None, lse=None, want_lse=True, workspace=None,
+                    stream=None):
     """GQA / sliding-window + sinks decode attention.  Returns (out, lse)."""
     for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (seq_lens, "seq_lens")):
         _dev(t, n)
@@ -132,7 +133,11 @@ def decode_attn_gqa(q, k_cache, v_cache, seq_lens, page_table=None, window=0, n_
         lse = torch.empty(B, Hq, dtype=torch.float32, device=q.device)
     nbytes = lib().decode_attn_gqa_workspace(B, Hq, Hkv, D, page_size, max_pages, int(window),
                                              int(n_sink), int(num_splits))
-    ws = _workspace(nbytes, q.device)
+    if workspace is not None:
+        _dev(workspace, "workspace")
+        ws, nbytes = workspace, workspace.numel() * workspace.element_size()
+    else:
+        ws = _workspace(nbytes, q.device)
     _check(lib().decode_attn_gqa(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), _ptr(page_table),
         int(window), int(n_sink), _ptr(out), _ptr(lse), B, Hq, Hkv, D, page_size, max_pages,

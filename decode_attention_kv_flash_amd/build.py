@@ -3,7 +3,8 @@
     python -m decode_attention_kv_flash_amd.build
 
 Produces ``decode_attention_kv_flash_amd/libdattn.so`` from ``csrc/`` (object
-files under ``_build/``).  Always recompiles: the result must match the
+files under ``_build/``).  DATTN_LIB_OUT / DATTN_BUILD_DIR redirect the output
+and DATTN_EXTRA_CFLAGS adds compiler flags (for tuning builds).  Always recompiles: the result must match the
 sources.  All HIP code is built with packed-fp32 instructions disabled.
 """
 from __future__ import annotations
@@ -15,8 +16,8 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
-OBJ = os.path.join(PKG, "_build")
-LIB = os.path.join(PKG, "libdattn.so")
+OBJ = os.environ.get("DATTN_BUILD_DIR", os.path.join(PKG, "_build"))
+LIB = os.environ.get("DATTN_LIB_OUT", os.path.join(PKG, "libdattn.so"))
 SOURCES = ["api.cpp", "gqa_decode.hip", "mla_decode.hip", "indexer.hip", "topk.hip"]
 ARCH = os.environ.get("DATTN_OFFLOAD_ARCH", "gfx950")
 
@@ -25,6 +26,7 @@ CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-fvisibility=hidden",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     f"-I{os.path.join(ROOT, 'include')}",
+    *os.environ.get("DATTN_EXTRA_CFLAGS", "").split(),
 ]
 
 

@@ -70,17 +70,35 @@ hipEvent_t pool_get() {
 }
 
 // ---------------------------------------------------------------- planning
-// Token splits per (sequence, KV head): enough workgroups for 8 per CU on
-// 256 CUs, but no split shorter than 256 tokens.
-int plan_gqa_splits(int32_t B, int32_t Hkv, int64_t max_tokens, int32_t req) {
-  if (req > 0) return req < kMaxSplits ? req : kMaxSplits;
-  const int64_t units = (int64_t)B * Hkv;
-  int64_t want = (2048 + units - 1) / units;
+// Token splits per (sequence, KV head): at most one per 256 attended tokens
+// (the cap), and within that the grid is sized to one full round of resident
+// workgroups (`slots` = workgroups per CU x CUs) -- a second, partial round
+// only adds a tail.
+int64_t gqa_split_cap(int64_t max_tokens) {
   int64_t cap = (max_tokens + 255) / 256;
   if (cap < 1) cap = 1;
-  int64_t n = want < cap ? want : cap;
-  if (n > kMaxSplits) n = kMaxSplits;
+  return cap < kMaxSplits ? cap : kMaxSplits;
+}
+
+int plan_gqa_splits(int32_t B, int32_t Hkv, int64_t max_tokens, int32_t req, int64_t slots) {
+  if (req > 0) return req < kMaxSplits ? req : kMaxSplits;
+  const int64_t units = (int64_t)B * Hkv;
+  int64_t n = slots / units;
+  const int64_t cap = gqa_split_cap(max_tokens);
+  if (n > cap) n = cap;
   return n < 1 ? 1 : (int)n;
+}
+
+// Resident split-kernel workgroups on the current device; 3 per CU on 256
+// CUs when the device cannot be queried.
+int64_t gqa_slots(bool bf16, int D, int G, bool paged, int page_size) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    cus = 256;
+  int per = dattn::gqa_blocks_per_cu(bf16, D, G, paged, page_size);
+  if (per < 1) per = 3;
+  return (int64_t)per * cus;
 }
 
 // MLA workgroups (64 heads each) run one per CU: aim for one full wave of
@@ -244,8 +262,10 @@ size_t decode_attn_gqa_workspace(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, 
                                  int32_t max_pages, int32_t window, int32_t n_sink,
                                  int32_t num_splits) {
   if (B < 1 || Hq < 1 || Hkv < 1 || D < 1 || page_size < 1 || num_splits < 0) return 0;
-  const int splits =
-      plan_gqa_splits(B, Hkv, gqa_max_tokens(page_size, max_pages, window, n_sink), num_splits);
+  // an upper bound on any plan: the requested count, else the split cap
+  const int splits = num_splits > 0 ? (num_splits < kMaxSplits ? num_splits : kMaxSplits)
+                                    : (int)gqa_split_cap(gqa_max_tokens(page_size, max_pages,
+                                                                        window, n_sink));
   return split_workspace((int64_t)B * Hq, splits, D);
 }
 
@@ -259,7 +279,8 @@ int decode_attn_gqa(const void* q, const void* k_cache, const void* v_cache, con
   if (rc) return rc;
   const bool paged = page_table != nullptr;
   const int splits = plan_gqa_splits(
-      B, Hkv, gqa_max_tokens(page_size, paged ? max_pages : 1, window, n_sink), num_splits);
+      B, Hkv, gqa_max_tokens(page_size, paged ? max_pages : 1, window, n_sink), num_splits,
+      num_splits > 0 ? 0 : gqa_slots(dtype == DATTN_BF16, D, Hq / Hkv, paged, page_size));
   const size_t need = split_workspace((int64_t)B * Hq, splits, D);
   if ((rc = check_workspace(workspace, workspace_bytes, need))) return rc;
 

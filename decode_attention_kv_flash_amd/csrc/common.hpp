@@ -14,16 +14,25 @@ __device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x 
 __device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
 __device__ __forceinline__ float bf16_to_f32(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
 
-// fp32 -> bf16, round to nearest even; NaN stays NaN.
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+
+// fp32 -> bf16 with the hardware converter (v_cvt_pk_bf16_f32: round to
+// nearest even, NaN preserved).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  return (uint16_t)(pack_bf16x2(f, 0.f) & 0xffffu);
+}
+
+// Pairs of bf16 halves from two dwords: (lo(a), lo(b)) and (hi(a), hi(b)).
+__device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
 }
 
 // DPP lane permutes inside a row of 16 lanes.
@@ -60,10 +69,17 @@ __device__ __forceinline__ float group_max(float x) {
   return x;
 }
 
+// 16-byte load of data read once (K/V or latent rows): the nontemporal hint
+// keeps the stream from displacing reused lines in the caches.
+__device__ __forceinline__ uint4 load_stream(const void* p) {
+  typedef unsigned __attribute__((ext_vector_type(4))) u32x4;
+  const u32x4 v = __builtin_nontemporal_load((const u32x4*)p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // exp2 of a value that may be -inf (gives 0).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;

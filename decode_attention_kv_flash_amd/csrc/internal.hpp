@@ -29,6 +29,8 @@ struct GqaArgs {
 };
 
 hipError_t launch_gqa(const GqaArgs& a, hipStream_t s);
+// Resident workgroups per CU of the split kernel for this shape (0 if unknown).
+int gqa_blocks_per_cu(bool bf16, int D, int G, bool paged, int page_size);
 
 struct CombineArgs {
   const float* part_o;    // [rows, splits, D]

@@ -87,8 +87,10 @@ typedef enum {
  *   scale      softmax scale; <= 0 means 1/sqrt(D)
  *   num_splits token-range splits per (sequence, KV head); 0 = automatic.
  *              Partial results are merged by log-sum-exp in a second kernel.
- *   workspace  device memory of at least decode_attn_gqa_workspace(...) bytes
- *              (may be NULL when that size is 0)
+ *   workspace  device memory of at least decode_attn_gqa_workspace(...) bytes,
+ *              256-byte aligned (may be NULL when that size is 0).  It holds
+ *              the split partials and needs no initialisation; calls that
+ *              share a workspace must be ordered on one stream.
  */
 DATTN_EXPORT int decode_attn_gqa(const void* q, const void* k_cache, const void* v_cache,
                     const int32_t* seq_lens, const int32_t* page_table,

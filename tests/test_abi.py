@@ -70,7 +70,7 @@ def test_gqa_workspace_sizes():
     L = api.lib()
     # one split: no workspace
     assert L.decode_attn_gqa_workspace(2, 4, 2, 64, 256, 1, 0, 0, 1) == 0
-    # explicit 8 splits on 16 x 32 heads x 128: o and lse partials, 256-aligned
+    # explicit 8 splits on 16 x 32 heads x 128: o and lse partials, each 256-aligned
     n = L.decode_attn_gqa_workspace(16, 32, 8, 128, 16, 512, 0, 0, 8)
     assert n == 16 * 32 * 8 * 128 * 4 + 16 * 32 * 8 * 4
     # window + sinks cap the planned splits below the cache capacity

@@ -114,6 +114,19 @@ def test_aliased_pages():
     assert_rows_close(got.reshape(-1, 128), want, TOL_BF16)
 
 
+def test_workspace_needs_no_initialisation_and_is_reusable():
+    """Garbage in the workspace and back-to-back calls that share it, with
+    different split counts, all give the oracle's result."""
+    x = wl.make_gqa(B=3, Hq=16, Hkv=4, D=128, seq_lens=[700, 1, 2222], seed=29, name="ws")
+    want, _ = oracle.gqa(x.q, x.k, x.v, x.seq_lens)
+    ws = torch.full((1 << 22,), 0xFF, dtype=torch.uint8, device="cuda")
+    for splits in (4, 4, 3, 8, 4):
+        out, _ = api.decode_attn_gqa(dev(x.q), dev(x.k_cache), dev(x.v_cache), dev(x.seq_lens),
+                                     dev(x.page_table), num_splits=splits, workspace=ws)
+        torch.cuda.synchronize()
+        assert_rows_close(out.float().cpu().reshape(-1, 128), want, TOL_BF16, f"splits {splits}")
+
+
 def test_deterministic():
     x = wl.make_gqa(B=2, Hq=32, Hkv=8, D=128, seq_lens=[999, 2048], seed=28)
     a, _ = run_gpu(x)
