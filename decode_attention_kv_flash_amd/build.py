@@ -30,6 +30,13 @@ CFLAGS = [
 ]
 
 
+# Per-file device-code flags.  The MLA kernel keeps its output accumulator in
+# AGPRs through inline assembly; its score MFMAs must then take VGPRs.
+FILE_FLAGS = {
+    "mla_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(OBJ, exist_ok=True)
     procs, objs = [], []
@@ -37,7 +44,7 @@ def build(verbose: bool = False) -> str:
         obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
         lang = ["-x", "hip"]
-        cmd = [HIPCC, *lang, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC, *lang, *CFLAGS, *FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))

@@ -17,6 +17,7 @@
 namespace {
 
 constexpr int kMaxSplits = 64;
+constexpr int kMlaMaxSplits = 256;
 constexpr int kTopkMax = 16384;
 thread_local std::string g_err;
 
@@ -101,17 +102,34 @@ int64_t gqa_slots(bool bf16, int D, int G, bool paged, int page_size) {
   return (int64_t)per * cus;
 }
 
-// MLA workgroups (64 heads each) run one per CU: aim for one full wave of
-// 256 workgroups, splits of at least 128 tokens.
+// MLA workgroups (128 or 64 heads each, 127 KB of LDS) run one per CU: aim
+// for one full wave of 256 workgroups with splits of at least 256 tokens; a
+// split holds at most kMlaMaxSplitTokens tokens, which sets a floor on the
+// count (a request below it is raised).  0 when the count would exceed
+// kMlaMaxSplits.
 int plan_mla_splits(int32_t B, int32_t H, int64_t max_tokens, int32_t req) {
-  if (req > 0) return req < kMaxSplits ? req : kMaxSplits;
-  const int64_t units = (int64_t)B * (H / 64);
-  int64_t want = (256 + units - 1) / units;
-  int64_t cap = (max_tokens + 127) / 128;
-  if (cap < 1) cap = 1;
-  int64_t n = want < cap ? want : cap;
-  if (n > kMaxSplits) n = kMaxSplits;
-  return n < 1 ? 1 : (int)n;
+  const int64_t floor_n = (max_tokens + dattn::kMlaMaxSplitTokens - 1) / dattn::kMlaMaxSplitTokens;
+  int64_t n;
+  if (req > 0) {
+    n = req;
+  } else {
+    const int64_t units = (int64_t)B * (H / dattn::mla_heads_per_workgroup(H));
+    const int64_t want = (256 + units - 1) / units;
+    const int64_t cap = (max_tokens + 255) / 256;
+    n = want < cap ? want : cap;
+  }
+  if (n < floor_n) n = floor_n;
+  if (n < 1) n = 1;
+  if (n > kMlaMaxSplits) n = req > 0 ? kMlaMaxSplits : 0;
+  if (n < floor_n) return 0;
+  return (int)n;
+}
+
+// MLA partials: unnormalised O [rows, splits, 512], reference maxima and
+// denominators [rows, splits] each.
+size_t mla_workspace(int64_t rows, int splits) {
+  return align256((size_t)rows * splits * 512 * sizeof(float)) +
+         2 * align256((size_t)rows * splits * sizeof(float));
 }
 
 // Upper bound on the tokens one sequence attends: the cache capacity
@@ -205,6 +223,8 @@ int validate_mla_common(const char* fn, const void* q, const void* latent, const
   if (d_latent != 512 || d_rope != 64)
     return fail(DATTN_EUNSUPPORTED, "%s: latent %d + rope %d; only 512 + 64 is built", fn, d_latent, d_rope);
   if (H % 64 != 0) return fail(DATTN_EUNSUPPORTED, "%s: H = %d is not a multiple of 64", fn, H);
+  if ((int64_t)B * S_max >= ((int64_t)1 << 31))
+    return fail(DATTN_EUNSUPPORTED, "%s: B * S_max must be below 2^31 cache rows", fn);
   if (H / 64 > 65535) return fail(DATTN_EINVAL, "%s: H too large", fn);
   if (dtype != DATTN_BF16) return fail(DATTN_EUNSUPPORTED, "%s: only bf16 is built", fn);
   if (num_splits < 0) return fail(DATTN_EINVAL, "%s: num_splits must be >= 0", fn);
@@ -313,7 +333,7 @@ int decode_attn_gqa(const void* q, const void* k_cache, const void* v_cache, con
   hipStream_t s = (hipStream_t)stream;
   if ((rc = launch("gqa_split", s, [&] { return dattn::launch_gqa(a, s); }))) return rc;
   if (splits > 1) {
-    dattn::CombineArgs c{a.part_o, a.part_lse, out, lse, B * Hq, splits, D, a.bf16};
+    dattn::CombineArgs c{a.part_o, a.part_lse, nullptr, out, lse, B * Hq, splits, D, a.bf16};
     if ((rc = launch("lse_combine", s, [&] { return dattn::launch_combine(c, s); }))) return rc;
   }
   return ok();
@@ -323,27 +343,26 @@ int decode_attn_gqa(const void* q, const void* k_cache, const void* v_cache, con
 
 size_t decode_attn_mla_workspace(int32_t B, int32_t H, int32_t d_latent, int32_t S_max,
                                  int32_t num_splits) {
-  if (B < 1 || H < 64 || d_latent < 1 || S_max < 1 || num_splits < 0) return 0;
+  if (B < 1 || H < 64 || H % 64 != 0 || d_latent < 1 || S_max < 1 || num_splits < 0) return 0;
   const int splits = plan_mla_splits(B, H, S_max, num_splits);
-  return split_workspace((int64_t)B * H, splits, d_latent);
+  return splits > 0 ? mla_workspace((int64_t)B * H, splits) : 0;
 }
 
+// The split kernel always writes unnormalised partials; the combine divides
+// (also for one split) and writes bf16 out and the natural-log lse.
 static int run_mla(dattn::MlaArgs& a, int splits, float* lse, uint16_t* out, void* workspace,
                    hipStream_t s, const char* name) {
+  const size_t rs = (size_t)a.B * a.H * splits;
   a.num_splits = splits;
   a.out = out;
   a.lse = lse;
-  if (splits > 1) {
-    a.part_o = (float*)workspace;
-    a.part_lse = (float*)((char*)workspace + align256((size_t)a.B * a.H * splits * 512 * sizeof(float)));
-  }
+  a.part_o = (float*)workspace;
+  a.part_lse = (float*)((char*)workspace + align256(rs * 512 * sizeof(float)));
+  a.part_l = (float*)((char*)a.part_lse + align256(rs * sizeof(float)));
   int rc = launch(name, s, [&] { return dattn::launch_mla(a, s); });
   if (rc) return rc;
-  if (splits > 1) {
-    dattn::CombineArgs c{a.part_o, a.part_lse, out, lse, a.B * a.H, splits, 512, 1};
-    if ((rc = launch("lse_combine", s, [&] { return dattn::launch_combine(c, s); }))) return rc;
-  }
-  return ok();
+  dattn::CombineArgs c{a.part_o, a.part_lse, a.part_l, out, lse, a.B * a.H, splits, 512, 1};
+  return launch("lse_combine", s, [&] { return dattn::launch_combine(c, s); });
 }
 
 int decode_attn_mla(const void* q_absorbed, const void* latent_cache, const int32_t* seq_lens,
@@ -359,8 +378,11 @@ int decode_attn_mla(const void* q_absorbed, const void* latent_cache, const int3
     if (!pow2(page_size)) return fail(DATTN_EUNSUPPORTED, "decode_attn_mla: paged cache needs a power-of-two page_size");
     if (max_pages < 1) return fail(DATTN_EINVAL, "decode_attn_mla: max_pages must be >= 1");
   }
-  const int splits = plan_mla_splits(B, H, S_max, num_splits);
-  if ((rc = check_workspace(workspace, workspace_bytes, split_workspace((int64_t)B * H, splits, 512))))
+  const int64_t max_tokens = page_table ? (int64_t)page_size * max_pages : S_max;
+  const int splits = plan_mla_splits(B, H, max_tokens, num_splits);
+  if (splits < 1) return fail(DATTN_EUNSUPPORTED, "decode_attn_mla: %lld tokens need more than %d splits",
+                              (long long)max_tokens, kMlaMaxSplits);
+  if ((rc = check_workspace(workspace, workspace_bytes, mla_workspace((int64_t)B * H, splits))))
     return rc;
   dattn::MlaArgs a{};
   a.q = (const uint16_t*)q_absorbed;
@@ -379,9 +401,9 @@ int decode_attn_mla(const void* q_absorbed, const void* latent_cache, const int3
 }
 
 size_t sparse_mla_attn_workspace(int32_t B, int32_t H, int32_t d_latent, int32_t k, int32_t num_splits) {
-  if (B < 1 || H < 64 || d_latent < 1 || k < 1 || num_splits < 0) return 0;
+  if (B < 1 || H < 64 || H % 64 != 0 || d_latent < 1 || k < 1 || num_splits < 0) return 0;
   const int splits = plan_mla_splits(B, H, k, num_splits);
-  return split_workspace((int64_t)B * H, splits, d_latent);
+  return splits > 0 ? mla_workspace((int64_t)B * H, splits) : 0;
 }
 
 int sparse_mla_attn(const void* q, const void* latent_cache, const int32_t* topk_idx, int32_t k,
@@ -394,7 +416,9 @@ int sparse_mla_attn(const void* q, const void* latent_cache, const int32_t* topk
   if (!topk_idx) return fail(DATTN_EINVAL, "sparse_mla_attn: topk_idx is NULL");
   if (k < 1) return fail(DATTN_EINVAL, "sparse_mla_attn: k must be >= 1");
   const int splits = plan_mla_splits(B, H, k, num_splits);
-  if ((rc = check_workspace(workspace, workspace_bytes, split_workspace((int64_t)B * H, splits, 512))))
+  if (splits < 1) return fail(DATTN_EUNSUPPORTED, "sparse_mla_attn: k = %d needs more than %d splits", k,
+                              kMlaMaxSplits);
+  if ((rc = check_workspace(workspace, workspace_bytes, mla_workspace((int64_t)B * H, splits))))
     return rc;
   dattn::MlaArgs a{};
   a.q = (const uint16_t*)q;

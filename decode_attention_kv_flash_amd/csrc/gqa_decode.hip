@@ -368,9 +368,12 @@ int occupancy_g(int G) {
 // Merge split partials (o_j normalised, lse_j in log2 units):
 // lse = max + log2 sum_j 2^(lse_j - max); o = sum_j 2^(lse_j - lse) o_j.
 // One thread per output element; it loads its row's split log-sum-exps and
-// its split partials together (one memory round trip), then merges.
+// its split partials together (one memory round trip), then merges.  Splits
+// may also hand over unnormalised sums with their reference maximum and
+// softmax denominator (CombineArgs::part_l): the same merge with weights
+// 2^(m - M) on both the sums and the denominators.
 constexpr int kCombineThreads = 256;
-constexpr int kMaxCombineSplits = 64;
+constexpr int kMaxCombineSplits = 256;
 constexpr int kCombineChunk = 16;
 
 template <bool BF16>
@@ -381,15 +384,17 @@ __global__ __launch_bounds__(kCombineThreads) void lse_combine_kernel(const Comb
   const int row = (int)(e / a.D), d = (int)(e % a.D);
   const int S = a.splits;
   const float* pl = a.part_lse + (size_t)row * S;
+  const float* ps = a.part_l ? a.part_l + (size_t)row * S : nullptr;
   const float* po = a.part_o + (size_t)row * S * a.D + d;
   float M = NEG_INF, wsum = 0.f, acc = 0.f;
   for (int j0 = 0; j0 < S; j0 += kCombineChunk) {
-    float x[kCombineChunk], v[kCombineChunk];
+    float x[kCombineChunk], v[kCombineChunk], l[kCombineChunk];
 #pragma unroll
     for (int u = 0; u < kCombineChunk; ++u) {
       const bool in = j0 + u < S;
       x[u] = in ? pl[j0 + u] : NEG_INF;
       v[u] = in ? po[(size_t)(j0 + u) * a.D] : 0.f;
+      l[u] = ps && in ? ps[j0 + u] : 1.f;
     }
     float Mc = M;
 #pragma unroll
@@ -401,7 +406,7 @@ __global__ __launch_bounds__(kCombineThreads) void lse_combine_kernel(const Comb
 #pragma unroll
     for (int u = 0; u < kCombineChunk; ++u) {
       const float w = fast_exp2(x[u] - mu);
-      wsum += w;
+      wsum = fmaf(w, l[u], wsum);
       acc = fmaf(w, v[u], acc);
     }
     M = Mc;

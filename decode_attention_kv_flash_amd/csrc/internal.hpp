@@ -35,6 +35,10 @@ int gqa_blocks_per_cu(bool bf16, int D, int G, bool paged, int page_size);
 struct CombineArgs {
   const float* part_o;    // [rows, splits, D]
   const float* part_lse;  // [rows, splits] (log2 units)
+  // nullptr: part_o holds o / l and part_lse log2(sum 2^s).  Otherwise
+  // part_o holds the unnormalised sum of 2^(s - m) v, part_lse the reference
+  // m and part_l [rows, splits] the sum of 2^(s - m).
+  const float* part_l;
   void* out;              // [rows, D]
   float* lse;             // [rows] natural log, or nullptr
   int32_t rows, splits, D;
@@ -52,12 +56,18 @@ struct MlaArgs {
   int32_t k_sel;
   uint16_t* out;            // [B, H, Dc] (num_splits == 1)
   float* lse;
-  float* part_o;
-  float* part_lse;
+  float* part_o;             // [B, H, splits, Dc] unnormalised sums
+  float* part_lse;           // [B, H, splits] reference maximum (log2 units)
+  float* part_l;             // [B, H, splits] softmax denominators
   int32_t B, H, S_max, page_size, log2_page, max_pages, num_splits;
   float scale_log2;
 };
 
+// Tokens one MLA split may hold (its cache rows are tabled in LDS); the
+// planner picks at least ceil(tokens / kMlaMaxSplitTokens) splits.
+constexpr int kMlaMaxSplitTokens = 4032;
+// 128 query heads per workgroup when H allows it, else 64 (H % 64 == 0).
+int mla_heads_per_workgroup(int H);
 hipError_t launch_mla(const MlaArgs& a, hipStream_t s);
 
 struct IndexerArgs {

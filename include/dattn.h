@@ -128,7 +128,15 @@ DATTN_EXPORT size_t decode_attn_gqa_workspace(int32_t B, int32_t Hq, int32_t Hkv
  *   S_max        contiguous: rows per sequence; paged: page_size * max_pages
  *   page_size    paged: a power of two; ignored when page_table == NULL
  *   scale        <= 0 means 1/sqrt(192) (DeepSeek-V3: 128 + 64 qk dims)
- *   num_splits   0 = automatic
+ *   num_splits   0 = automatic; a split holds at most 4032 tokens, so a
+ *                smaller count is raised to ceil(S_max / 4032) (at most 256)
+ *   workspace    decode_attn_mla_workspace bytes (never 0: the splits' partial
+ *                results always go through it)
+ * The cache must hold fewer than 2^31 rows (B * S_max contiguous, num_pages *
+ * page_size paged); page_table entries must name pages of the cache.
+ * Errors: DATTN_EINVAL / DATTN_EUNSUPPORTED for arguments outside the above,
+ * DATTN_EWORKSPACE for a missing or short workspace, DATTN_EHIP for a launch
+ * failure; nothing is written then.
  */
 DATTN_EXPORT int decode_attn_mla(const void* q_absorbed, const void* latent_cache,
                     const int32_t* seq_lens, const int32_t* page_table,
@@ -184,12 +192,16 @@ DATTN_EXPORT size_t dsa_topk_workspace(int32_t B, int32_t S_max, int32_t k);
  * Same arithmetic as decode_attn_mla, over the token set
  * { topk_idx[b, j] : 0 <= j < k, topk_idx[b, j] >= 0 } (gather of the
  * selected latent rows, "Attention Optimizations", "Computation Path");
- * entries equal to -1 are skipped; an index listed twice counts twice.
+ * entries outside [0, S_max) (-1 by convention) are skipped; an index listed
+ * twice counts twice.
  *
  *   q            [B, H, d_latent + d_rope] bf16
- *   latent_cache [B, S_max, d_latent + d_rope] bf16
- *   topk_idx     int32 [B, k], each entry -1 or in [0, S_max)
+ *   latent_cache [B, S_max, d_latent + d_rope] bf16, B * S_max < 2^31
+ *   topk_idx     int32 [B, k], entries in [0, S_max); any other value
+ *                (such as -1) marks an empty slot
  *   out          [B, H, d_latent] bf16;  lse fp32 [B, H] or NULL
+ *   num_splits   as for decode_attn_mla, with k in place of S_max
+ * A sequence with no selected token gets out = 0 and lse = -inf.
  */
 DATTN_EXPORT int sparse_mla_attn(const void* q, const void* latent_cache, const int32_t* topk_idx, int32_t k,
                     void* out, float* lse,

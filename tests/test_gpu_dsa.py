@@ -98,6 +98,28 @@ def test_sparse_mla_random_indices(splits):
     assert_lse_close(glse, wlse, 1e-5, "sparse")
 
 
+@pytest.mark.parametrize("splits", [0, 1])
+def test_sparse_mla_empty_lists_and_holes(splits):
+    """Empty slots anywhere in the list: a sequence with none selected (zero
+    output, lse -inf), holes between selected tokens, and a list whose first
+    tiles are all empty."""
+    lens = [500, 500, 500, 3000]
+    m = wl.make_mla(B=4, H=128, seq_lens=lens, seed=56, name="sparse_holes")
+    idx = wl.random_topk_indices(B=4, seq_lens=lens, k=512, seed=57)
+    idx[1] = -1
+    idx[2, ::3] = -1
+    idx[3, :200] = -1
+    got, glse = run_sparse(m, idx, splits)
+    rows1 = slice(128, 256)
+    assert torch.all(got[rows1] == 0)
+    assert torch.all(torch.isinf(glse[rows1])) and torch.all(glse[rows1] < 0)
+    want, wlse = oracle.mla(m.q, m.latent, idx=idx, scale=m.scale)
+    keep = torch.ones(4 * 128, dtype=torch.bool)
+    keep[rows1] = False
+    assert_rows_close(got[keep], want[keep], TOL_BF16, "sparse holes")
+    assert_lse_close(glse[keep], wlse[keep], 1e-5, "sparse holes")
+
+
 def test_sparse_with_all_tokens_equals_dense():
     m = wl.make_mla(B=2, H=64, seq_lens=[256, 256], seed=54)
     idx = torch.arange(256, dtype=torch.int32).repeat(2, 1)

@@ -80,3 +80,25 @@ def test_config4_full_size_sampled(cfg4):
     x = cfg4
     rows = rows_sample(x.B * x.H, 48, seed=4)
     check(x, 0, rows=rows)
+
+
+def test_mla_score_jumps_restart_the_split():
+    """Scores far above the first ones of a split (more than 2^64 apart in
+    exp2 units): rows whose latent is a multiple of one head's query."""
+    x = wl.make_mla(B=2, H=128, seq_lens=[3000, 700], seed=45, name="mla_spikes")
+    q = x.q.float()
+    x.latent[0, 100] = (1.5 * q[0, 0]).to(torch.bfloat16)    # ~60 nats above the rest
+    x.latent[0, 1500] = (3.0 * q[0, 0]).to(torch.bfloat16)   # ~60 nats above that
+    x.latent[1, 650] = (2.0 * q[1, 70]).to(torch.bfloat16)
+    for splits in (1, 0):
+        check(x, splits)
+
+
+@pytest.mark.parametrize("H", [64, 128])
+@pytest.mark.parametrize("splits", [0, 1])
+def test_mla_tile_group_and_split_boundaries(H, splits):
+    """Lengths at a 32-token tile, a 96-token group and the 4032-token split
+    capacity (a request for one split is raised to two for 4033 tokens)."""
+    lens = [31, 32, 96, 97, 4032, 4033]
+    x = wl.make_mla(B=len(lens), H=H, seq_lens=lens, seed=46, name=f"mla_bounds_h{H}")
+    check(x, splits)
