@@ -65,7 +65,7 @@ struct MlaArgs {
 
 // Tokens one MLA split may hold (its cache rows are tabled in LDS); the
 // planner picks at least ceil(tokens / kMlaMaxSplitTokens) splits.
-constexpr int kMlaMaxSplitTokens = 4032;
+constexpr int kMlaMaxSplitTokens = 3840;
 // 128 query heads per workgroup when H allows it, else 64 (H % 64 == 0).
 int mla_heads_per_workgroup(int H);
 hipError_t launch_mla(const MlaArgs& a, hipStream_t s);

@@ -12,10 +12,10 @@
 // Data movement: the split's cache rows (paged, contiguous or gathered by a
 // top-k list) are resolved once into a row table in LDS.  Tiles of 32 rows
 // (36 KB) then go from HBM straight into LDS by direct-to-LDS loads
-// (global_load_lds_dwordx4: no registers in between), three tile buffers
-// deep, so two tiles are in flight while one is computed.  Row r of a tile
-// keeps its 16-byte chunk c at slot c ^ f(r); both read patterns below are
-// then free of LDS bank conflicts.
+// (global_load_lds_dwordx4: no registers in between) into four tile
+// buffers, issued two tiles ahead of use.  Row r of a tile keeps its 16-byte
+// chunk c at slot c ^ f(r) within its group of eight chunks; both read
+// patterns below are then free of LDS bank conflicts.
 //
 // Per tile and wave:
 //   * S^T[token, head] = C[token, :] . Q^T over 576 dims: 36 32x32x16 bf16
@@ -24,17 +24,25 @@
 //   * online softmax in log2 units per head ("All the attentions", section 1:
 //     running maximum and sum); the reference maximum is set by the head's
 //     first scores and moves only when a score passes it by more than 2^64
-//     (exponentials stay finite in fp32 and keep their relative precision),
-//     so the 256-value accumulator is almost never rescaled;
+//     (exponentials stay finite in fp32 and keep their relative precision);
+//     when that happens the workgroup restarts the split with the larger
+//     reference, so the 256-value accumulator is never rescaled;
 //   * O[head, 0:512] += P . C[:, 0:512]: the S^T accumulator layout is
 //     exactly the A operand P needs (heads x tokens, the k order permuted the
 //     same way on both operands), and the B operand (tokens x dims) comes
 //     from the row-major tile by the gfx950 transpose read ds_read_b64_tr_b16.
-//     O lives in accumulation registers (AGPRs) for the whole split.  All
-//     MFMAs are issued by inline assembly that pins each operand to its
-//     register file (O in AGPRs; scores, Q and the tile fragments in VGPRs);
-//     each carries the wait states the compiler would otherwise insert
-//     (a VALU result feeding an MFMA; an MFMA result read by ordinary code).
+// One wave per SIMD cannot hide LDS latency behind other waves, so the loop
+// is software-pipelined: iteration t alternates the score MFMAs of tile t + 1
+// with the P.V MFMAs of tile t (independent chains), each LDS read issued
+// five MFMAs before its use, then runs the softmax of tile t + 1.
+//
+// O lives in accumulation registers (AGPRs) for the whole split.  All MFMAs
+// are issued by inline assembly that pins each operand to its register file
+// (O in AGPRs; scores, Q and the tile fragments in VGPRs) and carries the
+// wait states the compiler would otherwise insert.  The tile copies are
+// inline assembly too: the compiler then tracks the LDS reads alone and
+// waits for each exactly, and the copies' completion is awaited explicitly
+// before the barrier that hands a tile to the other waves.
 // P is rounded to bf16 for the MFMA; everything else accumulates in fp32.
 #include <type_traits>
 
@@ -46,27 +54,46 @@ namespace {
 
 constexpr int kDc = 512;            // c_KV width (the value)
 constexpr int kDq = 576;            // latent row: c_KV + k_pe
+constexpr int kRowBytes = kDq * 2;
 constexpr int kChunks = kDq / 8;    // 16-byte chunks per row
 constexpr int kTile = 32;           // tokens per tile
 constexpr int kHeadsPerWave = 32;
 constexpr int kTileChunks = kTile * kChunks;              // 2304
 constexpr int kTileBytes = kTileChunks * 16;              // 36864
+constexpr int kBuffers = 4;
 constexpr int kDmaPerTile = kTileChunks / 64;             // 36 wave-wide 1 KB copies
 constexpr int kKSteps = kDq / 16;                         // 36 MFMA k-steps for the scores
 constexpr int kNTiles = kDc / 32;                         // 16 output tiles of 32 dims
+constexpr int kPvSteps = 2 * kNTiles;                     // 2 k-steps of 16 tokens x 16 tiles
+constexpr int kRing = 3;                                  // LDS fragments in flight per operand
 constexpr float kTau = 64.0f;                             // reference-maximum slack (log2)
 constexpr uint32_t kPad = 0x80000000u;                    // row-table flag: no token here
-constexpr int kNT = 2;                                    // cache policy: nontemporal
+constexpr int kMaxTiles = kMlaMaxSplitTokens / kTile;
+// tiles t + 1 (scores) and up to t + 3 (prefetch) of the last iteration
+constexpr int kRowTable = (kMaxTiles + 3) * kTile;
+static_assert(kMlaMaxSplitTokens % kTile == 0, "splits hold whole tiles");
+static_assert(kBuffers * kTileBytes + kRowTable * 4 + 16 <= 160 * 1024, "fits the LDS");
 
-constexpr int kGroup = 3 * kTile;                         // tokens per loop iteration
-static_assert(kMlaMaxSplitTokens % kGroup == 0, "splits hold whole groups");
-constexpr int kRowTable = kMlaMaxSplitTokens + 2 * kTile; // + the tiles prefetched past the end
+// Chunk permutation of row r (low three bits of the chunk index only).  LDS
+// has 64 four-byte banks; a 16-byte read serves 16 lanes per pass and an
+// 8-byte read 32.  Rows are 1152 B apart, i.e. alternate between two
+// 128-byte halves of the bank space, so rows of equal parity among 16
+// consecutive ones must take distinct slots (score reads: 16 rows, one
+// chunk), and rows r, r + 2 (r % 4 < 2) must take slots in different halves
+// of an 8-chunk group (transpose reads: 4 rows, 4 chunks).  m -> (m & 1) << 2
+// | m >> 1 over m = (r / 2) % 8 does both.
+__device__ __forceinline__ int swz(int r) {
+  const int m = (r >> 1) & 7;
+  return ((m & 1) << 2) | (m >> 1);
+}
 
-// chunk permutation of row r (low three bits of the chunk index only)
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
-
+typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
-typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8;
+
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return (uint32_t)(uintptr_t)(const lds_char*)p;
+}
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
 // vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
@@ -76,12 +103,10 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Workgroup barrier that leaves the newest N direct-to-LDS copies of this
-// wave in flight: wait until at most N vector-memory operations are
-// outstanding and every LDS access of this wave is done, then s_barrier.
-// (A plain __syncthreads would drain all copies: its release fence treats
-// them as pending LDS writes.)  The signal fences keep the compiler from
-// moving memory accesses across the barrier.
+// Workgroup barrier that leaves the newest N tile copies of this wave in
+// flight: wait until at most N vector-memory operations are outstanding and
+// every LDS access of this wave is done, then s_barrier.  The signal fences
+// keep the compiler from moving memory accesses across the barrier.
 template <int N>
 __device__ __forceinline__ void barrier_in_flight() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -89,6 +114,22 @@ __device__ __forceinline__ void barrier_in_flight() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
   __builtin_amdgcn_s_barrier();
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// One wave-wide 16-byte-per-lane copy from global memory into LDS at
+// lds_dst + 16 * lane (lds_dst uniform).  M0 carries the LDS address and is
+// restored afterwards.
+__device__ __forceinline__ void copy_to_lds(const void* src, uint32_t lds_dst) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off nt\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"((uint64_t)(uintptr_t)src), "s"(lds_dst)
+      : "memory");
 }
 
 // The O accumulators are written by MFMAs the compiler does not see; before
@@ -108,17 +149,13 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_split_kernel(const MlaArgs a) 
   static_assert(kDmaPerTile % NW == 0, "copies split evenly over the waves");
   const float NEG_INF = -__builtin_inff();
 
-  // three tile buffers as distinct objects: the compiler then knows that a
-  // read of one does not wait for copies into another
-  __shared__ __attribute__((aligned(16))) char tile0[kTileBytes];
-  __shared__ __attribute__((aligned(16))) char tile1[kTileBytes];
-  __shared__ __attribute__((aligned(16))) char tile2[kTileBytes];
+  __shared__ __attribute__((aligned(16))) char tiles[kBuffers * kTileBytes];
   __shared__ __attribute__((aligned(16))) uint32_t rows[kRowTable];
   __shared__ int first_valid;
-  // restart votes of the even and odd loop iterations: a vote is read by
-  // every wave after the iteration's last barrier and cleared one iteration
-  // later, so a fast wave never overwrites a vote a slow wave has yet to read
-  __shared__ int restart_vote[2];
+  // restart votes: iteration u votes in slot u % 3, every wave reads it after
+  // the iteration's barrier, and iteration u + 2 clears it, so a fast wave
+  // never touches a vote a slow wave has yet to read
+  __shared__ int restart_vote[3];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -135,13 +172,10 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_split_kernel(const MlaArgs a) 
     const int cap = PAGED ? a.page_size * a.max_pages : a.S_max;
     N = max(0, min(a.seq_lens[b], cap));
   }
-  // splits hold whole groups of three tiles, so only a sequence's last split
-  // computes padded tiles
-  const int per = ((N + a.num_splits - 1) / a.num_splits + kGroup - 1) / kGroup * kGroup;
+  const int per = ((N + a.num_splits - 1) / a.num_splits + kTile - 1) / kTile * kTile;
   const int f_begin = min(N, split * per);
   const int f_end = min(N, f_begin + per);
-  int n_tiles = min((f_end - f_begin + kTile - 1) / kTile, kMlaMaxSplitTokens / kTile);
-  const int n_groups = (n_tiles + 2) / 3;
+  int n_tiles = min((f_end - f_begin + kTile - 1) / kTile, kMaxTiles);
 
   // Q^T fragments (B operand): lane holds head h0 + lj, dims 16 ks + 8 half + [0, 8)
   bf16x8_t qf[kKSteps];
@@ -151,16 +185,16 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_split_kernel(const MlaArgs a) 
     for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = *(const bf16x8_t*)(qrow + 16 * ks);
   }
 
-  // ---- row table: cache row of every position of the split.  Flag kPad
-  // marks a position without a token; its entry still names a row of finite
-  // data (a real row of the same split), so that P = 0 times it stays 0.
+  // ---- row table: cache row of every position of the split and of the
+  // three tiles past it.  Flag kPad marks a position without a token; its
+  // entry still names a row of finite data (a real row of the same split),
+  // so that P = 0 times it stays 0.
   if (threadIdx.x == 0) {
     first_valid = 0x7fffffff;
-    restart_vote[0] = restart_vote[1] = 0;
+    restart_vote[0] = restart_vote[1] = restart_vote[2] = 0;
   }
   __syncthreads();
-  // every tile a group touches, plus the two tiles prefetched past the last
-  const int n_rows = n_tiles > 0 ? (3 * n_groups + 2) * kTile : 0;
+  const int n_rows = n_tiles > 0 ? (n_tiles + 3) * kTile : 0;
   for (int i = threadIdx.x; i < n_rows; i += kThreads) {
     const int f = f_begin + i;
     uint32_t e;
@@ -196,52 +230,44 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_split_kernel(const MlaArgs a) 
     }
   }
 
-  // ---- direct-to-LDS tile copy: wave copy i (of 36) fills slots 64 i + lane;
-  // slot q is row q / 72, stored chunk q % 72, i.e. chunk (q % 72) ^ f(row)
-  uint32_t dma_rc[kDmaPerWave];  // row | chunk << 8, fixed for the kernel
-#pragma unroll
-  for (int j = 0; j < kDmaPerWave; ++j) {
-    const int q = 64 * (wave * kDmaPerWave + j) + lane;
-    const int r = q / kChunks;
-    dma_rc[j] = (uint32_t)r | ((uint32_t)((q - r * kChunks) ^ swz(r)) << 8);
-  }
-  auto issue = [&](auto buf_id, int tix) {
-    constexpr int BI = decltype(buf_id)::value;
-    char* buf = BI == 0 ? tile0 : BI == 1 ? tile1 : tile2;
+  const uint32_t tiles_base = lds_address(tiles);
+  auto buffer = [&](int tix) -> uint32_t {
+    return tiles_base + (uint32_t)(tix & (kBuffers - 1)) * kTileBytes;
+  };
+
+  // ---- tile copy: wave copy i (of 36) fills slots 64 i + lane; slot q is
+  // row q / 72, stored chunk q % 72, i.e. chunk (q % 72) ^ f(row)
+  auto issue = [&](int tix) {
+    const uint32_t dst = buffer(tix) + 1024u * (uint32_t)(wave * kDmaPerWave);
     const uint32_t* rt = rows + tix * kTile;
     constexpr int kBatch = 9;  // row lookups in flight together
     static_assert(kDmaPerWave % kBatch == 0, "whole batches");
 #pragma unroll
     for (int j0 = 0; j0 < kDmaPerWave; j0 += kBatch) {
-      uint32_t rc[kBatch], row[kBatch];
+      uint32_t rc[kBatch], row[kBatch];  // rc: row | chunk << 8 of this lane's slot
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
-        rc[j] = dma_rc[j0 + j];
-        asm volatile("" : "+v"(rc[j]));  // keep per-copy addresses out of long-lived registers
+        uint32_t q = 64 * (wave * kDmaPerWave + j0 + j) + lane;
+        asm volatile("" : "+v"(q));  // recomputed per tile: registers are the scarce resource
+        const uint32_t r = q / kChunks;
+        rc[j] = r | (((q - r * kChunks) ^ swz(r)) << 8);
       }
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) row[j] = rt[rc[j] & 0xff] & ~kPad;
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
         const uint64_t chunk = (uint64_t)row[j] * kChunks + (rc[j] >> 8);
-        __builtin_amdgcn_global_load_lds((const void*)((const char*)a.latent + 16 * chunk),
-                                         (lds_void*)(buf + 1024 * (wave * kDmaPerWave + j0 + j)),
-                                         16, 0, kNT);
+        copy_to_lds((const char*)a.latent + 16 * chunk, dst + 1024u * (j0 + j));
       }
     }
   };
-  auto prime = [&]() {
-    issue(std::integral_constant<int, 0>{}, 0);
-    issue(std::integral_constant<int, 1>{}, 1);
-    barrier_in_flight<kDmaPerWave>();
-  };
 
-  // ---- per-lane LDS addresses of the two read patterns
+  // ---- per-lane parts of the two LDS read patterns
   const int sw_lj = swz(lj);
   const int li = lane & 15, g = lane >> 4;
   const int r1 = 4 * half + (li >> 2);                 // token of k elements 0..3 (+16 kk, +8)
   const int c0 = 2 * (g & 1) + ((li >> 1) & 1);        // chunk of dims 32 n + 16 (g&1) + 4 (li&3)
-  const int sw_r1 = swz(r1);                           // rows r1 + 8, r1 + 16 share it
+  const int sw_r1 = swz(r1), sw_r9 = swz(r1 + 8);      // rows + 16 share them
 
   // O accumulators: defined (zeroed) by MFMAs with zero operands, so that
   // they are born in AGPRs and never pass through VGPRs
@@ -255,56 +281,75 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_split_kernel(const MlaArgs a) 
   zero_acc();
   // m_run: the head's reference maximum (log2 units); m_seen: largest score so far
   float m_run = NEG_INF, m_seen = NEG_INF, l_run = 0.f;
+  bf16x8_t pa[2];  // P of the tile whose P.V comes next, bf16, one per 16-token k-step
 
-  auto step = [&](auto buf_id, int tix, int par) {
-    constexpr int BI = decltype(buf_id)::value;
-    if (BI == 1 && threadIdx.x == 0) restart_vote[par ^ 1] = 0;  // read by all before this tile
-    const char* cur = BI == 0 ? tile0 : BI == 1 ? tile1 : tile2;
-    issue(std::integral_constant<int, (BI + 2) % 3>{}, tix + 2);
-
-    // Per-lane byte offsets into the tile, made opaque here so that the
-    // compiler keeps six of them per tile instead of an address per read.
+  // Scores of the tile in buffer sbuf (S^T, 32 tokens x 32 heads: lane holds
+  // head lj, tokens 8(v/4) + 4 half + v%4), alternated with the P.V MFMAs of
+  // the tile in buffer pbuf when WITH_PV.
+  auto scores = [&](auto with_pv, uint32_t sbuf, uint32_t pbuf) -> f32x16_t {
+    constexpr bool WITH_PV = decltype(with_pv)::value;
+    // Per-lane LDS addresses, made opaque here so that the compiler keeps
+    // eight per tile instead of an address per read.
     // A operand of the scores: row lj, chunk c = 2 ks + half, stored at slot
-    // 8 (c / 8) + ((c % 8) ^ f(lj)): offset so[ks % 4] + 128 (ks / 4).
-    // B operand of P.V: rows r1 (+8) + 16 kk, chunk c = 4 n + c0, stored at
-    // 8 (c / 8) + ((c % 8) ^ f(r1)): offset vo[n % 2] + 128 (n / 2) + ...
-    uint32_t so[4], vo[2];
+    // 8 (c / 8) + ((c % 8) ^ f(lj)): so[ks % 4] + 128 (ks / 4).
+    // B operand of P.V: rows r1 + 16 kk and r1 + 8 + 16 kk, chunk c = 4 n +
+    // c0, stored at 8 (c / 8) + ((c % 8) ^ f(row)): vo[n % 2] and
+    // vo[2 + n % 2], + 128 (n / 2) + 16 kk rows.
+    uint32_t so[4], vo[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      so[j] = lj * (kDq * 2) + 16 * (((2 * j) | half) ^ sw_lj);
+      so[j] = sbuf + lj * kRowBytes + 16 * (((2 * j) | half) ^ sw_lj);
       asm volatile("" : "+v"(so[j]));
     }
+    if constexpr (WITH_PV) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      vo[j] = r1 * (kDq * 2) + 16 * ((4 * j + c0) ^ sw_r1) + 8 * (li & 1);
-      asm volatile("" : "+v"(vo[j]));
-    }
-
-    // S^T (32 tokens x 32 heads): lane holds head lj, tokens 8(v/4) + 4 half + v%4
-    auto aread = [&](int ks) -> bf16x8_t {
-      return *(const bf16x8_t*)(cur + so[ks & 3] + 128 * (ks >> 2));
-    };
-    f32x16_t s;
-    {
-      bf16x8_t ring[3];
-#pragma unroll
-      for (int j = 0; j < 3; ++j) ring[j] = aread(j);
-      asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"
-                   : "=&v"(s) : "v"(ring[0]), "v"(qf[0]));
-      ring[0] = aread(3);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int ks = 1; ks < kKSteps; ++ks) {
-        asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
-                     : "+v"(s) : "v"(ring[ks % 3]), "v"(qf[ks]));
-        if (ks + 3 < kKSteps) ring[ks % 3] = aread(ks + 3);
-        __builtin_amdgcn_sched_barrier(0);
+      for (int j = 0; j < 2; ++j) {
+        vo[j] = pbuf + r1 * kRowBytes + 16 * ((4 * j + c0) ^ sw_r1) + 8 * (li & 1);
+        vo[2 + j] = pbuf + (r1 + 8) * kRowBytes + 16 * ((4 * j + c0) ^ sw_r9) + 8 * (li & 1);
+        asm volatile("" : "+v"(vo[j]), "+v"(vo[2 + j]));
       }
-      // the scores are read by ordinary code next: let the last MFMA retire
-      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s));
     }
+    auto aread = [&](int ks) -> bf16x8_t {
+      return *(const lds_bf16x8*)(uintptr_t)(so[ks & 3] + 128 * (ks >> 2));
+    };
+    auto vread = [&](int p) -> bf16x8_t {  // p = 16 kk + n
+      const int kk = p >> 4, n = p & 15;
+      const uint32_t imm = 128 * (n >> 1) + 16 * kk * kRowBytes;
+      const bf16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(uintptr_t)(vo[n & 1] + imm));
+      const bf16x4_t v2 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(uintptr_t)(vo[2 + (n & 1)] + imm));
+      return __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    bf16x8_t ar[kRing], vr[kRing];
+#pragma unroll
+    for (int j = 0; j < kRing; ++j) {
+      ar[j] = aread(j);
+      if constexpr (WITH_PV) vr[j] = vread(j);
+    }
+    f32x16_t s;
+    asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(ar[0]), "v"(qf[0]));
+#pragma unroll
+    for (int i = 0; i < kKSteps; ++i) {
+      if (i > 0)
+        asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                     : "+v"(s) : "v"(ar[i % kRing]), "v"(qf[i]));
+      if (i + kRing < kKSteps) ar[i % kRing] = aread(i + kRing);
+      if constexpr (WITH_PV) {
+        if (i < kPvSteps) {
+          asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                       : "+a"(acc[i & (kNTiles - 1)]) : "v"(pa[i >> 4]), "v"(vr[i % kRing]));
+          if (i + kRing < kPvSteps) vr[i % kRing] = vread(i + kRing);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // the scores are read by ordinary code next: let the last MFMA retire
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s));
+    return s;
+  };
 
-    // online softmax for head lj (lanes lj and lj + 32 share the head)
+  // Online softmax of tile tix from its scores s; leaves its P in pa and
+  // votes for a restart in restart_vote[slot] when a maximum jumps.
+  auto softmax = [&](f32x16_t s, int tix, int slot) {
     const uint32_t* rt = rows + tix * kTile + 4 * half;
     float mx = NEG_INF;
 #pragma unroll
@@ -322,7 +367,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_split_kernel(const MlaArgs a) 
     m_seen = fmaxf(m_seen, mx);
     // a head's first scores set its reference (its O is still zero); a later
     // score past the reference by more than kTau asks for a restart
-    if (m_run != NEG_INF && mx > m_run + kTau) restart_vote[par] = 1;
+    if (m_run != NEG_INF && mx > m_run + kTau) restart_vote[slot] = 1;
     if (m_run == NEG_INF) m_run = mx;
     const float mu = m_run == NEG_INF ? 0.f : m_run;
     float psum = 0.f;
@@ -332,64 +377,65 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_split_kernel(const MlaArgs a) 
       psum += s[v];
     }
     l_run += psum;
-
-    // O += P . V over two 16-token k-steps; V read transposed from the tile
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      uint4 pa;
-      pa.x = pack_bf16x2(s[8 * kk + 0], s[8 * kk + 1]);
-      pa.y = pack_bf16x2(s[8 * kk + 2], s[8 * kk + 3]);
-      pa.z = pack_bf16x2(s[8 * kk + 4], s[8 * kk + 5]);
-      pa.w = pack_bf16x2(s[8 * kk + 6], s[8 * kk + 7]);
-      const bf16x8_t pab = __builtin_bit_cast(bf16x8_t, pa);
-      auto vread = [&](int n) -> bf16x8_t {
-        // dims 32 n + 16 (g&1) + 4 (li&3) .. + 3 of tokens r1 + 16 kk and r1 + 16 kk + 8
-        const uint32_t off = vo[n & 1] + 128 * (n >> 1) + 16 * kk * (kDq * 2);
-        const bf16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(cur + off));
-        const bf16x4_t v2 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(cur + off + 8 * kDq * 2));
-        return __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7);
-      };
-      bf16x8_t vr[3];
-#pragma unroll
-      for (int n = 0; n < 3; ++n) vr[n] = vread(n);
-#pragma unroll
-      for (int n = 0; n < kNTiles; ++n) {
-        asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
-                     : "+a"(acc[n]) : "v"(pab), "v"(vr[n % 3]));
-        if (n + 3 < kNTiles) vr[n % 3] = vread(n + 3);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      uint4 p;
+      p.x = pack_bf16x2(s[8 * kk + 0], s[8 * kk + 1]);
+      p.y = pack_bf16x2(s[8 * kk + 2], s[8 * kk + 3]);
+      p.z = pack_bf16x2(s[8 * kk + 4], s[8 * kk + 5]);
+      p.w = pack_bf16x2(s[8 * kk + 6], s[8 * kk + 7]);
+      pa[kk] = __builtin_bit_cast(bf16x8_t, p);
     }
+  };
 
-    // tile tix + 1 complete in LDS for every wave (only tile tix + 2 may
-    // still be in flight), tile tix free for reuse
+  // Prologue: tiles 0..2 requested, tile 0 scored and its softmax taken,
+  // tile 1 complete in LDS.  (A prologue never votes: its reference is unset
+  // or already the largest score seen.)
+  auto prime = [&]() {
+    issue(0);
+    issue(1);
+    issue(2);
+    barrier_in_flight<2 * kDmaPerWave>();
+    softmax(scores(std::false_type{}, buffer(0), 0u), 0, 0);
     barrier_in_flight<kDmaPerWave>();
   };
 
-  // the loop body has no branches around tiles: a tile past the split is
-  // all padding (P = 0), and two tiles are always in flight
-  if (n_groups > 0) {
+  // Iteration t: request tile t + 3 (into the buffer tile t - 1 freed),
+  // P.V of tile t alternated with the scores of tile t + 1 (for the last t
+  // a padding tile, all flagged: its softmax changes nothing), then the
+  // softmax of tile t + 1.  No branches around tiles.  A restart leaves the
+  // tile loop and runs the prologue again.
+  while (n_tiles > 0) {
     prime();
-    for (int it = 0; it < n_groups; ++it) {
-      const int par = it & 1;
-      step(std::integral_constant<int, 0>{}, 3 * it, par);
-      step(std::integral_constant<int, 1>{}, 3 * it + 1, par);
-      step(std::integral_constant<int, 2>{}, 3 * it + 2, par);
-      if (restart_vote[par]) {
-        // some head's maximum jumped: redo the split with every head's
-        // reference at the largest score it has seen (each restart raises a
-        // reference by more than kTau, so restarts are few)
-        barrier_in_flight<0>();  // every wave has read the vote
-        if (threadIdx.x == 0) restart_vote[0] = restart_vote[1] = 0;
-        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::);  // in-flight MFMAs retire first
-        zero_acc();
-        m_run = m_seen;
-        l_run = 0.f;
-        prime();
-        it = -1;
+    int slot = 0;
+    bool again = false;
+    for (int t = 0; t < n_tiles; ++t) {
+      if (threadIdx.x == 0) restart_vote[slot == 2 ? 0 : slot + 1] = 0;  // iteration t - 2's
+      issue(t + 3);
+      const f32x16_t s = scores(std::true_type{}, buffer(t + 1), buffer(t));
+      softmax(s, t + 1, slot);
+      // tile t + 2 complete in LDS for every wave (only tile t + 3 may still
+      // be in flight); buffer of tile t free for reuse
+      barrier_in_flight<kDmaPerWave>();
+      if (restart_vote[slot]) {
+        again = true;
+        break;
       }
+      slot = slot == 2 ? 0 : slot + 1;
     }
-    wait_vmcnt<0>();  // the two prefetches past the end land before the workgroup ends
+    if (!again) {
+      wait_vmcnt<0>();  // the prefetches past the end land before the workgroup ends
+      break;
+    }
+    // some head's maximum jumped: redo the split with every head's reference
+    // at the largest score it has seen (each restart raises a reference by
+    // more than kTau, so restarts are few)
+    barrier_in_flight<0>();  // every wave has read the vote; no copy in flight
+    if (threadIdx.x == 0) restart_vote[0] = restart_vote[1] = restart_vote[2] = 0;
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::);  // in-flight MFMAs retire first
+    zero_acc();
+    m_run = m_seen;
+    l_run = 0.f;
   }
   settle(acc);
 
