@@ -373,31 +373,24 @@ def only(name, timer, steps, warmup, torch, lib, wl):
     print(json.dumps(r), flush=True)
 
 
-def cpu_baseline():
-    """The oracle on the host cores, on the headline workload (repeated to ~10 s)."""
+def cpu_baseline(target_s=15.0, max_passes=500):
+    """The oracle on the host cores, on the headline workload: whole passes
+    repeated until about target_s seconds of CPU work (a bounded sample)."""
     import oracle
     from decode_attention_kv_flash_amd import workloads as wl
     x = wl.config2_llama3_8b_gqa()
     nbytes = x.kv_bytes()
     log(f"[bench] cpu oracle on the gqa workload, {oracle.threads()} threads")
-    t0 = time.perf_counter()
-    oracle.gqa(x.q, x.k, x.v, x.seq_lens, scale=x.scale)
-    once = time.perf_counter() - t0
-    reps = 1
-    if once < 10.0:
-        more = min(19, int(10.0 / max(once, 1e-3)))
-        t1 = time.perf_counter()
-        for _ in range(more):
-            oracle.gqa(x.q, x.k, x.v, x.seq_lens, scale=x.scale)
-        once_total = once + (time.perf_counter() - t1)
-        reps += more
-    else:
-        once_total = once
-    value = nbytes * reps / once_total / 1e9
+    reps, total = 0, 0.0
+    while total < target_s and reps < max_passes:
+        t0 = time.perf_counter()
+        oracle.gqa(x.q, x.k, x.v, x.seq_lens, scale=x.scale)
+        total += time.perf_counter() - t0
+        reps += 1
+    value = nbytes * reps / total / 1e9
     return {"value": round(value, 3), "unit": "GB/s", "cores": oracle.threads(), "kind": "oracle",
             "sample": f"full gqa workload ({x.B * x.Hq} rows x {int(x.seq_lens[0])} tokens, "
-                      f"{nbytes} KV bytes) x {reps} passes, {once_total:.1f} s"}
-
+                      f"{nbytes} KV bytes) x {reps} passes, {total:.1f} s"}
 
 if __name__ == "__main__":
     main()
