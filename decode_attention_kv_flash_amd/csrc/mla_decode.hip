@@ -152,6 +152,8 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_split_kernel(const MlaArgs a) 
   __shared__ __attribute__((aligned(16))) char tiles[kBuffers * kTileBytes];
   __shared__ __attribute__((aligned(16))) uint32_t rows[kRowTable];
   __shared__ int first_valid;
+  // bit t: tile t holds a position without a token (its scores need the mask)
+  __shared__ uint32_t tile_pad[(kMaxTiles + 3 + 31) / 32];
   // restart votes: iteration u votes in slot u % 3, every wave reads it after
   // the iteration's barrier, and iteration u + 2 clears it, so a fast wave
   // never touches a vote a slow wave has yet to read
@@ -189,6 +191,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_split_kernel(const MlaArgs a) 
   // three tiles past it.  Flag kPad marks a position without a token; its
   // entry still names a row of finite data (a real row of the same split),
   // so that P = 0 times it stays 0.
+  if (threadIdx.x < (kMaxTiles + 3 + 31) / 32) tile_pad[threadIdx.x] = 0u;
   if (threadIdx.x == 0) {
     first_valid = 0x7fffffff;
     restart_vote[0] = restart_vote[1] = restart_vote[2] = 0;
@@ -216,6 +219,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_split_kernel(const MlaArgs a) 
       e = row | (ok ? 0u : kPad);
     }
     rows[i] = e;
+    if (e & kPad) atomicOr(&tile_pad[(i / kTile) >> 5], 1u << ((i / kTile) & 31));
   }
   __syncthreads();
   if constexpr (SPARSE) {
@@ -237,20 +241,42 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_split_kernel(const MlaArgs a) 
 
   // ---- tile copy: wave copy i (of 36) fills slots 64 i + lane; slot q is
   // row q / 72, stored chunk q % 72, i.e. chunk (q % 72) ^ f(row)
+  // This lane's slot in each copy: tile row r and stored chunk c' (a wave's
+  // copies cover tile rows 32 w / NW .. + 32 / NW - 1).  With 4 waves the
+  // nine slots are kept packed, ten bits each (row within the wave's eight,
+  // chunk); with 2 waves they are recomputed per tile (no registers spare).
+  auto slot_of = [&](uint32_t q) -> uint32_t {  // row | chunk << 8
+    const uint32_t r = q / kChunks;
+    return r | (((q - r * kChunks) ^ swz(r)) << 8);
+  };
+  uint32_t slot_pk[3] = {0u, 0u, 0u};
+  if constexpr (NW == 4) {
+#pragma unroll
+    for (int j = 0; j < kDmaPerWave; ++j) {
+      const uint32_t rc = slot_of(64 * (wave * kDmaPerWave + j) + lane);
+      slot_pk[j / 3] |= (((rc & 0xff) - 8 * wave) | ((rc >> 8) << 3)) << (10 * (j % 3));
+    }
+  }
   auto issue = [&](int tix) {
     const uint32_t dst = buffer(tix) + 1024u * (uint32_t)(wave * kDmaPerWave);
     const uint32_t* rt = rows + tix * kTile;
     constexpr int kBatch = 9;  // row lookups in flight together
     static_assert(kDmaPerWave % kBatch == 0, "whole batches");
+    uint32_t pk[3] = {slot_pk[0], slot_pk[1], slot_pk[2]};
+    asm volatile("" : "+v"(pk[0]), "+v"(pk[1]), "+v"(pk[2]));  // unpack here, not once per kernel
 #pragma unroll
     for (int j0 = 0; j0 < kDmaPerWave; j0 += kBatch) {
       uint32_t rc[kBatch], row[kBatch];  // rc: row | chunk << 8 of this lane's slot
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
-        uint32_t q = 64 * (wave * kDmaPerWave + j0 + j) + lane;
-        asm volatile("" : "+v"(q));  // recomputed per tile: registers are the scarce resource
-        const uint32_t r = q / kChunks;
-        rc[j] = r | (((q - r * kChunks) ^ swz(r)) << 8);
+        if constexpr (NW == 4) {
+          const uint32_t x = pk[j / 3] >> (10 * (j % 3));
+          rc[j] = (8 * wave + (x & 7)) | (((x >> 3) & 127) << 8);
+        } else {
+          uint32_t q = 64 * (wave * kDmaPerWave + j0 + j) + lane;
+          asm volatile("" : "+v"(q));  // recomputed per tile: registers are the scarce resource
+          rc[j] = slot_of(q);
+        }
       }
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) row[j] = rt[rc[j] & 0xff] & ~kPad;
@@ -350,30 +376,41 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_split_kernel(const MlaArgs a) 
   // Online softmax of tile tix from its scores s; leaves its P in pa and
   // votes for a restart in restart_vote[slot] when a maximum jumps.
   auto softmax = [&](f32x16_t s, int tix, int slot) {
-    const uint32_t* rt = rows + tix * kTile + 4 * half;
+    // maximum over the raw scores (the scale is positive), masking only in
+    // tiles that hold positions without a token
     float mx = NEG_INF;
+    if ((tile_pad[tix >> 5] >> (tix & 31)) & 1u) {
+      const uint32_t* rt = rows + tix * kTile + 4 * half;
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const uint4 e = *(const uint4*)(rt + 8 * q4);
-      const uint32_t ev[4] = {e.x, e.y, e.z, e.w};
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const uint4 e = *(const uint4*)(rt + 8 * q4);
+        const uint32_t ev[4] = {e.x, e.y, e.z, e.w};
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int v = 4 * q4 + u;
-        s[v] = (ev[u] & kPad) ? NEG_INF : s[v] * a.scale_log2;
-        mx = fmaxf(mx, s[v]);
+        for (int u = 0; u < 4; ++u) {
+          const int v = 4 * q4 + u;
+          if (ev[u] & kPad) s[v] = NEG_INF;
+          mx = fmaxf(mx, s[v]);
+        }
       }
+    } else {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[v]);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    // lanes lj and lj + 32 hold the two halves of head lj's tokens
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * a.scale_log2;
+    }
     m_seen = fmaxf(m_seen, mx);
     // a head's first scores set its reference (its O is still zero); a later
     // score past the reference by more than kTau asks for a restart
     if (m_run != NEG_INF && mx > m_run + kTau) restart_vote[slot] = 1;
     if (m_run == NEG_INF) m_run = mx;
-    const float mu = m_run == NEG_INF ? 0.f : m_run;
+    const float nmu = m_run == NEG_INF ? 0.f : -m_run;
     float psum = 0.f;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      s[v] = fast_exp2(s[v] - mu);
+      s[v] = fast_exp2(__builtin_fmaf(s[v], a.scale_log2, nmu));
       psum += s[v];
     }
     l_run += psum;
