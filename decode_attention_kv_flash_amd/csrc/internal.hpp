@@ -77,6 +77,7 @@ struct IndexerArgs {
   const int32_t* seq_lens;
   float* scores;           // [B, S_max]
   int32_t B, Hi, S_max;
+  int32_t tok_per_wg;      // set by the launcher
 };
 
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s);

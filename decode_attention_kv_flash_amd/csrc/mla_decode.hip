@@ -87,50 +87,8 @@ __device__ __forceinline__ int swz(int r) {
   return ((m & 1) << 2) | (m >> 1);
 }
 
-typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
 typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8;
-
-__device__ __forceinline__ uint32_t lds_address(const void* p) {
-  return (uint32_t)(uintptr_t)(const lds_char*)p;
-}
-
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
-// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Workgroup barrier that leaves the newest N tile copies of this wave in
-// flight: wait until at most N vector-memory operations are outstanding and
-// every LDS access of this wave is done, then s_barrier.  The signal fences
-// keep the compiler from moving memory accesses across the barrier.
-template <int N>
-__device__ __forceinline__ void barrier_in_flight() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
-  __builtin_amdgcn_s_barrier();
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
-// One wave-wide 16-byte-per-lane copy from global memory into LDS at
-// lds_dst + 16 * lane (lds_dst uniform).  M0 carries the LDS address and is
-// restored afterwards.
-__device__ __forceinline__ void copy_to_lds(const void* src, uint32_t lds_dst) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off nt\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"((uint64_t)(uintptr_t)src), "s"(lds_dst)
-      : "memory");
-}
 
 // The O accumulators are written by MFMAs the compiler does not see; before
 // ordinary code reads or writes them, let the last of those MFMAs retire
