@@ -175,9 +175,11 @@ def bench_dsa(d, timer, steps, warmup, torch, lib):
     lse = torch.empty(B, m.H, dtype=torch.float32, device=dev)
     nbytes = lib.sparse_mla_attn_workspace(B, m.H, 512, d.topk, 0)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    ibytes = lib.dsa_indexer_topk_workspace(B, S, d.topk)
+    iws = torch.empty(max(ibytes, 1), dtype=torch.uint8, device=dev)
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     a1 = [(ptr(qi), ptr(w), ptr(ki[r]), ptr(sl), d.topk, ptr(idx), ptr(scores), B, Hi, Di, S, 1,
-           None, 0, stream) for r in range(R)]
+           ptr(iws), ibytes, stream) for r in range(R)]
     a2 = (ptr(q), ptr(lat), ptr(idx), d.topk, ptr(out), ptr(lse), B, m.H, 512, 64, m.S_max, 1,
           ctypes.c_float(m.scale), 0, ptr(ws), nbytes, stream)
 

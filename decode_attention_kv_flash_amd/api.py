@@ -184,7 +184,7 @@ def dsa_indexer_topk(q_i, w, k_i_cache, seq_lens, k, *, topk_idx=None, return_sc
     if topk_idx is None:
         topk_idx = torch.empty(B, k, dtype=torch.int32, device=q_i.device)
     scores = torch.empty(B, S_max, dtype=torch.float32, device=q_i.device) if return_scores else None
-    nbytes = 0 if return_scores else lib().dsa_indexer_topk_workspace(B, S_max, k)
+    nbytes = lib().dsa_indexer_topk_workspace(B, S_max, k)
     ws = _workspace(nbytes, q_i.device)
     _check(lib().dsa_indexer_topk(
         _ptr(q_i), _ptr(w), _ptr(k_i_cache), _ptr(seq_lens), int(k), _ptr(topk_idx), _ptr(scores),

@@ -19,6 +19,7 @@ namespace {
 constexpr int kMaxSplits = 64;
 constexpr int kMlaMaxSplits = 256;
 constexpr int kTopkMax = 16384;
+constexpr int kTopkMaxRow = 1 << 30;  // tokens per row the top-k indexes
 thread_local std::string g_err;
 
 int fail(int code, const char* fmt, ...) {
@@ -437,25 +438,31 @@ int sparse_mla_attn(const void* q, const void* latent_cache, const int32_t* topk
 
 // ------------------------------------------------------------------- DSA
 
-size_t dsa_topk_workspace(int32_t, int32_t, int32_t) { return 0; }
+size_t dsa_topk_workspace(int32_t B, int32_t S_max, int32_t k) {
+  (void)k;
+  if (B < 1 || S_max < 1 || S_max > kTopkMaxRow) return 0;
+  return dattn::topk_workspace_bytes(B, S_max);
+}
 
 int dsa_topk(const float* scores, const int32_t* seq_lens, int32_t k, int32_t* topk_idx, int32_t B,
              int32_t S_max, void* workspace, size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   if (!scores || !seq_lens || !topk_idx) return fail(DATTN_EINVAL, "dsa_topk: NULL pointer argument");
   if (B < 1 || S_max < 1) return fail(DATTN_EINVAL, "dsa_topk: B and S_max must be >= 1");
+  if (B > 65535) return fail(DATTN_EINVAL, "dsa_topk: B must be <= 65535");
+  if (S_max > kTopkMaxRow) return fail(DATTN_EINVAL, "dsa_topk: S_max must be <= %d", kTopkMaxRow);
   if (k < 1 || k > kTopkMax) return fail(DATTN_EINVAL, "dsa_topk: k = %d outside [1, %d]", k, kTopkMax);
-  dattn::TopkArgs t{scores, seq_lens, topk_idx, B, S_max, k};
+  int rc = check_workspace(workspace, workspace_bytes, dsa_topk_workspace(B, S_max, k));
+  if (rc) return rc;
+  dattn::TopkArgs t{scores, seq_lens, topk_idx, B, S_max, k, (uint32_t*)workspace, 0, 0};
   hipStream_t s = (hipStream_t)stream;
-  int rc = launch("topk_select", s, [&] { return dattn::launch_topk(t, s); });
+  rc = launch("topk_select", s, [&] { return dattn::launch_topk(t, s); });
   return rc ? rc : ok();
 }
 
+// [scores fp32 B x S_max, used when scores_out is NULL | top-k workspace]
 size_t dsa_indexer_topk_workspace(int32_t B, int32_t S_max, int32_t k) {
-  (void)k;
-  if (B < 1 || S_max < 1) return 0;
-  return align256((size_t)B * S_max * sizeof(float));
+  if (B < 1 || S_max < 1 || S_max > kTopkMaxRow) return 0;
+  return align256((size_t)B * S_max * sizeof(float)) + dsa_topk_workspace(B, S_max, k);
 }
 
 int dsa_indexer_topk(const void* q_i, const float* w, const void* k_i_cache, const int32_t* seq_lens,
@@ -471,17 +478,17 @@ int dsa_indexer_topk(const void* q_i, const float* w, const void* k_i_cache, con
   if (Hi != 32 && Hi != 64 && Hi != 96 && Hi != 128)
     return fail(DATTN_EUNSUPPORTED, "dsa_indexer_topk: Hi = %d not in {32,64,96,128}", Hi);
   if (dtype != DATTN_BF16) return fail(DATTN_EUNSUPPORTED, "dsa_indexer_topk: only bf16 is built");
-  float* scores = scores_out;
-  if (!scores) {
-    int rc = check_workspace(workspace, workspace_bytes, dsa_indexer_topk_workspace(B, S_max, k));
-    if (rc) return rc;
-    scores = (float*)workspace;
-  }
+  if (S_max > kTopkMaxRow)
+    return fail(DATTN_EINVAL, "dsa_indexer_topk: S_max must be <= %d", kTopkMaxRow);
+  int rc = check_workspace(workspace, workspace_bytes, dsa_indexer_topk_workspace(B, S_max, k));
+  if (rc) return rc;
+  float* scores = scores_out ? scores_out : (float*)workspace;
+  uint32_t* topk_ws = (uint32_t*)((char*)workspace + align256((size_t)B * S_max * sizeof(float)));
   hipStream_t s = (hipStream_t)stream;
   dattn::IndexerArgs ia{(const uint16_t*)q_i, w, (const uint16_t*)k_i_cache, seq_lens, scores, B, Hi, S_max};
-  int rc = launch("indexer_scores", s, [&] { return dattn::launch_indexer(ia, s); });
+  rc = launch("indexer_scores", s, [&] { return dattn::launch_indexer(ia, s); });
   if (rc) return rc;
-  dattn::TopkArgs t{scores, seq_lens, topk_idx, B, S_max, k};
+  dattn::TopkArgs t{scores, seq_lens, topk_idx, B, S_max, k, topk_ws, 0, 0};
   rc = launch("topk_select", s, [&] { return dattn::launch_topk(t, s); });
   return rc ? rc : ok();
 }

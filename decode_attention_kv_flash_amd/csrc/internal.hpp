@@ -87,8 +87,12 @@ struct TopkArgs {
   const int32_t* seq_lens;
   int32_t* idx;            // [B, k]
   int32_t B, S_max, k;
+  uint32_t* ws;            // topk_workspace_bytes(B, S_max), 256-byte aligned
+  int32_t n_chunks;        // set by the launcher
+  int64_t row_words;       // set by the launcher
 };
 
+size_t topk_workspace_bytes(int B, int S_max);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 
 }  // namespace dattn

@@ -3,39 +3,68 @@
 //
 // ("Attention Optimizations", "Computation Path": indices = topk(I, 2048);
 // "Caveats": a top-k over the whole context is expensive, so it is a radix
-// select, not a sort.)  One workgroup of 1024 threads per row, which reads
-// the row once and keeps it on chip -- 32 columns of 1024 keys in registers,
-// up to 32 more in LDS -- so every later pass runs from registers and LDS:
-//   1. scores become order-preserving unsigned keys (-0.0 folded onto +0.0);
-//      column c, thread t holds token 1024 c + t;
-//   2. the keys' min and max fix the range; the select then resolves the
-//      offset v = key - min most significant digit first, 12 bits a pass: a
-//      4096-bin histogram in LDS of the keys that match the digits fixed so
-//      far (a wave whose keys share one bin adds its count with one atomic),
-//      a block scan from the top finds the digit holding the k-th largest and
-//      how many keys equal to the threshold T are still needed (`need`);
-//      integer-valued scores resolve in one or two passes;
-//   3. an ordered compaction: per column of 1024 tokens, ballots count the
-//      keys above T and the keys equal to T per wave; column and wave offsets
-//      in LDS give each key its rank among both, and a selected key goes to
-//      (keys above T before it) + min(keys equal to T before it, need), so
-//      indices come out ascending and ties go to the lower index.
-// Rows longer than 65536 tokens use the 8-bit streaming variant below.
+// select, not a sort.)
+//
+// Every row is cut into chunks of 2048 tokens, one workgroup of 256 threads
+// per chunk (thread t holds tokens chunk*2048 + 256 j + t, j < 8), so a batch
+// of long rows spreads over the whole chip.  Scores become order-preserving
+// unsigned keys (-0.0 folded onto +0.0) and the k-th largest key T is found
+// most significant byte first.  Workgroups meet only at kernel boundaries, five
+// launches on the same grid, and never add into shared counters: each chunk
+// stores its own 256-bin histogram of the current byte (over the keys that
+// match the bytes fixed so far), and every workgroup of the next launch sums
+// its row's chunk histograms itself, finds the byte holding the k-th largest
+// key and how many keys of that bin are still needed (`need`):
+//   launch 0: histograms of byte 3;
+//   launch l = 1, 2, 3: fix byte 4 - l, histograms of byte 3 - l; launch 3
+//             also counts, per chunk, the keys whose top three bytes are
+//             already above T's;
+//   launch 4 (write): fix byte 0, hence T and `need`.  The same column sums,
+//             taken over the chunks before this one only, give the keys above
+//             T and equal to T that precede the chunk; ballots rank the keys
+//             inside it, and a taken key goes to
+//             (keys above T before it) + min(keys equal to T before it, need),
+//             so indices come out ascending and ties go to the lower index.
+// Workgroup 0 of a row records each decision for the next launch.  Rows with
+// seq_len <= k are written directly by the first launch.  Nothing in the
+// workspace has to be cleared beforehand.
 #include "common.hpp"
 #include "internal.hpp"
 
 namespace dattn {
 namespace {
 
-constexpr int kThreads = 1024;
+constexpr int kTT = 256;             // threads per workgroup
+constexpr int kNW = kTT / 64;        // waves per workgroup
+constexpr int kKPT = 8;              // keys per thread
+constexpr int kChunk = kTT * kKPT;   // tokens per workgroup
+constexpr int kBins = 256;           // one byte of the key per launch
+constexpr int kColBatch = 16;        // chunk histograms loaded per batch
 
-// Phase marks for instrumented builds (nothing in the library build).
-#ifndef DATTN_TOPK_MARK
-#define DATTN_TOPK_MARK(i)
-#endif
-constexpr int kWaves = kThreads / 64;
-constexpr int kBins = 4096;
-constexpr int kDigit = 12;
+// One row's workspace, in 32-bit words.
+struct RowWs {
+  uint32_t* h;     // [4][n_chunks][256]: per-chunk histograms of bytes 3, 2, 1, 0
+  uint32_t* above; // [n_chunks]: keys whose top three bytes exceed T's
+  uint32_t* st;    // [8]: byte 3, need; top 16 bits, need; top 24 bits, need
+};
+
+__host__ __device__ inline size_t topk_row_words(int n_chunks) {
+  const size_t w = (size_t)n_chunks * (4 * kBins + 1) + 8;
+  return (w + 63) & ~(size_t)63;
+}
+
+__device__ __forceinline__ RowWs row_ws(const TopkArgs& a, int b) {
+  RowWs r;
+  r.h = a.ws + (size_t)b * a.row_words;
+  r.above = r.h + (size_t)4 * a.n_chunks * kBins;
+  r.st = r.above + a.n_chunks;
+  return r;
+}
+
+// seq_lens outside [0, S_max] are clamped into it
+__device__ __forceinline__ int row_len(const TopkArgs& a, int b) {
+  return min(max(a.seq_lens[b], 0), a.S_max);
+}
 
 __device__ __forceinline__ uint32_t order_key(float f) {
   uint32_t u = __float_as_uint(f);
@@ -43,13 +72,93 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// exclusive prefix sum over a block of NT threads; also returns the total
-template <int NT>
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t x, uint32_t* wave_tot,
-                                                         uint32_t& total) {
-  constexpr int NW = NT / 64;
+// This workgroup's keys, loaded without waiting for the row length (tokens
+// past S_max read the row's last entry; `valid_mask` sorts them out).
+__device__ __forceinline__ void load_keys(const TopkArgs& a, int b, int c, uint32_t (&key)[kKPT]) {
+  const float* row = a.scores + (size_t)b * a.S_max;
+  const int t0 = c * kChunk + (int)threadIdx.x;
+  float x[kKPT];
+#pragma unroll
+  for (int j = 0; j < kKPT; ++j) x[j] = row[min(t0 + j * kTT, a.S_max - 1)];
+#pragma unroll
+  for (int j = 0; j < kKPT; ++j) key[j] = order_key(x[j]);
+}
+
+// bit j: token 256 j + t of chunk c lies inside the row
+__device__ __forceinline__ uint32_t valid_mask(int c, int L) {
+  const int t0 = c * kChunk + (int)threadIdx.x;
+  uint32_t v = 0;
+#pragma unroll
+  for (int j = 0; j < kKPT; ++j) v |= (uint32_t)(t0 + j * kTT < L) << j;
+  return v;
+}
+
+// Thread t: column 255 - t of the row's chunk histograms `h` ([n_chunks][256]),
+// summed over the chunks < nc (`tot`) and over the chunks < c (`pre`).
+// Loads cover chunks < n_load (>= nc); with n_load = n_chunks they need not
+// wait for the row length.
+__device__ __forceinline__ void column_sums(const uint32_t* h, int n_load, int nc, int c,
+                                            uint32_t& tot, uint32_t& pre) {
+  const uint32_t* col = h + (kBins - 1 - threadIdx.x);
+  tot = 0;
+  pre = 0;
+  for (int c0 = 0; c0 < n_load; c0 += kColBatch) {
+    uint32_t v[kColBatch];
+#pragma unroll
+    for (int u = 0; u < kColBatch; ++u) v[u] = col[(size_t)min(c0 + u, n_load - 1) * kBins];
+#pragma unroll
+    for (int u = 0; u < kColBatch; ++u) {
+      tot += c0 + u < nc ? v[u] : 0u;
+      pre += c0 + u < c ? v[u] : 0u;
+    }
+  }
+}
+
+// Short grids load every chunk's column at once; long rows load only the
+// chunks inside the row, which costs a wait for the row length first.
+constexpr int kEagerChunks = 64;
+__device__ __forceinline__ void row_column_sums(const TopkArgs& a, const uint32_t* h, int L, int c,
+                                                uint32_t& tot, uint32_t& pre) {
+  const int nc = (L + kChunk - 1) / kChunk;
+  if (a.n_chunks <= kEagerChunks)
+    column_sums(h, a.n_chunks, nc, c, tot, pre);
+  else
+    column_sums(h, nc, nc, c, tot, pre);
+}
+
+// LDS histogram add; a wave whose active keys share one bin adds once.
+__device__ __forceinline__ void hist_add(uint32_t* h, bool act, uint32_t d) {
+  const uint64_t am = __ballot(act);
+  if (am == 0) return;
+  const int first = __ffsll((long long)am) - 1;
+  const uint32_t d0 = __shfl(d, first);
+  const uint64_t same = __ballot(act && d == d0);
+  if (same == am) {
+    if ((int)(threadIdx.x & 63) == first) atomicAdd(&h[d0], (uint32_t)__popcll(am));
+  } else if (act) {
+    atomicAdd(&h[d], 1u);
+  }
+}
+
+__device__ __forceinline__ uint32_t block_sum(uint32_t x, uint32_t* red) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  uint32_t s = 0;
+#pragma unroll
+  for (int w = 0; w < kNW; ++w) s += red[w];
+  __syncthreads();
+  return s;
+}
+
+// Thread t holds the count of bin 255 - t.  Returns the bin holding the
+// need-th largest key counting from the top, and in `rest` how many keys of
+// that bin are still needed.  All threads get the same answer.
+__device__ __forceinline__ uint32_t find_byte(uint32_t cnt, uint32_t need, uint32_t* wave_tot,
+                                              uint32_t* res, uint32_t& rest) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t inc = x;
+  uint32_t inc = cnt;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
     const uint32_t y = __shfl_up(inc, d);
@@ -57,379 +166,159 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t x, uint32_t* w
   }
   if (lane == 63) wave_tot[wave] = inc;
   __syncthreads();
-  if (wave == 0) {
-    const uint32_t v = lane < NW ? wave_tot[lane] : 0u;
-    uint32_t vi = v;
+  uint32_t before = inc - cnt;
 #pragma unroll
-    for (int d = 1; d < NW; d <<= 1) {
-      const uint32_t y = __shfl_up(vi, d);
-      if (lane >= d) vi += y;
-    }
-    if (lane < NW) wave_tot[lane] = vi - v;
-    if (lane == NW - 1) wave_tot[NW] = vi;
+  for (int w = 0; w < kNW; ++w) before += w < wave ? wave_tot[w] : 0u;
+  if (before < need && before + cnt >= need) {
+    res[0] = kBins - 1 - threadIdx.x;
+    res[1] = need - before;
   }
   __syncthreads();
-  const uint32_t res = wave_tot[wave] + inc - x;
-  total = wave_tot[NW];
-  __syncthreads();
-  return res;
+  rest = res[1];
+  return res[0];
 }
 
-template <int NT>
-__device__ __forceinline__ uint32_t block_reduce_min_max(uint32_t mn, uint32_t mx, uint32_t* red,
-                                                         uint32_t& out_max) {
-  constexpr int NW = NT / 64;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) {
-    mn = min(mn, (uint32_t)__shfl_xor(mn, d));
-    mx = max(mx, (uint32_t)__shfl_xor(mx, d));
+// Launch LEVEL (0..3): histograms of key byte 3 - LEVEL over the keys that
+// match the LEVEL bytes fixed so far.
+template <int LEVEL>
+__global__ __launch_bounds__(kTT) void topk_digit_kernel(const TopkArgs a) {
+  constexpr int kShift = 24 - 8 * LEVEL;
+  __shared__ uint32_t hist[kBins], wave_tot[kNW], res[2], red[kNW];
+  const int c = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const RowWs w = row_ws(a, b);
+  uint32_t key[kKPT];
+  load_keys(a, b, c, key);
+  uint32_t tot = 0, pre = 0, prev_prefix = 0, prev_need = (uint32_t)a.k;
+  const int L = row_len(a, b), K = a.k;
+  if (LEVEL > 0) {
+    if (LEVEL > 1) {
+      prev_prefix = w.st[2 * (LEVEL - 2)];
+      prev_need = w.st[2 * (LEVEL - 2) + 1];
+    }
+    row_column_sums(a, w.h + (size_t)(LEVEL - 1) * a.n_chunks * kBins, L, 0, tot, pre);
   }
-  if (lane == 0) {
-    red[wave] = mn;
-    red[NW + wave] = mx;
+  if (LEVEL == 0 && L <= K) {
+    int32_t* out = a.idx + (size_t)b * K;
+    for (int j = c * kTT + tid; j < K; j += a.n_chunks * kTT) out[j] = j < L ? j : -1;
+    return;
+  }
+  if (L <= K || c * kChunk >= L) return;
+  const uint32_t valid = valid_mask(c, L);
+  uint32_t prefix = 0;
+  if (LEVEL > 0) {
+    uint32_t need;
+    prefix = (prev_prefix << 8) | find_byte(tot, prev_need, wave_tot, res, need);
+    if (c == 0 && tid == 0) {
+      w.st[2 * (LEVEL - 1)] = prefix;
+      w.st[2 * (LEVEL - 1) + 1] = need;
+    }
+  }
+  hist[tid] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kKPT; ++j) {
+    const bool m = ((valid >> j) & 1u) && (LEVEL == 0 || (key[j] >> (kShift + 8)) == prefix);
+    hist_add(hist, m, (key[j] >> kShift) & (kBins - 1));
   }
   __syncthreads();
-  uint32_t a = 0xffffffffu, b = 0u;
+  w.h[((size_t)LEVEL * a.n_chunks + c) * kBins + tid] = hist[tid];
+  if (LEVEL == 3) {
+    uint32_t n = 0;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    a = min(a, red[w]);
-    b = max(b, red[NW + w]);
+    for (int j = 0; j < kKPT; ++j) n += ((valid >> j) & 1u) && (key[j] >> 8) > prefix;
+    n = block_sum(n, red);
+    if (tid == 0) w.above[c] = n;
   }
-  __syncthreads();
-  out_max = b;
-  return a;
 }
 
-// Per-column ballot counts -> exclusive offsets: cnt[j][w] becomes the number
-// of marked keys in columns < j plus those of waves < w in column j.
-template <int NT, int KPT>
-__device__ __forceinline__ void column_offsets(uint32_t (*cnt)[NT / 64], uint32_t* base) {
-  constexpr int NW = NT / 64;
-  const int tid = threadIdx.x;
-  __syncthreads();
-  for (int j = tid; j < KPT; j += NT) {
-    uint32_t acc = 0;
+__global__ __launch_bounds__(kTT) void topk_write_kernel(const TopkArgs a) {
+  __shared__ uint32_t wave_tot[kNW], res[2], red[kNW], eq_pre;
+  __shared__ uint32_t off_gt[kKPT * kNW], off_eq[kKPT * kNW];
+  const int c = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const RowWs w = row_ws(a, b);
+  uint32_t key[kKPT];
+  load_keys(a, b, c, key);
+  const uint32_t p24 = w.st[4], need2 = w.st[5];
+  uint32_t ab = 0;  // keys above T's top three bytes in the chunks before this one
+  for (int cc = tid; cc < c; cc += kTT) ab += w.above[cc];
+  const int L = row_len(a, b), K = a.k;
+  uint32_t tot, pre;
+  row_column_sums(a, w.h + (size_t)3 * a.n_chunks * kBins, L, c, tot, pre);
+  if (L <= K || c * kChunk >= L) return;
+  const uint32_t valid = valid_mask(c, L);
+  uint32_t need;
+  const uint32_t d0 = find_byte(tot, need2, wave_tot, res, need);
+  const uint32_t T = (p24 << 8) | d0;
+  const uint32_t bin = kBins - 1 - tid;
+  if (bin == d0) eq_pre = pre;
+  const uint32_t base_gt = block_sum(ab + (bin > d0 ? pre : 0u), red);  // syncs: eq_pre visible
+  const uint32_t base_eq = eq_pre;
+
+  // per (column j, wave) counts, then exclusive offsets in token order
+  uint64_t mg[kKPT], me[kKPT];
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const uint32_t c = cnt[j][w];
-      cnt[j][w] = acc;
-      acc += c;
+  for (int j = 0; j < kKPT; ++j) {
+    const bool v = (valid >> j) & 1u;
+    mg[j] = __ballot(v && key[j] > T);
+    me[j] = __ballot(v && key[j] == T);
+    if (lane == 0) {
+      off_gt[j * kNW + wave] = (uint32_t)__popcll(mg[j]);
+      off_eq[j * kNW + wave] = (uint32_t)__popcll(me[j]);
     }
-    base[j] = acc;
   }
   __syncthreads();
   if (tid < 64) {
-    // exclusive scan of the column totals, 64 lanes over KPT columns
-    constexpr int PER = (KPT + 63) / 64;
-    uint32_t c[PER], sum = 0;
+    constexpr int kE = kKPT * kNW;  // 32 entries, one per lane
+    const uint32_t g = lane < kE ? off_gt[lane] : 0u, e = lane < kE ? off_eq[lane] : 0u;
+    uint32_t ig = g, ie = e;
 #pragma unroll
-    for (int q = 0; q < PER; ++q) {
-      const int j = tid * PER + q;
-      c[q] = j < KPT ? base[j] : 0u;
-      sum += c[q];
+    for (int d = 1; d < kE; d <<= 1) {
+      const uint32_t yg = __shfl_up(ig, d), ye = __shfl_up(ie, d);
+      if (lane >= d) {
+        ig += yg;
+        ie += ye;
+      }
     }
-    uint32_t inc = sum;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const uint32_t y = __shfl_up(inc, d);
-      if (tid >= d) inc += y;
-    }
-    uint32_t acc = inc - sum;
-#pragma unroll
-    for (int q = 0; q < PER; ++q) {
-      const int j = tid * PER + q;
-      if (j < KPT) base[j] = acc;
-      acc += c[q];
+    if (lane < kE) {
+      off_gt[lane] = ig - g;
+      off_eq[lane] = ie - e;
     }
   }
   __syncthreads();
-}
-
-// Keys resident on chip: columns [0, RK) in registers, [RK, RK + LK) in LDS
-// (column c holds tokens c*NT .. c*NT + NT - 1, thread t owns token c*NT + t).
-constexpr int kNT = 1024;
-constexpr int kRK = 32;
-constexpr int kLK = 32;
-constexpr int kMaxCol = kRK + kLK;  // 65536 tokens
-constexpr int kNW = kNT / 64;
-constexpr size_t kResidentLds = (size_t)kLK * kNT * 4 + kBins * 4 + 2 * (size_t)kMaxCol * kNW * 4 +
-                                2 * kMaxCol * 4 + (kNW + 1) * 4 + 2 * kNW * 4 + 16;
-
-__global__ __launch_bounds__(kNT) void topk_kernel(const TopkArgs a) {
-  constexpr int NT = kNT, NW = kNW, BPT = kBins / NT;
-  extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
-  uint32_t* lds_keys = smem;                                     // [kLK][NT]
-  uint32_t* hist = lds_keys + kLK * NT;                          // [kBins]
-  uint32_t (*cnt_gt)[NW] = (uint32_t (*)[NW])(hist + kBins);     // [kMaxCol][NW]
-  uint32_t (*cnt_eq)[NW] = cnt_gt + kMaxCol;                     // [kMaxCol][NW]
-  uint32_t* base_gt = (uint32_t*)(cnt_eq + kMaxCol);             // [kMaxCol]
-  uint32_t* base_eq = base_gt + kMaxCol;                         // [kMaxCol]
-  uint32_t* wave_tot = base_eq + kMaxCol;                        // [NW + 1]
-  uint32_t* red = wave_tot + NW + 1;                             // [2 NW]
-  uint32_t* misc = red + 2 * NW;                                 // digit, need
-
-  const int b = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int L = a.seq_lens[b];
-  const int K = a.k;
-  const float* row = a.scores + (size_t)b * a.S_max;
-  int32_t* out = a.idx + (size_t)b * K;
-
-  if (L <= K) {
-    for (int j = tid; j < K; j += NT) out[j] = j < L ? j : -1;
-    return;
-  }
-  const int n_col = (L + NT - 1) / NT;
-  DATTN_TOPK_MARK(0);
-
-  // 1. one read of the row into order-preserving keys (0 past the row; real
-  //    keys are >= 1: only an all-ones NaN pattern maps to 0, moved to 1),
-  //    with the row's min and max
-  uint32_t rk[kRK];
-  uint32_t mn = 0xffffffffu, mx = 0u;
-  {
-    float x[kRK];
-#pragma unroll
-    for (int c = 0; c < kRK; ++c) x[c] = row[min(c * NT + tid, L - 1)];  // branch-free loads
-#pragma unroll
-    for (int c = 0; c < kRK; ++c) {
-      rk[c] = c * NT + tid < L ? max(order_key(x[c]), 1u) : 0u;
-      mn = min(mn, rk[c] ? rk[c] : 0xffffffffu);
-      mx = max(mx, rk[c]);
-    }
-    constexpr int LB = (kLK + 1) / 2;  // two batches of loads for the LDS columns
-    for (int c0 = kRK; c0 < n_col; c0 += LB) {
-      float y[LB];
-#pragma unroll
-      for (int u = 0; u < LB; ++u) y[u] = row[min((c0 + u) * NT + tid, L - 1)];
-#pragma unroll
-      for (int u = 0; u < LB; ++u) {
-        const int c = c0 + u;
-        const uint32_t k = c * NT + tid < L ? max(order_key(y[u]), 1u) : 0u;
-        mn = min(mn, k ? k : 0xffffffffu);
-        mx = max(mx, k);
-        if (c < n_col) lds_keys[(c - kRK) * NT + tid] = k;
-      }
-    }
-  }
-  // visit every resident key of this thread: f(key, column); LDS columns go
-  // in groups of 8 whose reads are issued together
-  auto for_each = [&](auto&& f) {
-#pragma unroll
-    for (int c = 0; c < kRK; ++c)
-      if (c < n_col) f(rk[c], c);
-    for (int c0 = kRK; c0 < n_col; c0 += 8) {
-      uint32_t y[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) y[u] = lds_keys[min(c0 + u - kRK, kLK - 1) * NT + tid];
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (c0 + u < n_col) f(y[u], c0 + u);
-    }
-  };
-  DATTN_TOPK_MARK(1);
-  uint32_t kmax;
-  const uint32_t kmin = block_reduce_min_max<NT>(mn, mx, red, kmax);
-  const uint32_t range = kmax - kmin;
-  DATTN_TOPK_MARK(2);
-
-  // 2. most significant digit first over v = key - kmin
-  int hi_bit = range ? 32 - __clz(range) : 0;
-  uint32_t prefix = 0, need = (uint32_t)K;
-  while (hi_bit > 0) {
-    const int width = hi_bit < kDigit ? hi_bit : kDigit;
-    const int lo_bit = hi_bit - width;
-    const uint32_t dmask = (1u << width) - 1u;
-    for (int i = tid; i < kBins; i += NT) hist[i] = 0;
-    __syncthreads();
-    for_each([&](uint32_t k, int) {
-      const uint32_t v = k - kmin;
-      if (k != 0u && (hi_bit >= 32 || (v >> hi_bit) == prefix)) atomicAdd(&hist[(v >> lo_bit) & dmask], 1u);
-    });
-    __syncthreads();
-    // scan the bins from the top: thread t holds bins 4095-BPT*t downwards
-    uint32_t cb[BPT], sum = 0;
-#pragma unroll
-    for (int q = 0; q < BPT; ++q) {
-      cb[q] = hist[kBins - 1 - BPT * tid - q];
-      sum += cb[q];
-    }
-    uint32_t tot;
-    const uint32_t before = block_exclusive_scan<NT>(sum, wave_tot, tot);
-    if (before < need && before + sum >= need) {
-      uint32_t acc = before;
-#pragma unroll
-      for (int q = 0; q < BPT; ++q) {
-        if (acc + cb[q] >= need) {
-          misc[0] = kBins - 1 - BPT * tid - q;
-          misc[1] = need - acc;
-          break;
-        }
-        acc += cb[q];
-      }
-    }
-    __syncthreads();
-    prefix = (prefix << width) | misc[0];
-    need = misc[1];
-    hi_bit = lo_bit;
-    __syncthreads();
-  }
-  const uint32_t vT = prefix;  // the k-th largest key is kmin + vT
-  DATTN_TOPK_MARK(3);
-
-  // 3. ordered compaction.  A key above T is taken; of the keys equal to T
-  //    the first `need` in index order are taken.  Its output position is
-  //    (keys above T before it) + min(keys equal to T before it, need).
   const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
-  for_each([&](uint32_t k, int c) {
-    const uint32_t v = k - kmin;
-    const uint64_t mg = __ballot(k != 0u && v > vT);
-    const uint64_t me = __ballot(k != 0u && v == vT);
-    if (lane == 0) {
-      cnt_gt[c][wave] = (uint32_t)__popcll(mg);
-      cnt_eq[c][wave] = (uint32_t)__popcll(me);
-    }
-  });
-  column_offsets<NT, kMaxCol>(cnt_gt, base_gt);
-  column_offsets<NT, kMaxCol>(cnt_eq, base_eq);
-  DATTN_TOPK_MARK(4);
-  for_each([&](uint32_t k, int c) {
-    const uint32_t v = k - kmin;
-    const bool gt = k != 0u && v > vT, eq = k != 0u && v == vT;
-    const uint64_t mg = __ballot(gt);
-    const uint64_t me = __ballot(eq);
-    const uint32_t r_gt = base_gt[c] + cnt_gt[c][wave] + (uint32_t)__popcll(mg & below);
-    const uint32_t r_eq = base_eq[c] + cnt_eq[c][wave] + (uint32_t)__popcll(me & below);
+  int32_t* out = a.idx + (size_t)b * K;
+  const int t0 = c * kChunk + tid;
+#pragma unroll
+  for (int j = 0; j < kKPT; ++j) {
+    const bool v = (valid >> j) & 1u;
+    const bool gt = v && key[j] > T, eq = v && key[j] == T;
+    const uint32_t r_gt = base_gt + off_gt[j * kNW + wave] + (uint32_t)__popcll(mg[j] & below);
+    const uint32_t r_eq = base_eq + off_eq[j * kNW + wave] + (uint32_t)__popcll(me[j] & below);
     if (gt || (eq && r_eq < need)) {
       const uint32_t pos = r_gt + min(r_eq, need);
-      if (pos < (uint32_t)K) out[pos] = c * NT + tid;  // always true when the select is right
-    }
-  });
-  DATTN_TOPK_MARK(5);
-}
-
-// Streaming variant for rows longer than 1024 * 64 tokens: 8-bit digits over
-// the raw key, scores re-read from memory every pass.
-__global__ __launch_bounds__(kThreads) void topk_stream_kernel(const TopkArgs a) {
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t wave_tot[kWaves + 1];
-  __shared__ uint32_t s_digit, s_need;
-
-  const int b = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int L = a.seq_lens[b];
-  const int K = a.k;
-  const float* row = a.scores + (size_t)b * a.S_max;
-  int32_t* out = a.idx + (size_t)b * K;
-
-  if (L <= K) {
-    for (int j = tid; j < K; j += kThreads) out[j] = j < L ? j : -1;
-    return;
-  }
-  uint32_t prefix = 0, mask = 0, need = (uint32_t)K;
-#pragma unroll 1
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    for (int i = tid; i < 256; i += kThreads) hist[i] = 0;
-    __syncthreads();
-    for (int base = 0; base < L; base += kThreads) {
-      const int t = base + tid;
-      bool act = false;
-      uint32_t d = 0;
-      if (t < L) {
-        const uint32_t key = order_key(row[t]);
-        act = (key & mask) == prefix;
-        d = (key >> shift) & 255u;
-      }
-      const uint64_t actm = __ballot(act);
-      if (actm == 0) continue;
-      const int first = __ffsll((long long)actm) - 1;
-      const uint32_t d0 = __shfl(d, first);
-      const uint64_t same = __ballot(act && d == d0);
-      if (same == actm) {
-        if (lane == first) atomicAdd(&hist[d0], (uint32_t)__popcll(same));
-      } else if (act) {
-        atomicAdd(&hist[d], 1u);
-      }
-    }
-    __syncthreads();
-    if (tid < 64) {
-      uint32_t c[4], sum = 0;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        c[q] = hist[255 - 4 * tid - q];
-        sum += c[q];
-      }
-      uint32_t inc = sum;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const uint32_t y = __shfl_up(inc, d);
-        if (tid >= d) inc += y;
-      }
-      const uint32_t before = inc - sum;
-      if (before < need && inc >= need) {
-        uint32_t acc = before;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if (acc + c[q] >= need) {
-            s_digit = 255 - 4 * tid - q;
-            s_need = need - acc;
-            break;
-          }
-          acc += c[q];
-        }
-      }
-    }
-    __syncthreads();
-    prefix |= s_digit << shift;
-    mask |= 255u << shift;
-    need = s_need;
-    __syncthreads();
-  }
-  const uint32_t T = prefix;
-  const int chunk = (L + kThreads - 1) / kThreads;
-  const int lo = min(L, tid * chunk), hi = min(L, lo + chunk);
-  uint32_t n_gt = 0, n_eq = 0;
-  for (int t = lo; t < hi; ++t) {
-    const uint32_t key = order_key(row[t]);
-    n_gt += key > T;
-    n_eq += key == T;
-  }
-  uint32_t tot;
-  const uint32_t gt_before = block_exclusive_scan<kThreads>(n_gt, wave_tot, tot);
-  const uint32_t eq_before = block_exclusive_scan<kThreads>(n_eq, wave_tot, tot);
-  uint32_t pos = gt_before + min(eq_before, need);
-  uint32_t eq_seen = eq_before;
-  for (int t = lo; t < hi; ++t) {
-    const uint32_t key = order_key(row[t]);
-    bool take = key > T;
-    if (key == T) take = eq_seen++ < need;
-    if (take) {
-      if (pos < (uint32_t)K) out[pos] = t;
-      ++pos;
+      if (pos < (uint32_t)K) out[pos] = t0 + j * kTT;  // always true when the select is right
     }
   }
 }
 
 }  // namespace
 
-hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
-  if (a.S_max <= kMaxCol * kNT) {
-    static bool configured = false;
-    if (!configured) {
-      hipError_t e = hipFuncSetAttribute((const void*)topk_kernel,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)kResidentLds);
-      if (e != hipSuccess) return e;
-      configured = true;
-    }
-    topk_kernel<<<a.B, kNT, kResidentLds, s>>>(a);
-  } else {
-    topk_stream_kernel<<<a.B, kThreads, 0, s>>>(a);
-  }
+size_t topk_workspace_bytes(int B, int S_max) {
+  const int nc = (S_max + kChunk - 1) / kChunk;
+  return ((size_t)B * topk_row_words(nc) * 4 + 255) & ~(size_t)255;
+}
+
+hipError_t launch_topk(const TopkArgs& a0, hipStream_t s) {
+  TopkArgs a = a0;
+  a.n_chunks = (a.S_max + kChunk - 1) / kChunk;
+  a.row_words = (int64_t)topk_row_words(a.n_chunks);
+  const dim3 grid(a.n_chunks, a.B);
+  topk_digit_kernel<0><<<grid, kTT, 0, s>>>(a);
+  topk_digit_kernel<1><<<grid, kTT, 0, s>>>(a);
+  topk_digit_kernel<2><<<grid, kTT, 0, s>>>(a);
+  topk_digit_kernel<3><<<grid, kTT, 0, s>>>(a);
+  topk_write_kernel<<<grid, kTT, 0, s>>>(a);
   return hipGetLastError();
 }
 

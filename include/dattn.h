@@ -128,8 +128,8 @@ DATTN_EXPORT size_t decode_attn_gqa_workspace(int32_t B, int32_t Hq, int32_t Hkv
  *   S_max        contiguous: rows per sequence; paged: page_size * max_pages
  *   page_size    paged: a power of two; ignored when page_table == NULL
  *   scale        <= 0 means 1/sqrt(192) (DeepSeek-V3: 128 + 64 qk dims)
- *   num_splits   0 = automatic; a split holds at most 4032 tokens, so a
- *                smaller count is raised to ceil(S_max / 4032) (at most 256)
+ *   num_splits   0 = automatic; a split holds at most 3840 tokens, so a
+ *                smaller count is raised to ceil(S_max / 3840) (at most 256)
  *   workspace    decode_attn_mla_workspace bytes (never 0: the splits' partial
  *                results always go through it)
  * The cache must hold fewer than 2^31 rows (B * S_max contiguous, num_pages *
@@ -166,7 +166,13 @@ DATTN_EXPORT size_t decode_attn_mla_workspace(int32_t B, int32_t H, int32_t d_la
  *   topk_idx   int32 [B, k] (written)
  *   scores_out fp32 [B, S_max] or NULL; when given, receives the scores
  *              (entries t >= seq_lens[b] are -inf)
- *   Hi a multiple of 32 (<= 128), Di = 128, dtype DATTN_BF16
+ *   Hi a multiple of 32 (<= 128), Di = 128, dtype DATTN_BF16, B <= 65535,
+ *   S_max <= 2^30
+ *   workspace  dsa_indexer_topk_workspace(B, S_max, k) bytes, 256-byte
+ *              aligned, always required (the selection keeps histograms and
+ *              per-chunk counts there; the first B*S_max*4 bytes, rounded up
+ *              to 256, hold the scores when scores_out is NULL).  Its contents
+ *              need no initialisation and are not meaningful afterwards.
  * Integer-valued inputs with |sum| < 2^24 give exact scores and therefore an
  * exact, reproducible selection.
  */
@@ -180,7 +186,10 @@ DATTN_EXPORT size_t dsa_indexer_topk_workspace(int32_t B, int32_t S_max, int32_t
 /* The selection step alone, on caller-provided fp32 scores [B, S_max]:
  * the k largest of scores[b, 0:seq_lens[b]], ties to the lower index,
  * ascending, -1 padded.  -0.0 and +0.0 are equal; NaN scores are not
- * supported (their position in the order is unspecified).  1 <= k <= 16384. */
+ * supported (their position in the order is unspecified).  1 <= k <= 16384,
+ * B <= 65535, S_max <= 2^30.  The workspace (dsa_topk_workspace bytes,
+ * 256-byte aligned, no initialisation needed) holds four 256-bin radix
+ * histograms and one count per 2048-token chunk of each row. */
 DATTN_EXPORT int dsa_topk(const float* scores, const int32_t* seq_lens, int32_t k, int32_t* topk_idx,
              int32_t B, int32_t S_max, void* workspace, size_t workspace_bytes, void* stream);
 

@@ -116,9 +116,17 @@ def test_dsa_validation():
     assert call(args(Hi=48)) == -2
     assert call(args(dt=0)) == -2
     assert call(args()) == -3                     # no scores buffer, no workspace
-    assert L.dsa_indexer_topk_workspace(8, 65536, 2048) == 8 * 65536 * 4
+    assert call(args(), scores=P(1)) == -3        # the selection always needs one
+    # top-k workspace per row: 4 x 256 + 1 words per 2048-token chunk + 8, rounded to 64 words
+    topk_ws = 8 * (((32 * 1025 + 8) + 63) // 64 * 64) * 4
+    assert L.dsa_topk_workspace(8, 65536, 2048) == topk_ws
+    assert L.dsa_indexer_topk_workspace(8, 65536, 2048) == 8 * 65536 * 4 + topk_ws
     assert L.dsa_topk(P(1), P(1), 0, P(1), 8, 100, None, 0, None) == -1
     assert L.dsa_topk(None, P(1), 4, P(1), 8, 100, None, 0, None) == -1
+    assert L.dsa_topk(P(1), P(1), 4, P(1), 70000, 100, None, 0, None) == -1   # B > 65535
+    assert L.dsa_topk(P(1), P(1), 4, P(1), 8, (1 << 30) + 1, None, 0, None) == -1
+    assert L.dsa_topk(P(1), P(1), 4, P(1), 8, 100, None, 0, None) == -3     # no workspace
+    assert L.dsa_topk(P(1), P(1), 4, P(1), 8, 100, P(256), 16, None) == -3  # too small
 
 
 def test_profile_calls_without_gpu():

@@ -73,6 +73,35 @@ def test_topk_alone(n_distinct, k):
     assert torch.equal(got, want)
 
 
+@pytest.mark.parametrize("n_distinct", [None, 1, 2])
+@pytest.mark.parametrize("k", [2048, 16384])
+def test_topk_long_and_ragged_rows(n_distinct, k):
+    """Rows of several 2048-token chunks with a ragged last chunk, longer than
+    65536, shorter than k, empty, and all-equal rows (every key ties)."""
+    lens = [131073, 70001, 16384, 16385, 2047, 0, 40000]
+    say(f"[dsa] topk lens={lens} k={k} n_distinct={n_distinct}")
+    s = wl.make_scores(B=len(lens), seq_lens=lens, n_distinct=n_distinct, seed=k + 7)
+    sl = torch.tensor(lens, dtype=torch.int32)
+    got = api.dsa_topk(dev(s), dev(sl), k).cpu()
+    want = oracle.topk(s, sl, k)
+    assert torch.equal(got, want)
+
+
+def test_topk_ignores_workspace_contents():
+    """The workspace holds no state between calls: garbage in it changes nothing."""
+    lens = [9000, 20000, 5]
+    s = wl.make_scores(B=3, seq_lens=lens, n_distinct=40, seed=3)
+    sl = dev(torch.tensor(lens, dtype=torch.int32))
+    k = 1000
+    nbytes = api.lib().dsa_topk_workspace(3, s.shape[1], k)
+    ws = torch.full((nbytes,), 0xAB, dtype=torch.uint8, device="cuda")
+    out = torch.empty(3, k, dtype=torch.int32, device="cuda")
+    api._check(api.lib().dsa_topk(api._ptr(dev(s)), api._ptr(sl), k, api._ptr(out), 3, s.shape[1],
+                                  api._ptr(ws), nbytes, None))
+    torch.cuda.synchronize()
+    assert torch.equal(out.cpu(), oracle.topk(s, sl.cpu(), k))
+
+
 def test_topk_run_to_run_identical():
     s = wl.make_scores(B=4, seq_lens=[30000] * 4, n_distinct=7, seed=9)
     sl = torch.tensor([30000] * 4, dtype=torch.int32)
