@@ -11,20 +11,22 @@
 //
 // Work is cut into 16-token blocks aligned to the page (a paged cache with
 // page_size a multiple of 16, or a contiguous cache): the page of a block is
-// one wave-uniform table lookup, and a lane's addresses are fixed offsets
-// from it.  The set's partial first and last blocks are masked per token.
-// Inside a workgroup each wave streams its own blocks:
-//   * eight lanes cover a 128-byte segment of a token row (16 bytes each), so
-//     one wave load instruction reads eight full 128-byte lines, and a lane
-//     holds D*size/128 segments of two tokens per block;
+// one wave-uniform scalar table lookup, and a lane's addresses are fixed
+// offsets from it.  The set's partial first and last blocks are masked per
+// token.  Inside a workgroup each wave streams its own blocks:
+//   * a lane holds one 16-byte piece of a token row: LPR = row bytes / 16
+//     lanes cover a row, one wave load instruction reads 64 / LPR whole rows,
+//     and a lane holds 16 * LPR / 64 rows of a block for K and as many for V;
+//   * two register buffers per wave: the loads of the wave's next block are
+//     in flight while it computes the current one;
 //   * scores are lane-partial dot products (v_dot2_f32_bf16 for bf16: the
-//     bf16 products are exact in fp32) summed over the 8 lanes with DPP;
+//     bf16 products are exact in fp32) summed over the row's lanes with DPP;
 //   * the softmax is the online one ("All the attentions", section 1: a
 //     running maximum and running sum, earlier partials rescaled), kept per
-//     token row of the wave; the reference maximum only moves when the new
-//     maximum exceeds it by more than 2^8, which bounds every exponential by
-//     2^8 and makes rescaling rare without changing the result;
-//   * P.V: for bf16 the two tokens' probabilities are rounded to bf16 and
+//     lane; the reference maximum only moves when the new maximum exceeds it
+//     by more than 2^8, which bounds every exponential by 2^8 and makes
+//     rescaling rare without changing the result;
+//   * P.V: for bf16 the probabilities of two tokens are rounded to bf16 and
 //     paired with the two tokens' values in one v_dot2_f32_bf16 per output
 //     (fp32 accumulation); for fp32 inputs it is plain fp32 FMA.
 // A split's result is (o / l, log2-sum-exp); lse_combine merges the splits
@@ -37,38 +39,40 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kStep = 16;     // tokens per wave step
+constexpr int kStep = 16;     // tokens per wave step (one block)
 constexpr float kTau = 8.0f;  // lazy-rescale threshold (log2 units)
-#ifndef DATTN_GQA_UNROLL
-#define DATTN_GQA_UNROLL 1
-#endif
-constexpr int kUnroll = DATTN_GQA_UNROLL;  // blocks whose loads a wave issues together
 
 template <bool BF16, int D>
 struct GqaShape {
   static constexpr int ESZ = BF16 ? 2 : 4;   // bytes per element
-  static constexpr int VEC = 16 / ESZ;       // elements per 16-byte piece
-  static constexpr int SEG = 128 / ESZ;      // elements per 128-byte segment
-  static constexpr int NH = D / SEG;         // 128-byte segments per row
-  static constexpr int DL = VEC * NH;        // dims a lane holds per token
-  static_assert(NH >= 1 && D % SEG == 0, "row split");
+  static constexpr int VEC = 16 / ESZ;       // elements of a row one lane holds
+  static constexpr int LPR = D / VEC;        // lanes per token row
+  static constexpr int RPI = 64 / LPR;       // token rows per wave load
+  static constexpr int TPL = kStep / RPI;    // token rows per lane per block
+  static_assert(D % VEC == 0 && LPR >= 8 && LPR <= 32 && TPL % 2 == 0, "row split");
 };
 
-template <bool BF16, int VEC>
-__device__ __forceinline__ void widen(const uint4& x, float (&f)[VEC]) {
-  if constexpr (BF16) {
-    f[0] = bf16_lo(x.x); f[1] = bf16_hi(x.x);
-    f[2] = bf16_lo(x.y); f[3] = bf16_hi(x.y);
-    f[4] = bf16_lo(x.z); f[5] = bf16_hi(x.z);
-    f[6] = bf16_lo(x.w); f[7] = bf16_hi(x.w);
-  } else {
-    f[0] = __uint_as_float(x.x); f[1] = __uint_as_float(x.y);
-    f[2] = __uint_as_float(x.z); f[3] = __uint_as_float(x.w);
-  }
-}
+// One block of K and V held by a lane: TPL token rows, one 16-byte piece each.
+template <int TPL>
+struct KvRegs {
+  uint4 k[TPL], v[TPL];
+};
+
+typedef const int32_t __attribute__((address_space(4))) cint32_t;
 
 __device__ __forceinline__ uint32_t u4(const uint4& x, int w) {
   return w == 0 ? x.x : w == 1 ? x.y : w == 2 ? x.z : x.w;
+}
+
+template <int N>
+__device__ __forceinline__ float row_sum(float x) {
+  if constexpr (N == 8 || N == 16) {
+    return group_sum<N>(x);
+  } else {
+    static_assert(N == 32, "lanes per row");
+    x = group_sum<16>(x);
+    return x + __shfl_xor(x, 16);
+  }
 }
 
 // PAGED_FAST: paged with page_size % 16 == 0, or contiguous (one lookup per
@@ -76,13 +80,13 @@ __device__ __forceinline__ uint32_t u4(const uint4& x, int w) {
 template <bool BF16, int D, int G, bool PAGED_FAST>
 __global__ __launch_bounds__(kThreads) void gqa_split_kernel(const GqaArgs a) {
   using S = GqaShape<BF16, D>;
-  constexpr int VEC = S::VEC, SEG = S::SEG, NH = S::NH, DL = S::DL;
+  constexpr int VEC = S::VEC, LPR = S::LPR, RPI = S::RPI, TPL = S::TPL;
   const float NEG_INF = -__builtin_inff();
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int r = lane >> 3;   // token row within an 8-row load
-  const int c = lane & 7;    // 16-byte column within a 128-byte segment
+  const int r = lane / LPR;  // token row within one wave load
+  const int c = lane % LPR;  // 16-byte piece of the row
   const int split = blockIdx.x;
   const int kvh = blockIdx.y;
   const int b = blockIdx.z;
@@ -103,176 +107,177 @@ __global__ __launch_bounds__(kThreads) void gqa_split_kernel(const GqaArgs a) {
   const int blk_begin = min(n_blocks, split * per);
   const int blk_end = min(n_blocks, blk_begin + per);
 
-  // This lane's pieces of the G query rows: dims hh*SEG + c*VEC + [0, VEC).
-  uint4 qv[G][NH];
+  // This lane's piece of each of the G query rows: dims c*VEC + [0, VEC).
+  uint4 qv[G];
   {
     const char* qb = (const char*)a.q + ((size_t)(b * a.Hq + kvh * G) * D + c * VEC) * S::ESZ;
 #pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int hh = 0; hh < NH; ++hh)
-        qv[h][hh] = *(const uint4*)(qb + ((size_t)h * D + hh * SEG) * S::ESZ);
+    for (int h = 0; h < G; ++h) qv[h] = *(const uint4*)(qb + (size_t)h * D * S::ESZ);
   }
 
-  float m[G], l[G], o[G][DL];
+  float m[G], l[G], o[G][VEC];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     m[h] = NEG_INF;
     l[h] = 0.f;
 #pragma unroll
-    for (int e = 0; e < DL; ++e) o[h][e] = 0.f;
+    for (int e = 0; e < VEC; ++e) o[h][e] = 0.f;
   }
 
   const size_t head_stride = (size_t)a.page_size * D;
   const size_t page_stride = (size_t)a.Hkv * head_stride;
   const char* kb = (const char*)a.k;
   const char* vb = (const char*)a.v;
-  const int32_t* pt = a.page_table ? a.page_table + (size_t)b * a.max_pages : nullptr;
+  // The page table is read-only for the whole launch: reading it through the
+  // constant address space lets wave-uniform lookups become scalar loads.
+  const cint32_t* pt = a.page_table ? (const cint32_t*)(uintptr_t)(a.page_table + (size_t)b * a.max_pages)
+                                    : nullptr;
   const size_t contig_base = ((size_t)b * a.Hkv + kvh) * head_stride;
-  const size_t lane_off = (size_t)c * VEC * S::ESZ;
+  const size_t lane_off = (size_t)c * 16;
 
   auto block_start = [&](int blk) {
     return blk < n_sb ? blk * kStep : (wb0 + blk - n_sb) * kStep;
   };
-  // physical page of the next block, loaded one block ahead
-  int phys_next = 0;
-  if (PAGED_FAST && pt && blk_begin + wave < blk_end)
-    phys_next = pt[block_start(blk_begin + wave) >> a.log2_page];
+  // Attended token range [lo, hi) inside block blk (never empty for a block
+  // below blk_end).
+  auto block_range = [&](int blk, int t0, int& lo, int& hi) {
+    const bool sink = blk < n_sb;
+    lo = max(sink ? 0 : w_start, t0);
+    hi = min(sink ? s_cnt : L, t0 + kStep);
+  };
+  // Physical page of a block (wave-uniform; PAGED_FAST with a page table).
+  auto page_of = [&](int blk) { return (int)pt[block_start(blk) >> a.log2_page]; };
 
-  for (int blk0 = blk_begin + wave; blk0 < blk_end; blk0 += kWaves * kUnroll) {
-    // issue the loads of kUnroll blocks of this wave, then compute them
-    uint4 kr[kUnroll][2][NH], vr[kUnroll][2][NH];
-    bool valid[kUnroll][2];
-#pragma unroll
-    for (int x = 0; x < kUnroll; ++x) {
-      const int blk = blk0 + x * kWaves;
-      const bool live = blk < blk_end;
-      const bool sink = blk < n_sb;
-      const int t0 = block_start(blk);
-      const int lo = sink ? 0 : w_start;
-      const int hi = live ? (sink ? s_cnt : L) : 0;
-      size_t base_fast = 0;
-      if constexpr (PAGED_FAST) {
-        if (pt) {
-          const int phys = phys_next;
-          if (blk + kWaves < blk_end) phys_next = pt[block_start(blk + kWaves) >> a.log2_page];
-          base_fast = (size_t)phys * page_stride + (size_t)kvh * head_stride +
-                      (size_t)(t0 & (a.page_size - 1)) * D;
-        } else {
-          base_fast = contig_base + (size_t)t0 * D;
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int t = t0 + 8 * u + r;
-        valid[x][u] = t >= lo && t < hi;
-        size_t off;
-        if constexpr (PAGED_FAST) {
-          off = (base_fast + (size_t)(8 * u + r) * D) * S::ESZ + lane_off;
-        } else {
-          const int phys = valid[x][u] ? pt[t >> a.log2_page] : 0;
-          off = ((size_t)phys * page_stride + (size_t)kvh * head_stride +
-                 (size_t)(t & (a.page_size - 1)) * D) * S::ESZ + lane_off;
-        }
-#pragma unroll
-        for (int hh = 0; hh < NH; ++hh) {
-          if (valid[x][u]) {
-            kr[x][u][hh] = load_stream(kb + off + hh * 128);
-            vr[x][u][hh] = load_stream(vb + off + hh * 128);
-          } else {
-            kr[x][u][hh] = make_uint4(0u, 0u, 0u, 0u);
-            vr[x][u][hh] = make_uint4(0u, 0u, 0u, 0u);
-          }
-        }
-      }
+  // Issue the K/V loads of block blk (< blk_end) into R.  A lane whose token
+  // is outside the attended range loads the nearest attended row of the block
+  // instead: every address stays inside a page the table names (or inside the
+  // contiguous sequence), nothing past L_b is read, and the row is masked at
+  // compute time, so the loads need no branches.
+  auto issue = [&](int blk, int phys, KvRegs<TPL>& R) {
+    const int t0 = block_start(blk);
+    int lo, hi;
+    block_range(blk, t0, lo, hi);
+    size_t base_fast = 0;
+    if constexpr (PAGED_FAST) {
+      base_fast = pt ? (size_t)phys * page_stride + (size_t)kvh * head_stride + (size_t)(t0 & (a.page_size - 1)) * D
+                     : contig_base + (size_t)t0 * D;
     }
+#pragma unroll
+    for (int u = 0; u < TPL; ++u) {
+      const int t = min(max(t0 + u * RPI + r, lo), hi - 1);
+      size_t off;
+      if constexpr (PAGED_FAST) {
+        off = (base_fast + (size_t)(t - t0) * D) * S::ESZ + lane_off;
+      } else {
+        const int ph = a.page_table[(size_t)b * a.max_pages + (t >> a.log2_page)];
+        off = ((size_t)ph * page_stride + (size_t)kvh * head_stride + (size_t)(t & (a.page_size - 1)) * D) *
+                  S::ESZ + lane_off;
+      }
+      R.k[u] = load_stream(kb + off);
+      R.v[u] = load_stream(vb + off);
+    }
+  };
 
+  // Scores, online softmax and P.V of block blk held in R; a block at or
+  // past blk_end is empty (every row masked).
+  auto compute = [&](int blk, const KvRegs<TPL>& R) {
+    const int t0 = block_start(blk);
+    int lo, hi;
+    block_range(blk, t0, lo, hi);
+    if (blk >= blk_end) hi = lo;
+    // scores (log2 units) of the lane's TPL tokens
+    float s[TPL][G];
 #pragma unroll
-    for (int x = 0; x < kUnroll; ++x) {
-    // scores (log2 units) of the lane's two tokens
-    float s[2][G];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < TPL; ++u) {
+      const int t = t0 + u * RPI + r;
+      const bool valid = t >= lo && t < hi;
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        float acc = 0.f;
-#pragma unroll
-        for (int hh = 0; hh < NH; ++hh) {
-          if constexpr (BF16) {
-            acc = dot2_bf16(kr[x][u][hh].x, qv[h][hh].x, acc);
-            acc = dot2_bf16(kr[x][u][hh].y, qv[h][hh].y, acc);
-            acc = dot2_bf16(kr[x][u][hh].z, qv[h][hh].z, acc);
-            acc = dot2_bf16(kr[x][u][hh].w, qv[h][hh].w, acc);
-          } else {
-            acc = fmaf(__uint_as_float(kr[x][u][hh].x), __uint_as_float(qv[h][hh].x), acc);
-            acc = fmaf(__uint_as_float(kr[x][u][hh].y), __uint_as_float(qv[h][hh].y), acc);
-            acc = fmaf(__uint_as_float(kr[x][u][hh].z), __uint_as_float(qv[h][hh].z), acc);
-            acc = fmaf(__uint_as_float(kr[x][u][hh].w), __uint_as_float(qv[h][hh].w), acc);
-          }
+        float acc;
+        if constexpr (BF16) {
+          acc = dot2_bf16(R.k[u].x, qv[h].x, 0.f);
+          acc = dot2_bf16(R.k[u].y, qv[h].y, acc);
+          acc = dot2_bf16(R.k[u].z, qv[h].z, acc);
+          acc = dot2_bf16(R.k[u].w, qv[h].w, acc);
+        } else {
+          acc = __uint_as_float(R.k[u].x) * __uint_as_float(qv[h].x);
+          acc = fmaf(__uint_as_float(R.k[u].y), __uint_as_float(qv[h].y), acc);
+          acc = fmaf(__uint_as_float(R.k[u].z), __uint_as_float(qv[h].z), acc);
+          acc = fmaf(__uint_as_float(R.k[u].w), __uint_as_float(qv[h].w), acc);
         }
-        acc = group_sum<8>(acc) * a.scale_log2;
-        s[u][h] = valid[x][u] ? acc : NEG_INF;
+        acc = row_sum<LPR>(acc) * a.scale_log2;
+        s[u][h] = valid ? acc : NEG_INF;
       }
     }
 
     // online softmax with a lazily moved reference maximum
-    float p[2][G];
+    float p[TPL][G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float mx = fmaxf(s[0][h], s[1][h]);
+      float mx = s[0][h];
+#pragma unroll
+      for (int u = 1; u < TPL; ++u) mx = fmaxf(mx, s[u][h]);
       if (mx > m[h] + kTau) {
         const float alpha = fast_exp2(m[h] - mx);  // 0 when m was -inf
         l[h] *= alpha;
 #pragma unroll
-        for (int e = 0; e < DL; ++e) o[h][e] *= alpha;
+        for (int e = 0; e < VEC; ++e) o[h][e] *= alpha;
         m[h] = mx;
       }
       const float mu = m[h] == NEG_INF ? 0.f : m[h];
-      p[0][h] = fast_exp2(s[0][h] - mu);
-      p[1][h] = fast_exp2(s[1][h] - mu);
-      l[h] += p[0][h] + p[1][h];
+      float ls = 0.f;
+#pragma unroll
+      for (int u = 0; u < TPL; ++u) {
+        p[u][h] = fast_exp2(s[u][h] - mu);
+        ls += p[u][h];
+      }
+      l[h] += ls;
     }
 
-    // P.V
+    // P.V (a masked row has p = 0 and finite values: it adds nothing)
     if constexpr (BF16) {
-      uint32_t pp[G];
 #pragma unroll
-      for (int h = 0; h < G; ++h) pp[h] = pack_bf16x2(p[0][h], p[1][h]);
+      for (int u = 0; u < TPL; u += 2) {
+        uint32_t pp[G];
 #pragma unroll
-      for (int hh = 0; hh < NH; ++hh) {
+        for (int h = 0; h < G; ++h) pp[h] = pack_bf16x2(p[u][h], p[u + 1][h]);
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          const uint32_t a0 = u4(vr[x][0][hh], w), a1 = u4(vr[x][1][hh], w);
+          const uint32_t a0 = u4(R.v[u], w), a1 = u4(R.v[u + 1], w);
           const uint32_t plo = pair_lo(a0, a1), phi = pair_hi(a0, a1);
-          const int e = hh * VEC + 2 * w;
 #pragma unroll
           for (int h = 0; h < G; ++h) {
-            o[h][e] = dot2_bf16(pp[h], plo, o[h][e]);
-            o[h][e + 1] = dot2_bf16(pp[h], phi, o[h][e + 1]);
+            o[h][2 * w] = dot2_bf16(pp[h], plo, o[h][2 * w]);
+            o[h][2 * w + 1] = dot2_bf16(pp[h], phi, o[h][2 * w + 1]);
           }
         }
       }
     } else {
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int u = 0; u < TPL; ++u) {
 #pragma unroll
-        for (int hh = 0; hh < NH; ++hh) {
-          float vf[VEC];
-          widen<BF16, VEC>(vr[x][u][hh], vf);
+        for (int h = 0; h < G; ++h)
 #pragma unroll
-          for (int h = 0; h < G; ++h)
-#pragma unroll
-            for (int e = 0; e < VEC; ++e)
-              o[h][hh * VEC + e] = fmaf(p[u][h], vf[e], o[h][hh * VEC + e]);
-        }
+          for (int e = 0; e < VEC; ++e) o[h][e] = fmaf(p[u][h], __uint_as_float(u4(R.v[u], e)), o[h][e]);
       }
     }
-    }
+  };
+
+  // One block per wave step: its page (a scalar load) is looked up one step
+  // ahead; the waves of the CU overlap each other's loads and arithmetic.
+  const bool paged_lookup = PAGED_FAST && pt;
+  int blk = __builtin_amdgcn_readfirstlane(blk_begin + wave);
+  int ph = paged_lookup && blk < blk_end ? page_of(blk) : 0;
+  for (; blk < blk_end; blk += kWaves) {
+    KvRegs<TPL> R;
+    issue(blk, ph, R);
+    if (paged_lookup && blk + kWaves < blk_end) ph = page_of(blk + kWaves);
+    compute(blk, R);
   }
 
-  // merge the 8 token rows of the wave (lanes c, c+8, ...)
+  // merge the token rows of the wave (lanes c, c + LPR, ...)
 #pragma unroll
-  for (int d = 8; d < 64; d <<= 1) {
+  for (int d = LPR; d < 64; d <<= 1) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const float mo = __shfl_xor(m[h], d);
@@ -282,7 +287,7 @@ __global__ __launch_bounds__(kThreads) void gqa_split_kernel(const GqaArgs a) {
       const float a1 = fast_exp2(m[h] - mu), a2 = fast_exp2(mo - mu);
       l[h] = l[h] * a1 + lo * a2;
 #pragma unroll
-      for (int e = 0; e < DL; ++e) o[h][e] = o[h][e] * a1 + __shfl_xor(o[h][e], d) * a2;
+      for (int e = 0; e < VEC; ++e) o[h][e] = o[h][e] * a1 + __shfl_xor(o[h][e], d) * a2;
       m[h] = mn;
     }
   }
@@ -294,9 +299,7 @@ __global__ __launch_bounds__(kThreads) void gqa_split_kernel(const GqaArgs a) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
 #pragma unroll
-      for (int hh = 0; hh < NH; ++hh)
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) sm_o[wave][h][hh * SEG + c * VEC + e] = o[h][hh * VEC + e];
+      for (int e = 0; e < VEC; ++e) sm_o[wave][h][c * VEC + e] = o[h][e];
       if (c == 0) {
         sm_m[wave][h] = m[h];
         sm_l[wave][h] = l[h];
