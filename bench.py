@@ -204,8 +204,10 @@ def tflops(flops, us):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    # the GPU's clocks take ~20 ms of sustained work to ramp up after idling
+    # (input generation runs on the CPU); 300 calls cover that
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--quick", action="store_true", help="headline workload only")
     ap.add_argument("--only", choices=["gqa", "swa", "mla", "dsa"],
                     help="time one workload and print its record (for profiling runs)")

@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -67,7 +68,9 @@ hipEvent_t pool_get() {
     return e;
   }
   hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  // timing events without the system-scope cache flush a default event
+  // performs: less added time around the kernel they bracket
+  if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
   return e;
 }
 
@@ -94,17 +97,14 @@ int plan_gqa_splits(int32_t B, int32_t Hkv, int64_t max_tokens, int32_t req, int
 // Resident split-kernel workgroups on the current device; 3 per CU on 256
 // CUs when the device cannot be queried.
 int64_t gqa_slots(bool bf16, int D, int G, bool paged, int page_size) {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-    cus = 256;
+  const int cus = dattn::device_cu_count();
   int per = dattn::gqa_blocks_per_cu(bf16, D, G, paged, page_size);
   if (per < 1) per = 3;
   return (int64_t)per * cus;
 }
 
 // MLA workgroups (128 or 64 heads each, 127 KB of LDS) run one per CU: aim
-// for one full wave of 256 workgroups with splits of at least 256 tokens; a
+// for one full wave of 256 workgroups with splits of at least 128 tokens; a
 // split holds at most kMlaMaxSplitTokens tokens, which sets a floor on the
 // count (a request below it is raised).  0 when the count would exceed
 // kMlaMaxSplits.
@@ -116,7 +116,7 @@ int plan_mla_splits(int32_t B, int32_t H, int64_t max_tokens, int32_t req) {
   } else {
     const int64_t units = (int64_t)B * (H / dattn::mla_heads_per_workgroup(H));
     const int64_t want = (256 + units - 1) / units;
-    const int64_t cap = (max_tokens + 255) / 256;
+    const int64_t cap = (max_tokens + 127) / 128;
     n = want < cap ? want : cap;
   }
   if (n < floor_n) n = floor_n;
@@ -150,6 +150,22 @@ size_t split_workspace(int64_t rows, int splits, int D) {
 }  // namespace
 
 namespace dattn {
+
+int device_cu_count() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cached[kMaxDevices];  // 0: not queried yet
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < kMaxDevices) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    cus = 256;
+  if (dev < kMaxDevices) cached[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
 
 void prof_begin(const char* name, hipStream_t s) {
   std::lock_guard<std::mutex> lk(g_prof_mu);

@@ -355,17 +355,28 @@ hipError_t launch_d(const GqaArgs& a, hipStream_t s) {
   return fast ? launch_df<BF16, D, true>(a, s) : launch_df<BF16, D, false>(a, s);
 }
 
+// Resident split-kernel workgroups per CU, queried once per kernel variant.
+template <bool BF16, int D, int G, bool FAST>
+int occupancy_one() {
+  static const int n = [] {
+    int v = 0;
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, gqa_split_kernel<BF16, D, G, FAST>, kThreads, 0) ==
+                   hipSuccess
+               ? v
+               : 0;
+  }();
+  return n;
+}
+
 template <bool BF16, int D, bool FAST>
 int occupancy_g(int G) {
-  int n = 0;
-  hipError_t e = hipErrorInvalidValue;
   switch (G) {
-    case 1: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gqa_split_kernel<BF16, D, 1, FAST>, kThreads, 0); break;
-    case 2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gqa_split_kernel<BF16, D, 2, FAST>, kThreads, 0); break;
-    case 4: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gqa_split_kernel<BF16, D, 4, FAST>, kThreads, 0); break;
-    case 8: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gqa_split_kernel<BF16, D, 8, FAST>, kThreads, 0); break;
+    case 1: return occupancy_one<BF16, D, 1, FAST>();
+    case 2: return occupancy_one<BF16, D, 2, FAST>();
+    case 4: return occupancy_one<BF16, D, 4, FAST>();
+    case 8: return occupancy_one<BF16, D, 8, FAST>();
   }
-  return e == hipSuccess ? n : 0;
+  return 0;
 }
 
 // Merge split partials (o_j normalised, lse_j in log2 units):

@@ -117,13 +117,16 @@ __global__ __launch_bounds__(kThreads) void indexer_kernel(const IndexerArgs a) 
   }
 }
 
-// Workgroups resident per CU for this head count (at least 1).
+// Workgroups resident per CU for this head count (at least 1), queried once.
 template <int NMT>
 int resident_per_cu() {
-  int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, (const void*)indexer_kernel<NMT>, kThreads, 0) !=
-          hipSuccess || n < 1)
-    n = 1;
+  static const int n = [] {
+    int v = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, (const void*)indexer_kernel<NMT>, kThreads, 0) !=
+            hipSuccess || v < 1)
+      v = 1;
+    return v;
+  }();
   return n;
 }
 
@@ -131,11 +134,7 @@ template <int NMT>
 hipError_t launch_nmt(IndexerArgs a, hipStream_t s) {
   // one round of resident workgroups: the token ranges (whole 32-token steps)
   // are sized so that B x ranges just fills the CUs, with no partial second round
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-    cus = 256;
-  const int64_t slots = (int64_t)cus * resident_per_cu<NMT>();
+  const int64_t slots = (int64_t)device_cu_count() * resident_per_cu<NMT>();
   const int64_t tokens = (int64_t)a.B * a.S_max;
   int64_t per = (tokens + slots - 1) / slots;
   per = (per + kTokWave - 1) / kTokWave * kTokWave;

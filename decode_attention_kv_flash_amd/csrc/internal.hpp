@@ -11,6 +11,10 @@ namespace dattn {
 void prof_begin(const char* name, hipStream_t s);
 void prof_end(hipStream_t s);
 
+// Compute units of the current device, queried once per device (256 when the
+// device cannot be queried); the decode calls make no other device queries.
+int device_cu_count();
+
 struct GqaArgs {
   const void* q;
   const void* k;
