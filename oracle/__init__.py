@@ -55,10 +55,11 @@ def _load():
         lib = ctypes.CDLL(_LIB)
         P, I, I64, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
         lib.oracle_gqa.argtypes = [P, P, P, I, I, I, I, I, I, P, I, I, D, P, I64, P, P]
+        lib.oracle_gqa_sink.argtypes = [P, P, P, I, I, I, I, I, I, P, I, I, P, D, P, I64, P, P]
         lib.oracle_mla.argtypes = [P, P, I, I, I, I, I, I, P, P, I, D, P, I64, P, P]
         lib.oracle_indexer.argtypes = [P, P, P, I, I, I, I, I, P, P]
         lib.oracle_topk.argtypes = [P, I, I, I, P, I, P]
-        for f in (lib.oracle_gqa, lib.oracle_mla, lib.oracle_indexer, lib.oracle_topk):
+        for f in (lib.oracle_gqa, lib.oracle_gqa_sink, lib.oracle_mla, lib.oracle_indexer, lib.oracle_topk):
             f.restype = I
         _lib = lib
     return _lib
@@ -97,13 +98,17 @@ def _check(rc, what):
         raise RuntimeError(f"oracle {what} failed with code {rc}")
 
 
-def gqa(q, k, v, seq_lens, *, window=0, n_sink=0, scale=None, rows=None):
+def gqa(q, k, v, seq_lens, *, window=0, n_sink=0, scale=None, rows=None, sink_logits=None):
     """Grouped-query decode attention in fp64.
 
     q [B,Hq,D]; k, v logical [B,Hkv,S_max,D] (fp32 or bf16, same dtype);
-    returns (out [n_rows, D] fp64, lse [n_rows] fp64) for flat rows b*Hq+h.
+    sink_logits: None, or [Hq] per-head sink logits (an extra softmax
+    denominator term exp(sink) with a zero value).
+    Returns (out [n_rows, D] fp64, lse [n_rows] fp64) for flat rows b*Hq+h.
     """
     lib = _load()
+    if sink_logits is not None:
+        return _gqa_sink(lib, q, k, v, seq_lens, window, n_sink, scale, rows, sink_logits)
     B, Hq, D = q.shape
     _, Hkv, S_max, _ = k.shape
     assert k.dtype == v.dtype == q.dtype
@@ -119,6 +124,27 @@ def gqa(q, k, v, seq_lens, *, window=0, n_sink=0, scale=None, rows=None):
                         _ptr(sl), int(window), int(n_sink), float(scale),
                         _ptr(r) if r is not None else None, n, _ptr(out), _ptr(lse))
     _check(rc, "gqa")
+    return out, lse
+
+
+def _gqa_sink(lib, q, k, v, seq_lens, window, n_sink, scale, rows, sink_logits):
+    B, Hq, D = q.shape
+    _, Hkv, S_max, _ = k.shape
+    assert k.dtype == v.dtype == q.dtype
+    if scale is None:
+        scale = D ** -0.5
+    q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+    sl = seq_lens.to(torch.int32).contiguous()
+    sk = torch.as_tensor(sink_logits, dtype=torch.float64).contiguous()
+    assert sk.shape == (Hq,)
+    r, n = _rows(rows)
+    n_out = n if r is not None else B * Hq
+    out = torch.empty(n_out, D, dtype=torch.float64)
+    lse = torch.empty(n_out, dtype=torch.float64)
+    rc = lib.oracle_gqa_sink(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, Hq, Hkv, D, S_max,
+                             _ptr(sl), int(window), int(n_sink), _ptr(sk), float(scale),
+                             _ptr(r) if r is not None else None, n, _ptr(out), _ptr(lse))
+    _check(rc, "gqa_sink")
     return out, lse
 
 

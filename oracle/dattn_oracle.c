@@ -77,13 +77,21 @@ static int attends(int t, int L, int window, int n_sink) {
  *   query head h reads KV head h / (Hq / Hkv): consecutive query heads share,
  *   as repeat_interleave / repeat_kv lay them out ("All the attentions",
  *   section 2; "Overview of Attention Mechanism", GQA "Code").
+ *   sink    NULL, or one logit per query head [Hq] (natural-log units): an
+ *           extra term exp(sink[h]) in the softmax denominator whose value is
+ *           zero -- the explicit learned sink logit ("Attention
+ *           Optimizations", "Attention sinks"); sink = 0 is the zero sink of
+ *           softmax-off-by-one, a token whose key and value are zero vectors
+ *           ("Overview of Attention Mechanism", StreamingLLM / attention
+ *           sink).  Then o = sum_t e^{s_t} v_t / (e^{sink} + sum_t e^{s_t}).
  * rows: flat row ids b*Hq + h to compute (NULL = all B*Hq, in order).
- * out [n_rows, D], lse [n_rows] (natural log; -inf and zeros for an empty set).
+ * out [n_rows, D], lse [n_rows] (natural log of the softmax denominator, the
+ * sink term included; -inf and zeros for an empty set without a sink).
  */
-int oracle_gqa(const void* q, const void* k, const void* v, int dtype,
-               int B, int Hq, int Hkv, int D, int S_max,
-               const int32_t* seq_lens, int window, int n_sink, double scale,
-               const int64_t* rows, int64_t n_rows, double* out, double* lse) {
+static int gqa_impl(const void* q, const void* k, const void* v, int dtype,
+                    int B, int Hq, int Hkv, int D, int S_max,
+                    const int32_t* seq_lens, int window, int n_sink, const double* sink,
+                    double scale, const int64_t* rows, int64_t n_rows, double* out, double* lse) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv != 0) return ORC_EINVAL;
   if (!rows) n_rows = (int64_t)B * Hq;
   const int G = Hq / Hkv;
@@ -118,8 +126,9 @@ int oracle_gqa(const void* q, const void* k, const void* v, int dtype,
       s[t] = scale * acc;
       if (s[t] > m) m = s[t];
     }
+    if (sink && sink[h] > m) m = sink[h];
     /* pass 2: exponentials, their sum, weighted values */
-    double l = 0.0;
+    double l = sink ? exp(sink[h] - m) : 0.0;
     for (int t = 0; t < L; ++t) {
       if (!attends(t, L, window, n_sink)) continue;
       const double p = exp(s[t] - m);
@@ -135,6 +144,23 @@ int oracle_gqa(const void* q, const void* k, const void* v, int dtype,
     free(s);
   }
   return err;
+}
+
+int oracle_gqa(const void* q, const void* k, const void* v, int dtype,
+               int B, int Hq, int Hkv, int D, int S_max,
+               const int32_t* seq_lens, int window, int n_sink, double scale,
+               const int64_t* rows, int64_t n_rows, double* out, double* lse) {
+  return gqa_impl(q, k, v, dtype, B, Hq, Hkv, D, S_max, seq_lens, window, n_sink, NULL, scale,
+                  rows, n_rows, out, lse);
+}
+
+int oracle_gqa_sink(const void* q, const void* k, const void* v, int dtype,
+                    int B, int Hq, int Hkv, int D, int S_max,
+                    const int32_t* seq_lens, int window, int n_sink, const double* sink,
+                    double scale, const int64_t* rows, int64_t n_rows, double* out, double* lse) {
+  if (!sink) return ORC_EINVAL;
+  return gqa_impl(q, k, v, dtype, B, Hq, Hkv, D, S_max, seq_lens, window, n_sink, sink, scale,
+                  rows, n_rows, out, lse);
 }
 
 /*

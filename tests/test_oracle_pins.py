@@ -144,6 +144,68 @@ def test_empty_sequence_gives_zeros_and_minus_inf():
 
 
 # --------------------------------------------------------------------------
+# explicit sink logit: one more softmax-denominator term with a zero value
+
+
+def test_sink_single_token_sigmoid():
+    # one token and a sink logit c: o = sigmoid(s0 - c) v0, lse = log(e^s0 + e^c)
+    x = _tiny(L=1, D=8, seed=4)
+    c = 0.37
+    out, lse = oracle.gqa(x.q, x.k, x.v, x.seq_lens, sink_logits=[c])
+    s0 = float((x.q[0, 0].double() * x.k[0, 0, 0].double()).sum()) * x.scale
+    a = 1.0 / (1.0 + math.exp(c - s0))
+    assert torch.allclose(out[0], a * x.v[0, 0, 0].double(), rtol=0, atol=1e-14)
+    assert lse[0].item() == pytest.approx(math.log(math.exp(s0) + math.exp(c)), abs=1e-13)
+
+
+def test_sink_on_empty_sequence():
+    # no token: the output is zero and the denominator is the sink term alone
+    x = wl.make_gqa(B=1, Hq=2, Hkv=1, D=8, seq_lens=[0], dtype=torch.float32, paged=False, seed=2)
+    out, lse = oracle.gqa(x.q, x.k, x.v, x.seq_lens, sink_logits=[-1.5, 2.0])
+    assert torch.all(out == 0)
+    assert lse.tolist() == [-1.5, 2.0]
+
+
+def _sdpa_with_sink_token(q, k, v, scale, L, sink, keep=None):
+    """Library attention over the cache plus one token whose key and value are
+    zero vectors and whose logit is raised by the head's sink (an additive
+    mask); q [Hq, D], k/v [Hkv, S, D] (fp64)."""
+    Hq, Hkv, D = q.shape[0], k.shape[0], q.shape[1]
+    kk = k[:, :L] if keep is None else k[:, keep]
+    vv = v[:, :L] if keep is None else v[:, keep]
+    n = kk.shape[1]
+    kk = torch.cat([kk, torch.zeros(Hkv, 1, D, dtype=kk.dtype)], dim=1).repeat_interleave(Hq // Hkv, 0)
+    vv = torch.cat([vv, torch.zeros(Hkv, 1, D, dtype=vv.dtype)], dim=1).repeat_interleave(Hq // Hkv, 0)
+    bias = torch.zeros(Hq, 1, n + 1, dtype=q.dtype)
+    bias[:, 0, n] = torch.as_tensor(sink, dtype=q.dtype)
+    return F.scaled_dot_product_attention(q[:, None, :], kk, vv, attn_mask=bias, scale=scale)[:, 0, :]
+
+
+def test_zero_sink_equals_library_attention_with_a_zero_token():
+    # softmax-off-by-one: a sink logit of 0 is a token whose key and value are zero
+    lens = [1, 9, 150]
+    x = wl.make_gqa(B=3, Hq=4, Hkv=2, D=32, seq_lens=lens, dtype=torch.float32, paged=False, seed=21)
+    out, _ = oracle.gqa(x.q, x.k, x.v, x.seq_lens, sink_logits=[0.0] * 4)
+    out = out.view(3, 4, 32)
+    for b, L in enumerate(lens):
+        want = _sdpa_with_sink_token(x.q[b].double(), x.k[b].double(), x.v[b].double(), x.scale, L, [0.0] * 4)
+        assert torch.allclose(out[b], want, rtol=1e-12, atol=1e-12)
+
+
+def test_learned_sink_with_window_equals_library_attention():
+    lens, window, n_sink = [40, 300], 64, 4
+    sinks = [-3.0, 0.5, 2.5, 7.0]
+    x = wl.make_gqa(B=2, Hq=4, Hkv=1, D=16, seq_lens=lens, dtype=torch.bfloat16, paged=False, seed=22)
+    out, lse = oracle.gqa(x.q, x.k, x.v, x.seq_lens, window=window, n_sink=n_sink, sink_logits=sinks)
+    out = out.view(2, 4, 16)
+    for b, L in enumerate(lens):
+        keep = _keep_list(L, window, n_sink)
+        want = _sdpa_with_sink_token(x.q[b].double(), x.k[b].double(), x.v[b].double(), x.scale, L,
+                                     sinks, keep=keep)
+        assert torch.allclose(out[b], want, rtol=1e-12, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
 # attention against the library routine (fp64 SDPA, CPU math path)
 
 
