@@ -107,8 +107,9 @@ def check(lib, rc):
         raise RuntimeError(lib.dattn_last_error().decode())
 
 
-def bench_gqa(x, timer, steps, warmup, torch, lib):
-    """decode_attn_gqa on a (paged) GQA workload; returns the timing record."""
+def bench_gqa(x, timer, steps, warmup, torch, lib, sink_logits=None):
+    """decode_attn_gqa on a (paged) GQA workload (decode_attn_gqa_sink when
+    sink_logits, fp32 [Hq], is given); returns the timing record."""
     dev = torch.device("cuda:0")
     q, sl = x.q.to(dev), x.seq_lens.to(dev)
     pt = x.page_table.to(dev) if x.page_table is not None else None
@@ -124,10 +125,17 @@ def bench_gqa(x, timer, steps, warmup, torch, lib):
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     dt = 1 if x.q.dtype == torch.bfloat16 else 0
-    args = [(ptr(q), ptr(kc[r]), ptr(vc[r]), ptr(sl), ptr(pt), x.window, x.n_sink, ptr(out),
-             ptr(lse), x.B, x.Hq, x.Hkv, x.D, x.page_size, max_pages, dt, ctypes.c_float(x.scale),
-             0, ptr(ws), nbytes, stream) for r in range(R)]
-    fn = lib.decode_attn_gqa
+    if sink_logits is None:
+        args = [(ptr(q), ptr(kc[r]), ptr(vc[r]), ptr(sl), ptr(pt), x.window, x.n_sink, ptr(out),
+                 ptr(lse), x.B, x.Hq, x.Hkv, x.D, x.page_size, max_pages, dt,
+                 ctypes.c_float(x.scale), 0, ptr(ws), nbytes, stream) for r in range(R)]
+        fn = lib.decode_attn_gqa
+    else:
+        sk = sink_logits.to(dev)
+        args = [(ptr(q), ptr(kc[r]), ptr(vc[r]), ptr(sl), ptr(pt), x.window, x.n_sink, ptr(sk),
+                 ptr(out), ptr(lse), x.B, x.Hq, x.Hkv, x.D, x.page_size, max_pages, dt,
+                 ctypes.c_float(x.scale), 0, ptr(ws), nbytes, stream) for r in range(R)]
+        fn = lib.decode_attn_gqa_sink
 
     def step(i):
         check(lib, fn(*args[i % R]))
@@ -296,6 +304,15 @@ def main():
             "split_kernel_GB/s": round(gbs(b3, r3["kernels"]["gqa_split"]["avg_us"]), 1),
             "kv_bytes_per_step": b3,
             "kernels_us": {k: v["avg_us"] for k, v in r3["kernels"].items()}}
+        # the same workload with an explicit sink logit per head
+        sk = torch.linspace(-2.0, 2.0, x3.Hq, dtype=torch.float32)
+        r3s = bench_gqa(x3, timer, steps, warmup, torch, lib, sink_logits=sk)
+        result["workloads"]["swa4096_sinks4_sink_logits"] = {
+            "step_us": round(r3s["wall_ms"] * 1e3, 2),
+            "GB/s": round(b3 / (r3s["wall_ms"] * 1e-3) / 1e9, 1),
+            "split_kernel_GB/s": round(gbs(b3, r3s["kernels"]["gqa_split"]["avg_us"]), 1),
+            "kv_bytes_per_step": b3,
+            "kernels_us": {k: v["avg_us"] for k, v in r3s["kernels"].items()}}
         del x3
         torch.cuda.empty_cache()
 

@@ -21,7 +21,7 @@ DATTN_F32, DATTN_BF16 = 0, 1
 STATUS = {0: "OK", -1: "EINVAL", -2: "EUNSUPPORTED", -3: "EWORKSPACE", -4: "EHIP"}
 
 EXPORTS = (
-    "decode_attn_gqa", "decode_attn_gqa_workspace",
+    "decode_attn_gqa", "decode_attn_gqa_sink", "decode_attn_gqa_workspace",
     "decode_attn_mla", "decode_attn_mla_workspace",
     "dsa_indexer_topk", "dsa_indexer_topk_workspace",
     "dsa_topk", "dsa_topk_workspace",
@@ -51,6 +51,8 @@ def lib() -> ctypes.CDLL:
     P, I32, SZ, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
     L.decode_attn_gqa.argtypes = [P, P, P, P, P, I32, I32, P, P, I32, I32, I32, I32, I32, I32,
                                   I32, F, I32, P, SZ, P]
+    L.decode_attn_gqa_sink.argtypes = [P, P, P, P, P, I32, I32, P, P, P, I32, I32, I32, I32, I32,
+                                       I32, I32, F, I32, P, SZ, P]
     L.decode_attn_gqa_workspace.argtypes = [I32] * 9
     L.decode_attn_mla.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, I32, F, I32,
                                   P, SZ, P]
@@ -64,7 +66,7 @@ def lib() -> ctypes.CDLL:
     for name in ("decode_attn_gqa_workspace", "decode_attn_mla_workspace",
                  "dsa_indexer_topk_workspace", "dsa_topk_workspace", "sparse_mla_attn_workspace"):
         getattr(L, name).restype = SZ
-    for name in ("decode_attn_gqa", "decode_attn_mla", "dsa_indexer_topk", "dsa_topk",
+    for name in ("decode_attn_gqa", "decode_attn_gqa_sink", "decode_attn_mla", "dsa_indexer_topk", "dsa_topk",
                  "sparse_mla_attn", "dattn_profile_enable", "dattn_profile_read",
                  "dattn_profile_reset"):
         getattr(L, name).restype = ctypes.c_int
@@ -115,10 +117,17 @@ def _workspace(nbytes: int, device) -> Optional[torch.Tensor]:
 
 def decode_attn_gqa(q, k_cache, v_cache, seq_lens, page_table=None, window=0, n_sink=0, *,
                     scale=None, num_splits=0, out=None, lse=None, want_lse=True, workspace=None,
-                    stream=None):
-    """GQA / sliding-window + sinks decode attention.  Returns (out, lse)."""
+                    stream=None, sink_logits=None):
+    """GQA / sliding-window + sinks decode attention.  Returns (out, lse).
+
+    sink_logits: optional device fp32 [Hq] explicit sink logits (decode_attn_gqa_sink).
+    """
     for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (seq_lens, "seq_lens")):
         _dev(t, n)
+    if sink_logits is not None:
+        _dev(sink_logits, "sink_logits")
+        if sink_logits.dtype != torch.float32 or sink_logits.shape != (q.shape[1],):
+            raise ValueError("sink_logits must be fp32 [Hq]")
     B, Hq, D = q.shape
     Hkv = k_cache.shape[1]
     page_size = k_cache.shape[2]
@@ -138,10 +147,17 @@ def decode_attn_gqa(q, k_cache, v_cache, seq_lens, page_table=None, window=0, n_
         ws, nbytes = workspace, workspace.numel() * workspace.element_size()
     else:
         ws = _workspace(nbytes, q.device)
-    _check(lib().decode_attn_gqa(
-        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), _ptr(page_table),
-        int(window), int(n_sink), _ptr(out), _ptr(lse), B, Hq, Hkv, D, page_size, max_pages,
-        _dtype_code(q), float(scale or 0.0), int(num_splits), _ptr(ws), nbytes, _stream(stream)))
+    if sink_logits is None:
+        _check(lib().decode_attn_gqa(
+            _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), _ptr(page_table),
+            int(window), int(n_sink), _ptr(out), _ptr(lse), B, Hq, Hkv, D, page_size, max_pages,
+            _dtype_code(q), float(scale or 0.0), int(num_splits), _ptr(ws), nbytes, _stream(stream)))
+    else:
+        _check(lib().decode_attn_gqa_sink(
+            _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), _ptr(page_table),
+            int(window), int(n_sink), _ptr(sink_logits.contiguous()), _ptr(out), _ptr(lse), B, Hq,
+            Hkv, D, page_size, max_pages, _dtype_code(q), float(scale or 0.0), int(num_splits),
+            _ptr(ws), nbytes, _stream(stream)))
     return out, lse
 
 

@@ -311,6 +311,17 @@ int decode_attn_gqa(const void* q, const void* k_cache, const void* v_cache, con
                     int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t page_size, int32_t max_pages,
                     int32_t dtype, float scale, int32_t num_splits, void* workspace,
                     size_t workspace_bytes, void* stream) {
+  return decode_attn_gqa_sink(q, k_cache, v_cache, seq_lens, page_table, window, n_sink, nullptr, out,
+                              lse, B, Hq, Hkv, D, page_size, max_pages, dtype, scale, num_splits,
+                              workspace, workspace_bytes, stream);
+}
+
+int decode_attn_gqa_sink(const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* seq_lens, const int32_t* page_table, int32_t window,
+                         int32_t n_sink, const float* sink_logits, void* out, float* lse, int32_t B,
+                         int32_t Hq, int32_t Hkv, int32_t D, int32_t page_size, int32_t max_pages,
+                         int32_t dtype, float scale, int32_t num_splits, void* workspace,
+                         size_t workspace_bytes, void* stream) {
   int rc = validate_gqa(q, k_cache, v_cache, seq_lens, page_table, n_sink, out, B, Hq, Hkv, D,
                         page_size, max_pages, dtype, scale, num_splits);
   if (rc) return rc;
@@ -343,6 +354,7 @@ int decode_attn_gqa(const void* q, const void* k_cache, const void* v_cache, con
   a.bf16 = dtype == DATTN_BF16;
   const float sc = scale > 0.f ? scale : 1.0f / std::sqrt((float)D);
   a.scale_log2 = sc * 1.4426950408889634f;
+  a.sink = sink_logits;
   if (splits > 1) {
     a.part_o = (float*)workspace;
     a.part_lse = (float*)((char*)workspace + align256((size_t)B * Hq * splits * D * sizeof(float)));
@@ -350,7 +362,8 @@ int decode_attn_gqa(const void* q, const void* k_cache, const void* v_cache, con
   hipStream_t s = (hipStream_t)stream;
   if ((rc = launch("gqa_split", s, [&] { return dattn::launch_gqa(a, s); }))) return rc;
   if (splits > 1) {
-    dattn::CombineArgs c{a.part_o, a.part_lse, nullptr, out, lse, B * Hq, splits, D, a.bf16};
+    dattn::CombineArgs c{a.part_o, a.part_lse, nullptr, out, lse, B * Hq, splits, D, a.bf16,
+                         sink_logits, Hq};
     if ((rc = launch("lse_combine", s, [&] { return dattn::launch_combine(c, s); }))) return rc;
   }
   return ok();

@@ -309,13 +309,18 @@ __global__ __launch_bounds__(kThreads) void gqa_split_kernel(const GqaArgs a) {
   __syncthreads();
 
   const size_t row0 = (size_t)b * a.Hq + (size_t)kvh * G;
+  // an explicit sink logit joins the denominator once per row: here when
+  // this workgroup holds the whole row, else in the combine
+  const bool with_sink = a.sink != nullptr && a.num_splits == 1;
   for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
     const int h = idx / D, d = idx % D;
     float M = NEG_INF;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][h]);
+    const float sink2 = with_sink ? a.sink[kvh * G + h] * kLog2e : NEG_INF;
+    M = fmaxf(M, sink2);
     const float mu = M == NEG_INF ? 0.f : M;
-    float lsum = 0.f, acc = 0.f;
+    float lsum = with_sink ? fast_exp2(sink2 - mu) : 0.f, acc = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
       const float f = fast_exp2(sm_m[w][h] - mu);
@@ -423,6 +428,14 @@ __global__ __launch_bounds__(kCombineThreads) void lse_combine_kernel(const Comb
       wsum = fmaf(w, l[u], wsum);
       acc = fmaf(w, v[u], acc);
     }
+    M = Mc;
+  }
+  if (a.sink) {  // one more term, exp(sink), with a zero value
+    const float x = a.sink[row % a.sink_heads] * kLog2e;
+    const float Mc = fmaxf(M, x);
+    const float f = fast_exp2(M - Mc);  // 0 while M is -inf
+    wsum = wsum * f + fast_exp2(x - Mc);
+    acc *= f;
     M = Mc;
   }
   const float val = wsum > 0.f ? acc / wsum : 0.f;

@@ -30,6 +30,9 @@ struct GqaArgs {
   int32_t page_size, log2_page, max_pages, num_splits;
   int32_t bf16;
   float scale_log2;  // softmax scale * log2(e)
+  // nullptr, or one sink logit per query head [Hq] (natural log): an extra
+  // softmax-denominator term exp(sink) with a zero value
+  const float* sink;
 };
 
 hipError_t launch_gqa(const GqaArgs& a, hipStream_t s);
@@ -47,6 +50,9 @@ struct CombineArgs {
   float* lse;             // [rows] natural log, or nullptr
   int32_t rows, splits, D;
   int32_t bf16;
+  // nullptr, or a sink logit per head (natural log) for row r: sink[r % sink_heads]
+  const float* sink = nullptr;
+  int32_t sink_heads = 1;
 };
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);

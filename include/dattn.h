@@ -101,6 +101,31 @@ DATTN_EXPORT int decode_attn_gqa(const void* q, const void* k_cache, const void*
                     int32_t num_splits, void* workspace, size_t workspace_bytes,
                     void* stream);
 
+/* decode_attn_gqa with an explicit sink logit per query head.
+ *
+ * Some models carry a learned sink logit instead of (or besides) keeping the
+ * first tokens ("Attention Optimizations", "Attention sinks": gpt-oss's
+ * explicit sink); softmax-off-by-one adds a zero sink, a token whose key and
+ * value are zero vectors ("Overview of Attention Mechanism", StreamingLLM /
+ * attention sink).  Both are one more term in the softmax denominator with
+ * a zero value:
+ *   o = sum_t e^{s_t} v_t / (e^{sink[h]} + sum_t e^{s_t})
+ * and lse = log(e^{sink[h]} + sum_t e^{s_t}) (so an empty T_b gives o = 0,
+ * lse = sink[h]).
+ *   sink_logits  device fp32 [Hq], natural-log units, read-only; NULL gives
+ *                exactly decode_attn_gqa.  A zero sink is all zeros.
+ * Every other argument, the workspace and the error behaviour are those of
+ * decode_attn_gqa (same workspace size).
+ */
+DATTN_EXPORT int decode_attn_gqa_sink(const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* seq_lens, const int32_t* page_table,
+                    int32_t window, int32_t n_sink, const float* sink_logits,
+                    void* out, float* lse,
+                    int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                    int32_t page_size, int32_t max_pages, int32_t dtype, float scale,
+                    int32_t num_splits, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
 /* Workspace bytes decode_attn_gqa needs for these sizes (0 if none); pass
  * max_pages = 1 for a contiguous cache. */
 DATTN_EXPORT size_t decode_attn_gqa_workspace(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,

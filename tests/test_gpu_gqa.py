@@ -39,6 +39,59 @@ def test_tiny_gqa_fp32_config():
         assert err <= TOL_F32
 
 
+def check_sink(x, sinks, num_splits=0):
+    """decode_attn_gqa_sink against the oracle with the same fp32 sink logits."""
+    say(f"[gqa-sink] {x.name or 'case'} B={x.B} Hq={x.Hq} Hkv={x.Hkv} D={x.D} "
+        f"lens={x.seq_lens.tolist()[:6]} window={x.window} sinks={x.n_sink} splits={num_splits}")
+    sk = torch.tensor(sinks, dtype=torch.float32)
+    out, lse = api.decode_attn_gqa(dev(x.q), dev(x.k_cache), dev(x.v_cache), dev(x.seq_lens),
+                                   dev(x.page_table), x.window, x.n_sink, scale=x.scale,
+                                   num_splits=num_splits, sink_logits=dev(sk))
+    torch.cuda.synchronize()
+    got, glse = out.float().cpu().reshape(-1, x.D), lse.cpu().reshape(-1)
+    want, wlse = oracle.gqa(x.q, x.k, x.v, x.seq_lens, window=x.window, n_sink=x.n_sink,
+                            scale=x.scale, sink_logits=sk.double())
+    err = assert_rows_close(got, want, tol_for(x.q.dtype), x.name)
+    assert_lse_close(glse, wlse, 1e-5, x.name)
+    return err
+
+
+@pytest.mark.parametrize("splits", [0, 1, 2, 4])
+def test_zero_sink_tiny_fp32(splits):
+    """softmax-off-by-one (all sinks 0) on the tiny fp32 workload, 1e-5."""
+    x = wl.config1_tiny_gqa()
+    assert check_sink(x, [0.0] * x.Hq, splits) <= TOL_F32
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,dtype,paged", [
+    (32, 8, 128, torch.bfloat16, True),
+    (8, 1, 64, torch.float32, False),
+])
+@pytest.mark.parametrize("splits", [0, 1, 3])
+def test_learned_sinks_ragged(Hq, Hkv, D, dtype, paged, splits):
+    x = wl.make_gqa(B=4, Hq=Hq, Hkv=Hkv, D=D, seq_lens=[1, 17, 300, 1029], dtype=dtype,
+                    page_size=16, paged=paged, seed=31, name=f"sinks_{Hq}_{Hkv}_{D}")
+    g = torch.Generator().manual_seed(5)
+    # logits spanning well below to well above the scores (N(0,1) data)
+    sinks = (torch.rand(Hq, generator=g) * 16 - 6).tolist()
+    check_sink(x, sinks, splits)
+
+
+@pytest.mark.parametrize("splits", [0, 2])
+def test_learned_sinks_with_window(splits):
+    x = wl.make_gqa(B=3, Hq=32, Hkv=8, D=128, seq_lens=[3, 700, 5000], dtype=torch.bfloat16,
+                    page_size=16, paged=True, window=512, n_sink=4, seed=32, name="sinks_window")
+    check_sink(x, [float(h % 7) - 3.0 for h in range(32)], splits)
+
+
+def test_sink_on_empty_sequences():
+    """No token: zero output and lse equal to the head's sink logit."""
+    x = wl.make_gqa(B=3, Hq=8, Hkv=2, D=64, seq_lens=[0, 40, 0], dtype=torch.bfloat16,
+                    page_size=16, paged=True, seed=33, name="sinks_empty")
+    for splits in (1, 2):
+        check_sink(x, [0.5 * h - 2.0 for h in range(8)], splits)
+
+
 @pytest.mark.parametrize("Hq,Hkv,D,dtype,paged", [
     (32, 8, 128, torch.bfloat16, True),
     (8, 8, 64, torch.bfloat16, True),     # MHA
