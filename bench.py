@@ -201,6 +201,43 @@ def bench_dsa(d, timer, steps, warmup, torch, lib):
     return rec
 
 
+def bench_append(timer, steps, warmup, torch, lib):
+    """Cache append of one decode step: K/V rows of the Llama-3-8B-shaped GQA
+    layer (B16, 8 KV heads, D128, paged 16), MLA latent rows (B32 x 576) and
+    indexer keys (B8 x 128).  Each moves its rows once from the new-row
+    buffer into the cache (bytes = 2 x rows)."""
+    dev = torch.device("cuda:0")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    g = torch.Generator().manual_seed(7)
+    res = {}
+    # GQA: 8192 tokens per sequence in a randomly permuted paged cache
+    B, Hkv, D, P, L = 16, 8, 128, 16, 8192
+    pages = B * L // P
+    kc = torch.empty(pages, Hkv, P, D, dtype=torch.bfloat16, device=dev)
+    vc = torch.empty_like(kc)
+    pt = torch.randperm(pages, generator=g).view(B, L // P).to(torch.int32).to(dev)
+    kn = torch.randn(B, Hkv, D, generator=g).to(torch.bfloat16).to(dev)
+    vn = torch.randn(B, Hkv, D, generator=g).to(torch.bfloat16).to(dev)
+    pos = torch.full((B,), L - 1, dtype=torch.int32, device=dev)
+    a = (ptr(kn), ptr(vn), ptr(kc), ptr(vc), ptr(pos), ptr(pt), B, Hkv, D, P, L // P, 0, 0, 1, stream)
+    r = timer.run(lambda i: check(lib, lib.kv_append_gqa(*a)), steps, warmup, ["kv_append"])
+    nb = 2 * 2 * B * Hkv * D * 2
+    res["gqa_b16_kv8_d128_paged16"] = {"us": round(r["kernels"]["kv_append"]["avg_us"], 2),
+                                       "bytes": nb, "GB/s": round(gbs(nb, r["kernels"]["kv_append"]["avg_us"]), 1)}
+    del kc, vc
+    for name, Bx, row, S in (("latent_b32_576", 32, 576, 16384), ("indexer_b8_128", 8, 128, 65536)):
+        cache = torch.empty(Bx, S, row, dtype=torch.bfloat16, device=dev)
+        new = torch.randn(Bx, row, generator=g).to(torch.bfloat16).to(dev)
+        p2 = torch.full((Bx,), S - 1, dtype=torch.int32, device=dev)
+        a2 = (ptr(new), ptr(cache), ptr(p2), None, Bx, row, S, 1, 1, stream)
+        r = timer.run(lambda i: check(lib, lib.kv_append_rows(*a2)), steps, warmup, ["kv_append"])
+        nb = 2 * Bx * row * 2
+        res[name] = {"us": round(r["kernels"]["kv_append"]["avg_us"], 2), "bytes": nb,
+                     "GB/s": round(gbs(nb, r["kernels"]["kv_append"]["avg_us"]), 1)}
+        del cache
+    return res
+
+
 def gbs(nbytes, us):
     return None if not us else nbytes / (us * 1e-6) / 1e9
 
@@ -217,7 +254,7 @@ def main():
     # (input generation runs on the CPU); 300 calls cover that
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--quick", action="store_true", help="headline workload only")
-    ap.add_argument("--only", choices=["gqa", "swa", "mla", "dsa"],
+    ap.add_argument("--only", choices=["gqa", "swa", "mla", "dsa", "append"],
                     help="time one workload and print its record (for profiling runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="time a plain 1 GiB device copy (reference for HBM byte counters)")
@@ -351,6 +388,10 @@ def main():
         del d5
         torch.cuda.empty_cache()
 
+        log("[bench] cache append (GQA K/V, MLA latent, indexer keys)")
+        result["workloads"]["kv_append"] = bench_append(timer, steps, warmup, torch, lib)
+        torch.cuda.empty_cache()
+
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline()
     print(json.dumps(result), flush=True)
@@ -386,6 +427,8 @@ def only(name, timer, steps, warmup, torch, lib, wl):
         m = wl.config4_mla()
         r = bench_mla(m, timer, steps, warmup, torch, lib)
         r["kv_bytes_per_step"], r["flops_per_step"] = m.kv_bytes(), m.flops()
+    elif name == "append":
+        r = bench_append(timer, steps, warmup, torch, lib)
     else:
         d = wl.config5_dsa()
         r = bench_dsa(d, timer, steps, warmup, torch, lib)

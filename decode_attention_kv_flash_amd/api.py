@@ -26,6 +26,7 @@ EXPORTS = (
     "dsa_indexer_topk", "dsa_indexer_topk_workspace",
     "dsa_topk", "dsa_topk_workspace",
     "sparse_mla_attn", "sparse_mla_attn_workspace",
+    "kv_append_gqa", "kv_append_rows",
     "dattn_last_error", "dattn_version",
     "dattn_profile_enable", "dattn_profile_read", "dattn_profile_reset",
 )
@@ -54,6 +55,8 @@ def lib() -> ctypes.CDLL:
     L.decode_attn_gqa_sink.argtypes = [P, P, P, P, P, I32, I32, P, P, P, I32, I32, I32, I32, I32,
                                        I32, I32, F, I32, P, SZ, P]
     L.decode_attn_gqa_workspace.argtypes = [I32] * 9
+    L.kv_append_gqa.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, I32, P]
+    L.kv_append_rows.argtypes = [P, P, P, P, I32, I32, I32, I32, I32, P]
     L.decode_attn_mla.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, I32, F, I32,
                                   P, SZ, P]
     L.decode_attn_mla_workspace.argtypes = [I32] * 5
@@ -67,6 +70,7 @@ def lib() -> ctypes.CDLL:
                  "dsa_indexer_topk_workspace", "dsa_topk_workspace", "sparse_mla_attn_workspace"):
         getattr(L, name).restype = SZ
     for name in ("decode_attn_gqa", "decode_attn_gqa_sink", "decode_attn_mla", "dsa_indexer_topk", "dsa_topk",
+                 "kv_append_gqa", "kv_append_rows",
                  "sparse_mla_attn", "dattn_profile_enable", "dattn_profile_read",
                  "dattn_profile_reset"):
         getattr(L, name).restype = ctypes.c_int
@@ -159,6 +163,41 @@ def decode_attn_gqa(q, k_cache, v_cache, seq_lens, page_table=None, window=0, n_
             Hkv, D, page_size, max_pages, _dtype_code(q), float(scale or 0.0), int(num_splits),
             _ptr(ws), nbytes, _stream(stream)))
     return out, lse
+
+
+def kv_append_gqa(k_new, v_new, k_cache, v_cache, positions, page_table=None, *, ring_pages=0,
+                  fixed_pages=0, stream=None):
+    """Write each sequence's new K/V rows [B, Hkv, D] at positions[b] of the
+    (paged) caches; with ring_pages > 0 the page table is a rolling buffer."""
+    for t, n in ((k_new, "k_new"), (v_new, "v_new"), (k_cache, "k_cache"), (v_cache, "v_cache"),
+                 (positions, "positions")):
+        _dev(t, n)
+    B, Hkv, D = k_new.shape
+    page_size = k_cache.shape[2]
+    max_pages = 1
+    if page_table is not None:
+        _dev(page_table, "page_table")
+        max_pages = page_table.shape[1]
+    _check(lib().kv_append_gqa(
+        _ptr(k_new.contiguous()), _ptr(v_new.contiguous()), _ptr(k_cache), _ptr(v_cache),
+        _ptr(positions), _ptr(page_table), B, Hkv, D, page_size, max_pages, int(ring_pages),
+        int(fixed_pages), _dtype_code(k_new), _stream(stream)))
+
+
+def kv_append_rows(rows_new, cache, positions, page_table=None, *, stream=None):
+    """Write each sequence's new row [B, X] (MLA latent or indexer key) at
+    positions[b] of a cache [pages, page_size, X] or [B, S_max, X]."""
+    for t, n in ((rows_new, "rows_new"), (cache, "cache"), (positions, "positions")):
+        _dev(t, n)
+    B, X = rows_new.shape
+    page_size = cache.shape[1]
+    max_pages = 1
+    if page_table is not None:
+        _dev(page_table, "page_table")
+        max_pages = page_table.shape[1]
+    _check(lib().kv_append_rows(
+        _ptr(rows_new.contiguous()), _ptr(cache), _ptr(positions), _ptr(page_table), B, X,
+        page_size, max_pages, _dtype_code(rows_new), _stream(stream)))
 
 
 def decode_attn_mla(q_absorbed, latent_cache, seq_lens, page_table=None, *, d_latent=512,

@@ -522,4 +522,64 @@ int dsa_indexer_topk(const void* q_i, const float* w, const void* k_i_cache, con
   return rc ? rc : ok();
 }
 
+// ------------------------------------------------------------- cache append
+static int append_common(const char* fn, const void* ptrs[], int n_ptrs, const int32_t* positions,
+                         int32_t B, int32_t heads, int64_t row_bytes, bool paged, int32_t page_size,
+                         int32_t max_pages, int32_t dtype) {
+  for (int i = 0; i < n_ptrs; ++i) {
+    if (!ptrs[i]) return fail(DATTN_EINVAL, "%s: NULL pointer argument", fn);
+    if ((uintptr_t)ptrs[i] % 16 != 0) return fail(DATTN_EINVAL, "%s: buffers must be 16-byte aligned", fn);
+  }
+  if (!positions) return fail(DATTN_EINVAL, "%s: NULL pointer argument", fn);
+  if (B < 1 || B > 65535) return fail(DATTN_EINVAL, "%s: B must be in [1, 65535]", fn);
+  if (heads < 1) return fail(DATTN_EINVAL, "%s: head count must be >= 1", fn);
+  if (dtype != DATTN_F32 && dtype != DATTN_BF16) return fail(DATTN_EUNSUPPORTED, "%s: dtype %d", fn, dtype);
+  if (row_bytes < 16 || row_bytes % 16 != 0 || row_bytes > (1 << 20))
+    return fail(DATTN_EUNSUPPORTED, "%s: a row of %lld bytes is not a multiple of 16", fn, (long long)row_bytes);
+  if (page_size < 1) return fail(DATTN_EINVAL, "%s: page_size must be >= 1", fn);
+  if (paged) {
+    if (!pow2(page_size)) return fail(DATTN_EUNSUPPORTED, "%s: paged cache needs a power-of-two page_size", fn);
+    if (max_pages < 1) return fail(DATTN_EINVAL, "%s: max_pages must be >= 1", fn);
+  }
+  return DATTN_OK;
+}
+
+int kv_append_gqa(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                  const int32_t* positions, int32_t* page_table, int32_t B, int32_t Hkv, int32_t D,
+                  int32_t page_size, int32_t max_pages, int32_t ring_pages, int32_t fixed_pages,
+                  int32_t dtype, void* stream) {
+  const void* ptrs[] = {k_new, v_new, k_cache, v_cache};
+  const int64_t esz = dtype == DATTN_BF16 ? 2 : 4;
+  int rc = append_common("kv_append_gqa", ptrs, 4, positions, B, Hkv, (int64_t)D * esz,
+                         page_table != nullptr, page_size, max_pages, dtype);
+  if (rc) return rc;
+  if (D < 1) return fail(DATTN_EINVAL, "kv_append_gqa: D must be >= 1");
+  if (ring_pages < 0 || fixed_pages < 0)
+    return fail(DATTN_EINVAL, "kv_append_gqa: ring_pages and fixed_pages must be >= 0");
+  if (ring_pages > 0 && !page_table)
+    return fail(DATTN_EINVAL, "kv_append_gqa: a rolling buffer needs a page table");
+  dattn::KvAppendArgs a{k_new, v_new, k_cache, v_cache, positions, page_table, B, Hkv,
+                        (int32_t)(D * esz), page_size, page_table ? ilog2(page_size) : 0,
+                        page_table ? max_pages : 1, ring_pages, fixed_pages};
+  hipStream_t s = (hipStream_t)stream;
+  rc = launch("kv_append", s, [&] { return dattn::launch_kv_append(a, s); });
+  return rc ? rc : ok();
+}
+
+int kv_append_rows(const void* rows_new, void* cache, const int32_t* positions,
+                   const int32_t* page_table, int32_t B, int32_t row_elems, int32_t page_size,
+                   int32_t max_pages, int32_t dtype, void* stream) {
+  const void* ptrs[] = {rows_new, cache};
+  const int64_t esz = dtype == DATTN_BF16 ? 2 : 4;
+  int rc = append_common("kv_append_rows", ptrs, 2, positions, B, 1, (int64_t)row_elems * esz,
+                         page_table != nullptr, page_size, max_pages, dtype);
+  if (rc) return rc;
+  dattn::KvAppendArgs a{rows_new, nullptr, cache, nullptr, positions, (int32_t*)page_table, B, 1,
+                        (int32_t)(row_elems * esz), page_size, page_table ? ilog2(page_size) : 0,
+                        page_table ? max_pages : 1, 0, 0};
+  hipStream_t s = (hipStream_t)stream;
+  rc = launch("kv_append", s, [&] { return dattn::launch_kv_append(a, s); });
+  return rc ? rc : ok();
+}
+
 }  // extern "C"

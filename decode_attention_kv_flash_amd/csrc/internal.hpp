@@ -105,4 +105,19 @@ struct TopkArgs {
 size_t topk_workspace_bytes(int B, int S_max);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 
+// Cache append: one new row per (sequence, head) into one or two caches laid
+// out [pages, heads, page_size, row] (contiguous: pages = B, page_size = S_max).
+struct KvAppendArgs {
+  const void* new0;        // [B, heads, row]
+  const void* new1;        // second cache's rows (V), or nullptr
+  void* cache0;
+  void* cache1;            // nullptr for a single cache
+  const int32_t* positions;  // [B]; negative: no append
+  int32_t* page_table;     // [B, max_pages] or nullptr (contiguous)
+  int32_t B, heads, row_bytes, page_size, log2_page, max_pages;
+  int32_t ring_pages, fixed_pages;
+};
+
+hipError_t launch_kv_append(const KvAppendArgs& a, hipStream_t s);
+
 }  // namespace dattn

@@ -133,6 +133,56 @@ DATTN_EXPORT size_t decode_attn_gqa_workspace(int32_t B, int32_t Hq, int32_t Hkv
                                  int32_t n_sink, int32_t num_splits);
 
 /* ------------------------------------------------------------------------ */
+/* Cache append: the new token's entries, written before attending.
+ *
+ * Decoding writes the current token into the cache and then attends over it
+ * ("Attention Optimizations", "DSA: DeepSeek Sparse Attention", "Computation
+ * Path": update_cache of the latent row and of the indexer key).  Entry
+ * position p of sequence b goes to slot p % page_size of physical page
+ * page_table[b][p / page_size] (PagedAttention block table, "All the
+ * attentions", section 8), or to [b, p] of a contiguous cache.
+ *
+ * kv_append_gqa: one K row and one V row per KV head.
+ *   k_new, v_new  [B, Hkv, D] dtype, read-only
+ *   k_cache, v_cache  [num_pages, Hkv, page_size, D] (the decode_attn_gqa layout),
+ *                 written at the appended slots only
+ *   positions     device int32 [B]: the position written (the current token
+ *                 is position L_b - 1 once seq_lens counts it); a negative
+ *                 entry skips the sequence, and so does a position past the
+ *                 cache (p >= page_size * max_pages, or >= S_max contiguous)
+ *   page_table    device int32 [B, max_pages], or NULL (contiguous,
+ *                 page_size = S_max).  Pages the append writes must not be
+ *                 shared with another sequence (copy them first).
+ *   ring_pages, fixed_pages  rolling buffer for a sliding window ("All the
+ *                 attentions", section 4: the cache becomes a rolling buffer
+ *                 of fixed size, new entries replacing the oldest).  With
+ *                 ring_pages > 0 a write into logical page j >= fixed_pages +
+ *                 ring_pages first sets page_table[b][j] = page_table[b][j -
+ *                 ring_pages] (so the table is written).  Entries below
+ *                 fixed_pages + ring_pages are the caller's: fixed_pages for
+ *                 the attention-sink tokens, never recycled, then the ring.
+ *                 For window W the ring needs ceil((W - 1) / page_size) + 1
+ *                 pages so that a recycled page holds no token any later
+ *                 query's window reaches.  0 = no rolling buffer.
+ *   D * sizeof(dtype) must be a multiple of 16 bytes; every buffer 16-byte
+ *   aligned.  Errors: DATTN_EINVAL / DATTN_EUNSUPPORTED before any launch.
+ *
+ * kv_append_rows: one row per token (the MLA latent cache [c_KV | k_pe],
+ *   576 values, or the indexer key cache, 128 values).
+ *   rows_new   [B, row_elems] dtype
+ *   cache      [num_pages, page_size, row_elems] or contiguous [B, S_max, row_elems]
+ *   the rest as for kv_append_gqa (no rolling buffer).
+ */
+DATTN_EXPORT int kv_append_gqa(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                  const int32_t* positions, int32_t* page_table, int32_t B, int32_t Hkv,
+                  int32_t D, int32_t page_size, int32_t max_pages, int32_t ring_pages,
+                  int32_t fixed_pages, int32_t dtype, void* stream);
+
+DATTN_EXPORT int kv_append_rows(const void* rows_new, void* cache, const int32_t* positions,
+                  const int32_t* page_table, int32_t B, int32_t row_elems, int32_t page_size,
+                  int32_t max_pages, int32_t dtype, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Absorbed MLA decode attention over a latent cache.
  *
  * For each sequence b and head h: s_t = scale * q_absorbed[b,h] . row_t over

@@ -134,3 +134,42 @@ def test_profile_calls_without_gpu():
     api.profile_reset()
     assert api.profile_read("gqa") == (0.0, 0)
     api.profile_enable(False)
+
+
+def _append(**kw):
+    args = dict(k_new=256, v_new=256, k_cache=256, v_cache=256, positions=256, page_table=None,
+                B=2, Hkv=8, D=128, page_size=16, max_pages=4, ring=0, fixed=0, dtype=1)
+    args.update(kw)
+    P = lambda x: None if x is None else ctypes.c_void_p(x)
+    return api.lib().kv_append_gqa(
+        P(args["k_new"]), P(args["v_new"]), P(args["k_cache"]), P(args["v_cache"]),
+        P(args["positions"]), P(args["page_table"]), args["B"], args["Hkv"], args["D"],
+        args["page_size"], args["max_pages"], args["ring"], args["fixed"], args["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k_new=None), -1),
+    (dict(positions=None), -1),
+    (dict(v_cache=264), -1),                 # not 16-byte aligned
+    (dict(B=0), -1),
+    (dict(Hkv=0), -1),
+    (dict(dtype=5), -2),
+    (dict(D=4), -2),                         # a row of 8 bytes
+    (dict(D=100), -2),                       # 200 bytes, not a multiple of 16
+    (dict(page_table=256, page_size=24), -2),
+    (dict(page_table=256, max_pages=0), -1),
+    (dict(ring=3), -1),                      # rolling buffer without a page table
+    (dict(page_table=256, ring=-1), -1),
+])
+def test_append_validation(kw, code):
+    rc = _append(**kw)
+    assert rc == code, api.lib().dattn_last_error()
+    assert api.lib().dattn_last_error()
+
+
+def test_append_rows_validation():
+    L = api.lib()
+    P = ctypes.c_void_p
+    # a latent row of 577 bf16 values is not a multiple of 16 bytes
+    assert L.kv_append_rows(P(256), P(256), P(256), None, 2, 577, 100, 1, 1, None) == -2
+    assert L.kv_append_rows(None, P(256), P(256), None, 2, 576, 100, 1, 1, None) == -1

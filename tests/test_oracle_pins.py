@@ -206,6 +206,42 @@ def test_learned_sink_with_window_equals_library_attention():
 
 
 # --------------------------------------------------------------------------
+# cache append in logical order
+
+
+def test_append_matches_library_index_put():
+    from oracle import cache as ocache
+    g = torch.Generator().manual_seed(9)
+    for shape, new_shape in (((3, 2, 11, 5), (3, 2, 5)), ((3, 11, 7), (3, 7))):
+        c = torch.randn(*shape, generator=g)
+        new = torch.randn(*new_shape, generator=g)
+        pos = torch.tensor([10, -1, 0])
+        got = ocache.append(c, pos, new)
+        want = c.clone()
+        keep = pos >= 0
+        b = torch.arange(3)[keep]
+        if c.dim() == 4:
+            want.permute(0, 2, 1, 3).index_put_((b, pos[keep]), new[keep])
+        else:
+            want.index_put_((b, pos[keep]), new[keep])
+        assert torch.equal(got, want)
+        assert torch.equal(got[1], c[1])  # a negative position appends nothing
+
+
+def test_attention_after_append_sees_the_new_token():
+    # appending a token whose key dominates every score makes it the output
+    from oracle import cache as ocache
+    x = wl.make_gqa(B=1, Hq=1, Hkv=1, D=4, seq_lens=[6], dtype=torch.float32, paged=False, seed=12)
+    x.q[0, 0] = torch.tensor([1.0, 0, 0, 0])
+    k_new = torch.tensor([[[400.0, 0, 0, 0]]])
+    v_new = torch.tensor([[[1.0, 2.0, 3.0, 4.0]]])
+    k = ocache.append(x.k, [5], k_new)
+    v = ocache.append(x.v, [5], v_new)
+    out, _ = oracle.gqa(x.q, k, v, x.seq_lens)
+    assert torch.allclose(out[0], v_new[0, 0].double(), atol=1e-30)
+
+
+# --------------------------------------------------------------------------
 # attention against the library routine (fp64 SDPA, CPU math path)
 
 
