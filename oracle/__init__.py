@@ -14,7 +14,8 @@ into it.  Closed-form byte and FLOP accounting lives in ``accounting.py``.
 Parity status per function (what pins each one is listed in the tests):
   gqa        pinned (library SDPA in fp64, keep-list compaction, brute force)
   mla        pinned (expanded, un-absorbed MLA through library SDPA)
-  indexer    pinned (hand-computed fixture, invariants, brute force)
+  indexer    pinned (hand-computed fixture, invariants, brute force); its fp8
+             e4m3 decoding pinned code by code against torch.float8_e4m3fn
   topk       pinned (characterising invariants, brute force on tiny inputs)
   accounting pinned (numbers printed on the pages, tests/golden)
 """
@@ -33,7 +34,7 @@ _SRC = os.path.join(_HERE, "dattn_oracle.c")
 _LIB = os.path.join(_HERE, "libdattn_oracle.so")
 _lib = None
 
-F32, BF16 = 0, 1
+F32, BF16, FP8_E4M3 = 0, 1, 2
 
 
 def build(force: bool = True) -> str:
@@ -59,6 +60,8 @@ def _load():
         lib.oracle_mla.argtypes = [P, P, I, I, I, I, I, I, P, P, I, D, P, I64, P, P]
         lib.oracle_indexer.argtypes = [P, P, P, I, I, I, I, I, P, P]
         lib.oracle_topk.argtypes = [P, I, I, I, P, I, P]
+        lib.oracle_e4m3_value.argtypes = [I]
+        lib.oracle_e4m3_value.restype = D
         for f in (lib.oracle_gqa, lib.oracle_gqa_sink, lib.oracle_mla, lib.oracle_indexer, lib.oracle_topk):
             f.restype = I
         _lib = lib
@@ -78,7 +81,14 @@ def _dtype_code(t: torch.Tensor) -> int:
         return F32
     if t.dtype == torch.bfloat16:
         return BF16
-    raise TypeError(f"oracle takes fp32 or bf16, got {t.dtype}")
+    if t.dtype == torch.float8_e4m3fn:
+        return FP8_E4M3
+    raise TypeError(f"oracle takes fp32, bf16 or fp8 e4m3, got {t.dtype}")
+
+
+def e4m3_value(code: int) -> float:
+    """The oracle's decoding of one fp8 e4m3 byte (for pinning the decoder)."""
+    return float(_load().oracle_e4m3_value(int(code)))
 
 
 def _ptr(t: torch.Tensor):

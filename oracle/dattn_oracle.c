@@ -28,9 +28,12 @@
  *
  * Parallelism: OpenMP over independent output rows only.
  *
- * Element types: 0 = fp32, 1 = bf16 given as raw 16-bit patterns.  A bf16
- * value widens exactly to fp32 by a 16-bit left shift, and fp32 widens exactly
- * to double.
+ * Element types: 0 = fp32, 1 = bf16 given as raw 16-bit patterns, 2 = fp8
+ * e4m3 (the OCP "e4m3fn" format: 1 sign bit, 4 exponent bits with bias 7, 3
+ * mantissa bits, subnormals at exponent 0, no infinities, S.1111.111 = NaN)
+ * given as raw bytes.  A bf16 value widens exactly to fp32 by a 16-bit left
+ * shift, an e4m3 value is decoded exactly from its fields, and fp32 widens
+ * exactly to double.
  */
 #include <math.h>
 #include <stdint.h>
@@ -39,14 +42,26 @@
 
 #define ORC_F32 0
 #define ORC_BF16 1
+#define ORC_FP8_E4M3 2
 
 #define ORC_OK 0
 #define ORC_EINVAL (-1)
 #define ORC_ENOTINT (-2)
 #define ORC_ENOMEM (-3)
 
+/* e4m3 byte -> value: (-1)^s 2^(e-7) (1 + m/8), or 2^-6 (m/8) when e = 0. */
+static double e4m3_value(uint8_t x) {
+  const int sign = x >> 7, e = (x >> 3) & 15, m = x & 7;
+  if (e == 15 && m == 7) return NAN;
+  const double v = e ? ldexp(1.0 + m / 8.0, e - 7) : ldexp(m / 8.0, -6);
+  return sign ? -v : v;
+}
+
+double oracle_e4m3_value(int x) { return e4m3_value((uint8_t)x); }
+
 static double elem(const void* p, int dtype, int64_t i) {
   if (dtype == ORC_F32) return (double)((const float*)p)[i];
+  if (dtype == ORC_FP8_E4M3) return e4m3_value(((const uint8_t*)p)[i]);
   uint32_t bits = (uint32_t)((const uint16_t*)p)[i] << 16;
   float f;
   memcpy(&f, &bits, sizeof f);

@@ -485,6 +485,24 @@ def test_indexer_weight_and_head_permutation():
         assert torch.equal(s3[b, :L], s[b, :L])
 
 
+def test_e4m3_decoding_matches_library_for_every_code():
+    # the oracle's own decoder of the fp8 format against torch's float8_e4m3fn
+    codes = torch.arange(256, dtype=torch.uint8)
+    lib_vals = codes.view(torch.float8_e4m3fn).to(torch.float64)
+    for c in range(256):
+        got, want = oracle.e4m3_value(c), lib_vals[c].item()
+        assert (math.isnan(got) and math.isnan(want)) or got == want, (c, got, want)
+    assert oracle.e4m3_value(0x7E) == 448.0 and oracle.e4m3_value(0x01) == 2.0 ** -9
+
+
+def test_indexer_fp8_equals_bf16_on_the_same_integers():
+    # integers in [-4, 4] are exact in e4m3: the scores cannot depend on the encoding
+    d = _small_dsa(31)
+    s16 = oracle.indexer(d.q_i, d.w, d.k_i, d.seq_lens)
+    s8 = oracle.indexer(d.q_i.to(torch.float8_e4m3fn), d.w, d.k_i.to(torch.float8_e4m3fn), d.seq_lens)
+    assert torch.equal(s16, s8)
+
+
 def test_indexer_rejects_non_integers():
     x = _small_dsa(4)
     q = x.q_i.float()
