@@ -198,6 +198,14 @@ def bench_dsa(d, timer, steps, warmup, torch, lib):
     rec = timer.run(step, steps, warmup, ["indexer_scores", "topk_select", "sparse_mla_split",
                                           "lse_combine"])
     rec["copies"] = R
+    # the indexer with its inputs in fp8 e4m3 (exact for these integers): half the key bytes
+    qi8 = qi.to(torch.float8_e4m3fn)
+    ki8 = [t.to(torch.float8_e4m3fn) for t in ki]
+    a8 = [(ptr(qi8), ptr(w), ptr(ki8[r]), ptr(sl), d.topk, ptr(idx), ptr(scores), B, Hi, Di, S, 2,
+           ptr(iws), ibytes, stream) for r in range(R)]
+    r8 = timer.run(lambda i: check(lib, lib.dsa_indexer_topk(*a8[i % R])), steps, warmup,
+                   ["indexer_scores", "topk_select"])
+    rec["fp8"] = r8
     return rec
 
 
@@ -384,7 +392,12 @@ def main():
             "topk_us": ku["topk_select"]["avg_us"],
             "sparse_mla_TFLOP/s": round(tflops(fs, ku["sparse_mla_split"]["avg_us"]), 2),
             "sparse_mla_GB/s": round(gbs(bs, ku["sparse_mla_split"]["avg_us"]), 1),
-            "kernels_us": {k: v["avg_us"] for k, v in ku.items()}}
+            "kernels_us": {k: v["avg_us"] for k, v in ku.items()},
+            "indexer_fp8": {
+                "indexer_us": r5["fp8"]["kernels"]["indexer_scores"]["avg_us"],
+                "indexer_GB/s": round(gbs(bi // 2, r5["fp8"]["kernels"]["indexer_scores"]["avg_us"]), 1),
+                "key_bytes_per_step": bi // 2,
+                "indexer_topk_step_us": round(r5["fp8"]["wall_ms"] * 1e3, 2)}}
         del d5
         torch.cuda.empty_cache()
 

@@ -17,7 +17,7 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libdattn.so")
 
-DATTN_F32, DATTN_BF16 = 0, 1
+DATTN_F32, DATTN_BF16, DATTN_FP8_E4M3 = 0, 1, 2
 STATUS = {0: "OK", -1: "EINVAL", -2: "EUNSUPPORTED", -3: "EWORKSPACE", -4: "EHIP"}
 
 EXPORTS = (
@@ -105,6 +105,8 @@ def _dtype_code(t: torch.Tensor) -> int:
         return DATTN_F32
     if t.dtype == torch.bfloat16:
         return DATTN_BF16
+    if t.dtype == torch.float8_e4m3fn:
+        return DATTN_FP8_E4M3
     raise ValueError(f"unsupported dtype {t.dtype}")
 
 
@@ -236,6 +238,8 @@ def dsa_indexer_topk(q_i, w, k_i_cache, seq_lens, k, *, topk_idx=None, return_sc
         raise ValueError("w must be fp32")
     B, Hi, Di = q_i.shape
     S_max = k_i_cache.shape[1]
+    if q_i.dtype != k_i_cache.dtype:
+        raise ValueError("q_i and k_i_cache must have one dtype")
     if topk_idx is None:
         topk_idx = torch.empty(B, k, dtype=torch.int32, device=q_i.device)
     scores = torch.empty(B, S_max, dtype=torch.float32, device=q_i.device) if return_scores else None

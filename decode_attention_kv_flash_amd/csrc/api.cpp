@@ -506,7 +506,8 @@ int dsa_indexer_topk(const void* q_i, const float* w, const void* k_i_cache, con
   if (Di != 128) return fail(DATTN_EUNSUPPORTED, "dsa_indexer_topk: Di = %d; only 128 is built", Di);
   if (Hi != 32 && Hi != 64 && Hi != 96 && Hi != 128)
     return fail(DATTN_EUNSUPPORTED, "dsa_indexer_topk: Hi = %d not in {32,64,96,128}", Hi);
-  if (dtype != DATTN_BF16) return fail(DATTN_EUNSUPPORTED, "dsa_indexer_topk: only bf16 is built");
+  if (dtype != DATTN_BF16 && dtype != DATTN_FP8_E4M3)
+    return fail(DATTN_EUNSUPPORTED, "dsa_indexer_topk: dtype %d; bf16 and fp8 e4m3 are built", dtype);
   if (S_max > kTopkMaxRow)
     return fail(DATTN_EINVAL, "dsa_indexer_topk: S_max must be <= %d", kTopkMaxRow);
   int rc = check_workspace(workspace, workspace_bytes, dsa_indexer_topk_workspace(B, S_max, k));
@@ -514,7 +515,7 @@ int dsa_indexer_topk(const void* q_i, const float* w, const void* k_i_cache, con
   float* scores = scores_out ? scores_out : (float*)workspace;
   uint32_t* topk_ws = (uint32_t*)((char*)workspace + align256((size_t)B * S_max * sizeof(float)));
   hipStream_t s = (hipStream_t)stream;
-  dattn::IndexerArgs ia{(const uint16_t*)q_i, w, (const uint16_t*)k_i_cache, seq_lens, scores, B, Hi, S_max};
+  dattn::IndexerArgs ia{q_i, w, k_i_cache, seq_lens, scores, B, Hi, S_max, 0, dtype == DATTN_FP8_E4M3};
   rc = launch("indexer_scores", s, [&] { return dattn::launch_indexer(ia, s); });
   if (rc) return rc;
   dattn::TopkArgs t{scores, seq_lens, topk_idx, B, S_max, k, topk_ws, 0, 0};

@@ -81,13 +81,14 @@ int mla_heads_per_workgroup(int H);
 hipError_t launch_mla(const MlaArgs& a, hipStream_t s);
 
 struct IndexerArgs {
-  const uint16_t* q;       // [B, Hi, 128] bf16
+  const void* q;           // [B, Hi, 128] bf16 or fp8 e4m3
   const float* w;          // [B, Hi]
-  const uint16_t* k;       // [B, S_max, 128] bf16
+  const void* k;           // [B, S_max, 128], q's type
   const int32_t* seq_lens;
   float* scores;           // [B, S_max]
   int32_t B, Hi, S_max;
   int32_t tok_per_wg;      // set by the launcher
+  int32_t fp8;             // 1: q and k are fp8 e4m3 (OCP e4m3fn)
 };
 
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s);

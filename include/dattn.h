@@ -45,7 +45,10 @@
 extern "C" {
 #endif
 
-typedef enum { DATTN_F32 = 0, DATTN_BF16 = 1 } dattn_dtype;
+/* Element types.  DATTN_FP8_E4M3 is the OCP fp8 "e4m3fn" format (1 sign, 4
+ * exponent bits with bias 7, 3 mantissa bits, no infinities), one byte per
+ * value; the lightning indexer's inputs only. */
+typedef enum { DATTN_F32 = 0, DATTN_BF16 = 1, DATTN_FP8_E4M3 = 2 } dattn_dtype;
 
 typedef enum {
   DATTN_OK = 0,
@@ -235,13 +238,17 @@ DATTN_EXPORT size_t decode_attn_mla_workspace(int32_t B, int32_t H, int32_t d_la
  * ascending index order; when k > seq_lens[b] the tail is -1.  The caller
  * folds any positive constant (such as n_heads^-0.5) into w.
  *
- *   q_i        [B, Hi, Di] bf16;  w fp32 [B, Hi];  k_i_cache [B, S_max, Di] bf16
+ *   q_i        [B, Hi, Di] dtype;  w fp32 [B, Hi];  k_i_cache [B, S_max, Di] dtype
+ *              (dtype DATTN_BF16, or DATTN_FP8_E4M3: the indexer in FP8 as
+ *              the pages give it ("Long context, KV eviction and sparse
+ *              attention", "Sparse attention": a lightweight indexer scoring
+ *              all past tokens with few heads in FP8), half the key bytes)
  *   seq_lens   int32 [B], 0 <= L_b <= S_max
  *   k          1 <= k <= 16384
  *   topk_idx   int32 [B, k] (written)
  *   scores_out fp32 [B, S_max] or NULL; when given, receives the scores
  *              (entries t >= seq_lens[b] are -inf)
- *   Hi a multiple of 32 (<= 128), Di = 128, dtype DATTN_BF16, B <= 65535,
+ *   Hi a multiple of 32 (<= 128), Di = 128, dtype DATTN_BF16 or DATTN_FP8_E4M3, B <= 65535,
  *   S_max <= 2^30
  *   workspace  dsa_indexer_topk_workspace(B, S_max, k) bytes, 256-byte
  *              aligned, always required (the selection keeps histograms and

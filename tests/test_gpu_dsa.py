@@ -33,6 +33,59 @@ def check_indexer(x, k):
     return idx, want_idx
 
 
+FP8 = torch.float8_e4m3fn
+
+
+def check_indexer_fp8(x, k):
+    """The indexer with q_i and k_i in fp8 e4m3 (exact for the integer inputs)
+    against the oracle on the same fp8 values."""
+    say(f"[dsa] indexer fp8 B={x.B} Hi={x.q_i.shape[1]} lens={x.seq_lens.tolist()[:4]} k={k}")
+    q8, k8 = x.q_i.to(FP8), x.k_i.to(FP8)
+    idx, scores = api.dsa_indexer_topk(dev(q8), dev(x.w), dev(k8), dev(x.seq_lens), k,
+                                       return_scores=True)
+    torch.cuda.synchronize()
+    idx, scores = idx.cpu(), scores.cpu()
+    want = oracle.indexer(q8, x.w, k8, x.seq_lens)
+    for b, L in enumerate(x.seq_lens.tolist()):
+        assert torch.equal(scores[b, :L].double(), want[b, :L].double()), f"fp8 scores row {b}"
+        assert torch.all(torch.isinf(scores[b, L:]))
+    assert torch.equal(idx, oracle.topk(want, x.seq_lens, k))
+
+
+@pytest.mark.parametrize("Hi", [32, 64, 96, 128])
+def test_indexer_fp8_small(Hi):
+    x = wl.make_dsa(B=3, seq_lens=[5, 700, 3001], Hi=Hi, topk=64, H=64, seed=61)
+    check_indexer_fp8(x, 64)
+
+
+@pytest.mark.parametrize("k", [1, 2048, 5000])
+def test_indexer_fp8_topk_sizes(k):
+    x = wl.make_dsa(B=2, seq_lens=[4096, 2500], topk=k, H=64, seed=62)
+    check_indexer_fp8(x, k)
+
+
+def test_indexer_fp8_hand_worked_example():
+    import json, os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "indexer_tiny.json")))
+    q = torch.zeros(1, 32, 128, dtype=torch.float32)
+    q[0, :2, :3] = torch.tensor(g["q_i"], dtype=torch.float32)
+    w = torch.zeros(1, 32)
+    w[0, :2] = torch.tensor(g["w"], dtype=torch.float32)
+    k = torch.zeros(1, 5, 128, dtype=torch.float32)
+    k[0, :, :3] = torch.tensor(g["k_i"], dtype=torch.float32)
+    for kk, want in g["topk"].items():
+        idx, sc = api.dsa_indexer_topk(dev(q.to(FP8)), dev(w), dev(k.to(FP8)),
+                                       dev(torch.tensor([5], dtype=torch.int32)), int(kk), return_scores=True)
+        torch.cuda.synchronize()
+        assert idx.cpu()[0].tolist() == want
+        assert sc.cpu()[0].tolist() == [float(v) for v in g["scores"]]
+
+
+def test_indexer_fp8_full_size(cfg5):
+    """The DSA workload's indexer (B8 x 65536 tokens, 64 heads, top-2048) in fp8."""
+    check_indexer_fp8(cfg5, cfg5.topk)
+
+
 @pytest.mark.parametrize("Hi", [32, 64, 128])
 def test_indexer_small(Hi):
     x = wl.make_dsa(B=3, seq_lens=[5, 700, 3001], Hi=Hi, topk=64, H=64, seed=51)
