@@ -242,6 +242,53 @@ def test_attention_after_append_sees_the_new_token():
 
 
 # --------------------------------------------------------------------------
+# Quest: query-aware page selection
+
+
+def test_quest_bound_holds_for_every_key():
+    from oracle import quest
+    x = wl.make_gqa(B=2, Hq=4, Hkv=2, D=32, seq_lens=[70, 160], dtype=torch.float32, paged=False, seed=71)
+    kmin, kmax = quest.page_minmax(x.k, x.seq_lens)
+    up = quest.upper_bounds(x.q, kmin, kmax, x.seq_lens, 2)
+    for b, L in enumerate([70, 160]):
+        for h in range(4):
+            s = x.k[b, h // 2, : L // 16 * 16].double() @ x.q[b, h].double()
+            best = s.view(-1, 16).amax(1)
+            assert torch.all(best <= up[b, h, : L // 16] + 1e-12)
+            assert torch.all(torch.isinf(up[b, h, L // 16:]))
+
+
+def test_quest_full_budget_equals_full_attention():
+    # every full page chosen plus the partial one is the whole cache
+    from oracle import quest
+    x = wl.make_gqa(B=2, Hq=4, Hkv=1, D=16, seq_lens=[37, 100], dtype=torch.bfloat16, paged=False, seed=72)
+    (out, lse), chosen = quest.decode(x.q, x.k, x.v, x.seq_lens, budget=100)
+    want, wlse = oracle.gqa(x.q, x.k, x.v, x.seq_lens)
+    assert torch.allclose(out, want, rtol=1e-12, atol=1e-12)
+    assert torch.allclose(lse, wlse, rtol=1e-12, atol=1e-12)
+    assert chosen[0] == [0, 1] and chosen[4] == list(range(6))
+
+
+def test_quest_picks_the_page_that_points_along_the_query():
+    # page 3's keys are a large multiple of the query: its bound dominates, so a
+    # budget of one page picks it, and the output is close to its values' mix
+    from oracle import quest
+    x = wl.make_gqa(B=1, Hq=1, Hkv=1, D=8, seq_lens=[90], dtype=torch.float32, paged=False, seed=73)
+    x.k[0, 0, 48:64] = 20.0 * x.q[0, 0]
+    (out, _), chosen = quest.decode(x.q, x.k, x.v, x.seq_lens, budget=1)
+    assert chosen == [[3]]
+    assert torch.allclose(out[0], x.v[0, 0, 48:64].double().mean(0), atol=1e-6)
+
+
+def test_quest_ties_go_to_the_lower_page():
+    from oracle import quest
+    x = wl.make_gqa(B=1, Hq=2, Hkv=1, D=4, seq_lens=[96], dtype=torch.float32, paged=False, seed=74)
+    x.k[0, 0, :96] = x.k[0, 0, :16].repeat(6, 1)  # six identical pages
+    (_, _), chosen = quest.decode(x.q, x.k, x.v, x.seq_lens, budget=3)
+    assert chosen == [[0, 1, 2], [0, 1, 2]]
+
+
+# --------------------------------------------------------------------------
 # attention against the library routine (fp64 SDPA, CPU math path)
 
 
