@@ -7,7 +7,8 @@ Prints ONE JSON line on stdout.  The headline `value` is the KV bytes the
 Llama-3-8B-shaped GQA layer must read (B16, 32/8 heads, D128, 8192 tokens,
 paged 16, bf16) divided by the wall time of one decode_attn_gqa call (split
 kernel + log-sum-exp combine), K calls timed back to back with inputs resident
-in HBM.  The other workloads (window + sinks, MLA, DSA) are reported under
+in HBM.  The other workloads (window + sinks, MLA, DSA, Quest page selection,
+cache append) are reported under
 "workloads".  A step is one call of the hot path on one batch; buffers rotate
 over copies whose total exceeds 1 GiB so no step reads another's data from
 the 256 MB Infinity Cache.
@@ -209,6 +210,58 @@ def bench_dsa(d, timer, steps, warmup, torch, lib):
     return rec
 
 
+def bench_quest(x, timer, steps, warmup, torch, lib, budget):
+    """Quest on a GQA workload: per query head the `budget` 16-token blocks with
+    the largest key bounds plus the partial block (bounds, top-k, attention
+    over the chosen blocks, combine), and the block-summary build."""
+    dev = torch.device("cuda:0")
+    q, sl, pt = x.q.to(dev), x.seq_lens.to(dev), x.page_table.to(dev)
+    R = copies_for(2 * x.k_cache.numel() * x.k_cache.element_size())
+    kc = [x.k_cache.to(dev) for _ in range(R)]
+    vc = [x.v_cache.to(dev) for _ in range(R)]
+    max_pages = x.page_table.shape[1]
+    nblk = x.page_size * max_pages // 16
+    kmm = [torch.empty(x.B, x.Hkv, nblk, 2, x.D, dtype=x.k.dtype, device=dev) for _ in range(R)]
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    dt = 1 if x.q.dtype == torch.bfloat16 else 0
+    mm = [(ptr(kc[r]), ptr(sl), ptr(pt), ptr(kmm[r]), 0, x.B, x.Hkv, x.D, x.page_size, max_pages, dt,
+           stream) for r in range(R)]
+    for a in mm:
+        check(lib, lib.quest_page_minmax(*a))
+    out = torch.empty_like(q)
+    lse = torch.empty(x.B, x.Hq, dtype=torch.float32, device=dev)
+    nbytes = lib.decode_attn_quest_workspace(x.B, x.Hq, x.Hkv, x.D, x.page_size, max_pages, budget, dt, 0)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    args = [(ptr(q), ptr(kc[r]), ptr(vc[r]), ptr(kmm[r]), ptr(sl), ptr(pt), budget, ptr(out), ptr(lse),
+             None, x.B, x.Hq, x.Hkv, x.D, x.page_size, max_pages, dt, ctypes.c_float(x.scale), 0,
+             ptr(ws), nbytes, stream) for r in range(R)]
+    rec = timer.run(lambda i: check(lib, lib.decode_attn_quest(*args[i % R])), steps, warmup,
+                    ["quest_bounds", "topk_select", "gqa_split", "lse_combine"])
+    # the summary of every block, and the refresh of one block per sequence
+    rec["minmax_full"] = timer.run(lambda i: check(lib, lib.quest_page_minmax(*mm[i % R])), steps,
+                                   warmup // 4, ["quest_minmax"])
+    last = int(x.seq_lens.min()) // 16 - 1
+    inc = [a[:4] + (last,) + a[5:] for a in mm]
+    rec["minmax_one_block"] = timer.run(lambda i: check(lib, lib.quest_page_minmax(*inc[i % R])), steps,
+                                        warmup // 4, ["quest_minmax"])
+    rec["copies"] = R
+    return rec
+
+
+def quest_bytes(x, budget):
+    """Algorithmic bytes of one Quest step: block summaries, the bounds
+    written and read back by the select, and K/V of the chosen tokens per
+    query head."""
+    esz = x.k.element_size()
+    summ = sel = bounds = 0
+    for L in x.seq_lens.tolist():
+        nf = L // 16
+        summ += x.Hkv * nf * 2 * x.D * esz
+        bounds += 2 * x.Hq * nf * 4
+        sel += x.Hq * (min(budget, nf) * 16 + L % 16) * 2 * x.D * esz
+    return summ, bounds, sel
+
+
 def bench_append(timer, steps, warmup, torch, lib):
     """Cache append of one decode step: K/V rows of the Llama-3-8B-shaped GQA
     layer (B16, 8 KV heads, D128, paged 16), MLA latent rows (B32 x 576) and
@@ -262,7 +315,7 @@ def main():
     # (input generation runs on the CPU); 300 calls cover that
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--quick", action="store_true", help="headline workload only")
-    ap.add_argument("--only", choices=["gqa", "swa", "mla", "dsa", "append"],
+    ap.add_argument("--only", choices=["gqa", "swa", "mla", "dsa", "append", "quest"],
                     help="time one workload and print its record (for profiling runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="time a plain 1 GiB device copy (reference for HBM byte counters)")
@@ -336,6 +389,26 @@ def main():
                               "kernels_us": {k: v["avg_us"] for k, v in r2["kernels"].items()}},
         },
     }
+    if not args.quick:
+        budget = 128  # blocks of 16: 2048 tokens per query head
+        log(f"[bench] quest on the gqa config, budget {budget} blocks")
+        rq = bench_quest(x2, timer, steps, warmup, torch, lib, budget)
+        kq = rq["kernels"]
+        summ, bnd, selb = quest_bytes(x2, budget)
+        kbytes = x2.k.element_size() * x2.Hkv * x2.D * int(x2.seq_lens.sum())
+        mm_us = rq["minmax_full"]["kernels"]["quest_minmax"]["avg_us"]
+        result["workloads"]["quest_llama3_8b_budget2048"] = {
+            "step_us": round(rq["wall_ms"] * 1e3, 2),
+            "dense_step_us": round(r2["wall_ms"] * 1e3, 2),
+            "bytes_per_step": summ + bnd + selb,
+            "GB/s": round((summ + bnd + selb) / (rq["wall_ms"] * 1e-3) / 1e9, 1),
+            "bounds_GB/s": round(gbs(summ, kq["quest_bounds"]["avg_us"]), 1),
+            "attention_GB/s": round(gbs(selb, kq["gqa_split"]["avg_us"]), 1),
+            "topk_us": kq["topk_select"]["avg_us"],
+            "kernels_us": {k: v["avg_us"] for k, v in kq.items()},
+            "minmax_all_blocks_us": round(mm_us, 2),
+            "minmax_all_blocks_GB/s": round(gbs(kbytes, mm_us), 1),
+            "minmax_one_block_us": round(rq["minmax_one_block"]["kernels"]["quest_minmax"]["avg_us"], 2)}
     del x2
 
     if not args.quick:
@@ -442,6 +515,10 @@ def only(name, timer, steps, warmup, torch, lib, wl):
         r["kv_bytes_per_step"], r["flops_per_step"] = m.kv_bytes(), m.flops()
     elif name == "append":
         r = bench_append(timer, steps, warmup, torch, lib)
+    elif name == "quest":
+        x = wl.config2_llama3_8b_gqa()
+        r = bench_quest(x, timer, steps, warmup, torch, lib, 128)
+        r["bytes_per_step"] = sum(quest_bytes(x, 128))
     else:
         d = wl.config5_dsa()
         r = bench_dsa(d, timer, steps, warmup, torch, lib)

@@ -27,6 +27,7 @@ EXPORTS = (
     "dsa_topk", "dsa_topk_workspace",
     "sparse_mla_attn", "sparse_mla_attn_workspace",
     "kv_append_gqa", "kv_append_rows",
+    "quest_page_minmax", "decode_attn_quest", "decode_attn_quest_workspace",
     "dattn_last_error", "dattn_version",
     "dattn_profile_enable", "dattn_profile_read", "dattn_profile_reset",
 )
@@ -57,6 +58,10 @@ def lib() -> ctypes.CDLL:
     L.decode_attn_gqa_workspace.argtypes = [I32] * 9
     L.kv_append_gqa.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, I32, P]
     L.kv_append_rows.argtypes = [P, P, P, P, I32, I32, I32, I32, I32, P]
+    L.quest_page_minmax.argtypes = [P, P, P, P, I32, I32, I32, I32, I32, I32, I32, P]
+    L.decode_attn_quest.argtypes = [P, P, P, P, P, P, I32, P, P, P, I32, I32, I32, I32, I32, I32,
+                                    I32, F, I32, P, SZ, P]
+    L.decode_attn_quest_workspace.argtypes = [I32] * 9
     L.decode_attn_mla.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, I32, F, I32,
                                   P, SZ, P]
     L.decode_attn_mla_workspace.argtypes = [I32] * 5
@@ -66,11 +71,11 @@ def lib() -> ctypes.CDLL:
     L.dsa_topk_workspace.argtypes = [I32] * 3
     L.sparse_mla_attn.argtypes = [P, P, P, I32, P, P, I32, I32, I32, I32, I32, I32, F, I32, P, SZ, P]
     L.sparse_mla_attn_workspace.argtypes = [I32] * 5
-    for name in ("decode_attn_gqa_workspace", "decode_attn_mla_workspace",
+    for name in ("decode_attn_gqa_workspace", "decode_attn_mla_workspace", "decode_attn_quest_workspace",
                  "dsa_indexer_topk_workspace", "dsa_topk_workspace", "sparse_mla_attn_workspace"):
         getattr(L, name).restype = SZ
     for name in ("decode_attn_gqa", "decode_attn_gqa_sink", "decode_attn_mla", "dsa_indexer_topk", "dsa_topk",
-                 "kv_append_gqa", "kv_append_rows",
+                 "kv_append_gqa", "kv_append_rows", "quest_page_minmax", "decode_attn_quest",
                  "sparse_mla_attn", "dattn_profile_enable", "dattn_profile_read",
                  "dattn_profile_reset"):
         getattr(L, name).restype = ctypes.c_int
@@ -200,6 +205,72 @@ def kv_append_rows(rows_new, cache, positions, page_table=None, *, stream=None):
     _check(lib().kv_append_rows(
         _ptr(rows_new.contiguous()), _ptr(cache), _ptr(positions), _ptr(page_table), B, X,
         page_size, max_pages, _dtype_code(rows_new), _stream(stream)))
+
+
+QUEST_BLOCK = 16  # tokens per summarised block
+
+
+def quest_page_minmax(k_cache, seq_lens, page_table=None, *, kminmax=None, first_block=0,
+                      stream=None):
+    """Per-block key summaries [B, Hkv, n_blocks, 2, D] (kmin, kmax) of a
+    decode_attn_gqa K cache; blocks [first_block, L_b // 16) are (re)written.
+    Returns kminmax (allocated when not given)."""
+    for t, n in ((k_cache, "k_cache"), (seq_lens, "seq_lens")):
+        _dev(t, n)
+    Hkv, page_size, D = k_cache.shape[1], k_cache.shape[2], k_cache.shape[3]
+    B = seq_lens.shape[0]
+    max_pages = 1
+    if page_table is not None:
+        _dev(page_table, "page_table")
+        max_pages = page_table.shape[1]
+    n_blocks = page_size * max_pages // QUEST_BLOCK
+    if kminmax is None:
+        kminmax = torch.empty(B, Hkv, n_blocks, 2, D, dtype=k_cache.dtype, device=k_cache.device)
+    else:
+        _dev(kminmax, "kminmax")
+        if tuple(kminmax.shape) != (B, Hkv, n_blocks, 2, D) or kminmax.dtype != k_cache.dtype:
+            raise ValueError(f"kminmax must be {k_cache.dtype} [{B}, {Hkv}, {n_blocks}, 2, {D}]")
+    _check(lib().quest_page_minmax(
+        _ptr(k_cache), _ptr(seq_lens), _ptr(page_table), _ptr(kminmax), int(first_block), B, Hkv, D,
+        page_size, max_pages, _dtype_code(k_cache), _stream(stream)))
+    return kminmax
+
+
+def decode_attn_quest(q, k_cache, v_cache, kminmax, seq_lens, budget, page_table=None, *,
+                      scale=None, num_splits=0, out=None, lse=None, want_lse=True,
+                      want_selected=False, workspace=None, stream=None):
+    """Quest decode: per query head the `budget` 16-token blocks with the
+    largest key bounds plus the partial last block.  Returns (out, lse) or,
+    with want_selected, (out, lse, selected [B, Hq, budget] int32, -1 padded)."""
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (kminmax, "kminmax"),
+                 (seq_lens, "seq_lens")):
+        _dev(t, n)
+    B, Hq, D = q.shape
+    Hkv, page_size = k_cache.shape[1], k_cache.shape[2]
+    max_pages = 1
+    if page_table is not None:
+        _dev(page_table, "page_table")
+        max_pages = page_table.shape[1]
+    if kminmax.dtype != k_cache.dtype or kminmax.shape[:2] != (B, Hkv):
+        raise ValueError("kminmax must come from quest_page_minmax on this cache")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty(B, Hq, dtype=torch.float32, device=q.device)
+    sel = torch.empty(B, Hq, int(budget), dtype=torch.int32, device=q.device) if want_selected else None
+    dt = _dtype_code(q)
+    nbytes = lib().decode_attn_quest_workspace(B, Hq, Hkv, D, page_size, max_pages, int(budget), dt,
+                                               int(num_splits))
+    if workspace is not None:
+        _dev(workspace, "workspace")
+        ws, nbytes = workspace, workspace.numel() * workspace.element_size()
+    else:
+        ws = _workspace(nbytes, q.device)
+    _check(lib().decode_attn_quest(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kminmax), _ptr(seq_lens), _ptr(page_table),
+        int(budget), _ptr(out), _ptr(lse), _ptr(sel), B, Hq, Hkv, D, page_size, max_pages, dt,
+        float(scale or 0.0), int(num_splits), _ptr(ws), nbytes, _stream(stream)))
+    return (out, lse, sel) if want_selected else (out, lse)
 
 
 def decode_attn_mla(q_absorbed, latent_cache, seq_lens, page_table=None, *, d_latent=512,

@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdarg>
@@ -522,6 +523,180 @@ int dsa_indexer_topk(const void* q_i, const float* w, const void* k_i_cache, con
   rc = launch("topk_select", s, [&] { return dattn::launch_topk(t, s); });
   return rc ? rc : ok();
 }
+
+}  // extern "C"
+
+// ------------------------------------------------------------------- Quest
+
+namespace {
+
+// Summary slots per sequence: the full 16-token blocks the cache can hold.
+int64_t quest_blocks(int32_t page_size, int32_t max_pages, bool paged) {
+  return (int64_t)page_size * (paged ? max_pages : 1) / 16;
+}
+
+int validate_quest_cache(const char* fn, const void* k, const void* kminmax, const int32_t* seq_lens,
+                         const int32_t* page_table, int32_t B, int32_t Hkv, int32_t D,
+                         int32_t page_size, int32_t max_pages, int32_t dtype) {
+  if (!k || !kminmax || !seq_lens) return fail(DATTN_EINVAL, "%s: NULL pointer argument", fn);
+  if (B < 1 || Hkv < 1) return fail(DATTN_EINVAL, "%s: B and Hkv must be >= 1", fn);
+  if (B > 65535 || Hkv > 65535) return fail(DATTN_EINVAL, "%s: B and Hkv must be <= 65535", fn);
+  if (D != 64 && D != 128) return fail(DATTN_EUNSUPPORTED, "%s: head dim %d not in {64,128}", fn, D);
+  if (dtype != DATTN_F32 && dtype != DATTN_BF16) return fail(DATTN_EUNSUPPORTED, "%s: dtype %d", fn, dtype);
+  if (page_size < 1) return fail(DATTN_EINVAL, "%s: page_size must be >= 1", fn);
+  if (page_table) {
+    if (!pow2(page_size) || page_size < 16)
+      return fail(DATTN_EUNSUPPORTED, "%s: paged cache needs a power-of-two page_size >= 16, got %d", fn, page_size);
+    if (max_pages < 1) return fail(DATTN_EINVAL, "%s: max_pages must be >= 1", fn);
+  }
+  if (quest_blocks(page_size, max_pages, page_table != nullptr) >= ((int64_t)1 << 31))
+    return fail(DATTN_EINVAL, "%s: too many 16-token blocks per sequence", fn);
+  return DATTN_OK;
+}
+
+dattn::QuestArgs quest_args(const void* q, const void* k, const void* kminmax, const int32_t* seq_lens,
+                            const int32_t* page_table, int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                            int32_t page_size, int32_t max_pages, int32_t dtype) {
+  dattn::QuestArgs a{};
+  a.q = q;
+  a.k = k;
+  a.kminmax = const_cast<void*>(kminmax);
+  a.seq_lens = seq_lens;
+  a.page_table = page_table;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.D = D;
+  a.G = Hq / Hkv;
+  a.page_size = page_size;
+  a.log2_page = page_table ? ilog2(page_size) : 0;
+  a.max_pages = page_table ? max_pages : 1;
+  a.max_blocks = (int32_t)quest_blocks(page_size, max_pages, page_table != nullptr);
+  a.bf16 = dtype == DATTN_BF16;
+  return a;
+}
+
+struct QuestPlan {
+  int splits;
+  size_t upper, n_full, sel, topk, parts, total;  // byte offsets of the workspace parts
+};
+
+QuestPlan plan_quest(int32_t B, int32_t Hq, int32_t D, int64_t max_blocks, int32_t budget, bool bf16,
+                     int32_t num_splits, bool own_sel) {
+  QuestPlan p{};
+  const int64_t rows = (int64_t)B * Hq;
+  const int64_t kept = budget < max_blocks ? budget : max_blocks;
+  const int64_t max_tokens = 16 * (kept + 1);  // the chosen blocks and the partial one
+  const int64_t slots =
+      num_splits > 0 ? 0 : (int64_t)std::max(dattn::gqa_listed_blocks_per_cu(bf16, D), 3) * dattn::device_cu_count();
+  p.splits = plan_gqa_splits((int32_t)B, Hq, max_tokens, num_splits, slots);
+  const int64_t nb = max_blocks > 0 ? max_blocks : 1;
+  p.upper = 0;
+  p.n_full = p.upper + align256((size_t)rows * nb * sizeof(float));
+  p.sel = p.n_full + align256((size_t)rows * sizeof(int32_t));
+  p.topk = p.sel + (own_sel ? align256((size_t)rows * budget * sizeof(int32_t)) : 0);
+  p.parts = p.topk + dattn::topk_workspace_bytes((int)rows, (int)nb);
+  p.total = p.parts + split_workspace(rows, p.splits, D);
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int quest_page_minmax(const void* k_cache, const int32_t* seq_lens, const int32_t* page_table,
+                      void* kminmax, int32_t first_block, int32_t B, int32_t Hkv, int32_t D,
+                      int32_t page_size, int32_t max_pages, int32_t dtype, void* stream) {
+  int rc = validate_quest_cache("quest_page_minmax", k_cache, kminmax, seq_lens, page_table, B, Hkv, D,
+                                page_size, max_pages, dtype);
+  if (rc) return rc;
+  if (first_block < 0) return fail(DATTN_EINVAL, "quest_page_minmax: first_block must be >= 0");
+  dattn::QuestArgs a = quest_args(nullptr, k_cache, kminmax, seq_lens, page_table, B, Hkv, Hkv, D,
+                                  page_size, max_pages, dtype);
+  a.first_block = first_block;
+  hipStream_t s = (hipStream_t)stream;
+  if ((rc = launch("quest_minmax", s, [&] { return dattn::launch_quest_minmax(a, s); }))) return rc;
+  return ok();
+}
+
+size_t decode_attn_quest_workspace(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t page_size,
+                                   int32_t max_pages, int32_t budget, int32_t dtype, int32_t num_splits) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || D < 1 || page_size < 1 || max_pages < 1 || budget < 1 ||
+      num_splits < 0)
+    return 0;
+  const QuestPlan p = plan_quest(B, Hq, D, quest_blocks(page_size, max_pages, true), budget,
+                                 dtype == DATTN_BF16, num_splits, true);
+  return p.total;
+}
+
+int decode_attn_quest(const void* q, const void* k_cache, const void* v_cache, const void* kminmax,
+                      const int32_t* seq_lens, const int32_t* page_table, int32_t budget, void* out,
+                      float* lse, int32_t* selected, int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                      int32_t page_size, int32_t max_pages, int32_t dtype, float scale, int32_t num_splits,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = validate_gqa(q, k_cache, v_cache, seq_lens, page_table, 0, out, B, Hq, Hkv, D, page_size,
+                        max_pages, dtype, scale, num_splits);
+  if (rc) return rc;
+  if ((rc = validate_quest_cache("decode_attn_quest", k_cache, kminmax, seq_lens, page_table, B, Hkv, D,
+                                 page_size, max_pages, dtype)))
+    return rc;
+  if (budget < 1 || budget > kTopkMax)
+    return fail(DATTN_EINVAL, "decode_attn_quest: budget = %d pages outside [1, %d]", budget, kTopkMax);
+  if ((int64_t)B * Hq > 65535) return fail(DATTN_EINVAL, "decode_attn_quest: B * Hq must be <= 65535");
+  const bool paged = page_table != nullptr;
+  dattn::QuestArgs qa = quest_args(q, k_cache, kminmax, seq_lens, page_table, B, Hq, Hkv, D, page_size,
+                                   max_pages, dtype);
+  const QuestPlan p = plan_quest(B, Hq, D, qa.max_blocks, budget, dtype == DATTN_BF16, num_splits,
+                                 selected == nullptr);
+  if ((rc = check_workspace(workspace, workspace_bytes, p.total))) return rc;
+  char* ws = (char*)workspace;
+  hipStream_t s = (hipStream_t)stream;
+  int32_t* sel = selected ? selected : (int32_t*)(ws + p.sel);
+  qa.upper = (float*)(ws + p.upper);
+  qa.n_full = (int32_t*)(ws + p.n_full);
+  if (qa.max_blocks > 0) {
+    if ((rc = launch("quest_bounds", s, [&] { return dattn::launch_quest_bounds(qa, s); }))) return rc;
+    dattn::TopkArgs t{qa.upper, qa.n_full, sel, B * Hq, qa.max_blocks, budget, (uint32_t*)(ws + p.topk), 0, 0};
+    if ((rc = launch("topk_select", s, [&] { return dattn::launch_topk(t, s); }))) return rc;
+  }
+
+  dattn::GqaArgs a{};
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.seq_lens = seq_lens;
+  a.page_table = page_table;
+  a.out = out;
+  a.lse = lse;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.D = D;
+  a.G = Hq / Hkv;
+  a.page_size = page_size;
+  a.log2_page = paged ? ilog2(page_size) : 0;
+  a.max_pages = paged ? max_pages : 1;
+  a.num_splits = p.splits;
+  a.bf16 = dtype == DATTN_BF16;
+  const float sc = scale > 0.f ? scale : 1.0f / std::sqrt((float)D);
+  a.scale_log2 = sc * 1.4426950408889634f;
+  a.block_list = sel;
+  a.list_len = qa.max_blocks > 0 ? budget : 0;
+  if (p.splits > 1) {
+    a.part_o = (float*)(ws + p.parts);
+    a.part_lse = (float*)(ws + p.parts + align256((size_t)B * Hq * p.splits * D * sizeof(float)));
+  }
+  if ((rc = launch("gqa_split", s, [&] { return dattn::launch_gqa(a, s); }))) return rc;
+  if (p.splits > 1) {
+    dattn::CombineArgs c{a.part_o, a.part_lse, nullptr, out, lse, B * Hq, p.splits, D, a.bf16};
+    if ((rc = launch("lse_combine", s, [&] { return dattn::launch_combine(c, s); }))) return rc;
+  }
+  return ok();
+}
+
+}  // extern "C"
+
+extern "C" {
 
 // ------------------------------------------------------------- cache append
 static int append_common(const char* fn, const void* ptrs[], int n_ptrs, const int32_t* positions,

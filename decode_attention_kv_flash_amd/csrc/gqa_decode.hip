@@ -77,7 +77,11 @@ __device__ __forceinline__ float row_sum(float x) {
 
 // PAGED_FAST: paged with page_size % 16 == 0, or contiguous (one lookup per
 // block); otherwise every token resolves its own page.
-template <bool BF16, int D, int G, bool PAGED_FAST>
+// LISTED: the token set is a list of 16-token blocks per query head (the
+// pages a query-aware selection chose, ascending, -1 padded) plus the
+// partial last block; one query head per workgroup (G = 1), reading KV head
+// h / (Hq / Hkv).
+template <bool BF16, int D, int G, bool PAGED_FAST, bool LISTED = false>
 __global__ __launch_bounds__(kThreads) void gqa_split_kernel(const GqaArgs a) {
   using S = GqaShape<BF16, D>;
   constexpr int VEC = S::VEC, LPR = S::LPR, RPI = S::RPI, TPL = S::TPL;
@@ -88,21 +92,27 @@ __global__ __launch_bounds__(kThreads) void gqa_split_kernel(const GqaArgs a) {
   const int r = lane / LPR;  // token row within one wave load
   const int c = lane % LPR;  // 16-byte piece of the row
   const int split = blockIdx.x;
-  const int kvh = blockIdx.y;
+  static_assert(!LISTED || G == 1, "a listed token set is per query head");
+  const int qh0 = LISTED ? (int)blockIdx.y : (int)blockIdx.y * G;  // first query head
+  const int kvh = LISTED ? (int)blockIdx.y / a.G : (int)blockIdx.y;
   const int b = blockIdx.z;
 
   // Token set [0, s_cnt) u [w_start, L) as 16-token blocks: sink blocks
-  // first, then the window's blocks (aligned down to 16).
+  // first, then the window's blocks (aligned down to 16).  LISTED: the
+  // listed blocks, then the partial last block.
   const int L = a.seq_lens[b];
   int s_cnt = 0, w_start = 0;
-  if (a.window > 0 && a.window < L) {
+  if (!LISTED && a.window > 0 && a.window < L) {
     w_start = L - a.window;
     s_cnt = min(a.n_sink, w_start);
   }
-  const int n_sb = (s_cnt + kStep - 1) / kStep;
+  const int n_full = L / kStep;
+  const int n_sb = LISTED ? min(a.list_len, n_full) : (s_cnt + kStep - 1) / kStep;
   const int wb0 = w_start / kStep;
-  const int n_wb = L > 0 ? (L + kStep - 1) / kStep - wb0 : 0;
+  const int n_wb = LISTED ? (L % kStep != 0) : L > 0 ? (L + kStep - 1) / kStep - wb0 : 0;
   const int n_blocks = n_sb + n_wb;
+  const cint32_t* list = LISTED ? (const cint32_t*)(uintptr_t)(a.block_list + ((size_t)b * a.Hq + qh0) * a.list_len)
+                                : nullptr;
   const int per = (n_blocks + a.num_splits - 1) / a.num_splits;
   const int blk_begin = min(n_blocks, split * per);
   const int blk_end = min(n_blocks, blk_begin + per);
@@ -110,7 +120,7 @@ __global__ __launch_bounds__(kThreads) void gqa_split_kernel(const GqaArgs a) {
   // This lane's piece of each of the G query rows: dims c*VEC + [0, VEC).
   uint4 qv[G];
   {
-    const char* qb = (const char*)a.q + ((size_t)(b * a.Hq + kvh * G) * D + c * VEC) * S::ESZ;
+    const char* qb = (const char*)a.q + ((size_t)(b * a.Hq + qh0) * D + c * VEC) * S::ESZ;
 #pragma unroll
     for (int h = 0; h < G; ++h) qv[h] = *(const uint4*)(qb + (size_t)h * D * S::ESZ);
   }
@@ -136,11 +146,17 @@ __global__ __launch_bounds__(kThreads) void gqa_split_kernel(const GqaArgs a) {
   const size_t lane_off = (size_t)c * 16;
 
   auto block_start = [&](int blk) {
+    if constexpr (LISTED) return (blk < n_sb ? max((int)list[blk], 0) : n_full) * kStep;
     return blk < n_sb ? blk * kStep : (wb0 + blk - n_sb) * kStep;
   };
   // Attended token range [lo, hi) inside block blk (never empty for a block
   // below blk_end).
   auto block_range = [&](int blk, int t0, int& lo, int& hi) {
+    if constexpr (LISTED) {
+      lo = t0;
+      hi = min(L, t0 + kStep);
+      return;
+    }
     const bool sink = blk < n_sb;
     lo = max(sink ? 0 : w_start, t0);
     hi = min(sink ? s_cnt : L, t0 + kStep);
@@ -308,7 +324,7 @@ __global__ __launch_bounds__(kThreads) void gqa_split_kernel(const GqaArgs a) {
   }
   __syncthreads();
 
-  const size_t row0 = (size_t)b * a.Hq + (size_t)kvh * G;
+  const size_t row0 = (size_t)b * a.Hq + (size_t)qh0;
   // an explicit sink logit joins the denominator once per row: here when
   // this workgroup holds the whole row, else in the combine
   const bool with_sink = a.sink != nullptr && a.num_splits == 1;
@@ -317,7 +333,7 @@ __global__ __launch_bounds__(kThreads) void gqa_split_kernel(const GqaArgs a) {
     float M = NEG_INF;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][h]);
-    const float sink2 = with_sink ? a.sink[kvh * G + h] * kLog2e : NEG_INF;
+    const float sink2 = with_sink ? a.sink[qh0 + h] * kLog2e : NEG_INF;
     M = fmaxf(M, sink2);
     const float mu = M == NEG_INF ? 0.f : M;
     float lsum = with_sink ? fast_exp2(sink2 - mu) : 0.f, acc = 0.f;
@@ -357,6 +373,12 @@ hipError_t launch_df(const GqaArgs& a, hipStream_t s) {
 template <bool BF16, int D>
 hipError_t launch_d(const GqaArgs& a, hipStream_t s) {
   const bool fast = !a.page_table || a.page_size % kStep == 0;
+  if (a.block_list) {  // listed 16-token blocks: the page table (or contiguous cache) is block-aligned
+    if (!fast) return hipErrorInvalidValue;
+    dim3 grid(a.num_splits, a.Hq, a.B), block(kThreads);
+    gqa_split_kernel<BF16, D, 1, true, true><<<grid, block, 0, s>>>(a);
+    return hipGetLastError();
+  }
   return fast ? launch_df<BF16, D, true>(a, s) : launch_df<BF16, D, false>(a, s);
 }
 
@@ -367,6 +389,18 @@ int occupancy_one() {
     int v = 0;
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, gqa_split_kernel<BF16, D, G, FAST>, kThreads, 0) ==
                    hipSuccess
+               ? v
+               : 0;
+  }();
+  return n;
+}
+
+template <bool BF16, int D>
+int occupancy_listed() {
+  static const int n = [] {
+    int v = 0;
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, gqa_split_kernel<BF16, D, 1, true, true>, kThreads,
+                                                        0) == hipSuccess
                ? v
                : 0;
   }();
@@ -455,6 +489,11 @@ hipError_t launch_gqa(const GqaArgs& a, hipStream_t s) {
     if (a.D == 128) return launch_d<false, 128>(a, s);
   }
   return hipErrorInvalidValue;
+}
+
+int gqa_listed_blocks_per_cu(bool bf16, int D) {
+  if (bf16) return D == 64 ? occupancy_listed<true, 64>() : occupancy_listed<true, 128>();
+  return D == 64 ? occupancy_listed<false, 64>() : occupancy_listed<false, 128>();
 }
 
 int gqa_blocks_per_cu(bool bf16, int D, int G, bool paged, int page_size) {

@@ -33,11 +33,34 @@ struct GqaArgs {
   // nullptr, or one sink logit per query head [Hq] (natural log): an extra
   // softmax-denominator term exp(sink) with a zero value
   const float* sink;
+  // nullptr, or per query head a list of 16-token blocks [B, Hq, list_len]
+  // (ascending, -1 padded) attended besides the partial last block; window
+  // and sinks are then unused and the grid runs one query head per workgroup
+  const int32_t* block_list;
+  int32_t list_len;
 };
 
 hipError_t launch_gqa(const GqaArgs& a, hipStream_t s);
 // Resident workgroups per CU of the split kernel for this shape (0 if unknown).
 int gqa_blocks_per_cu(bool bf16, int D, int G, bool paged, int page_size);
+int gqa_listed_blocks_per_cu(bool bf16, int D);
+
+// Query-aware page selection (Quest): per-block key min/max summaries and the
+// per-query-head bounds; the choice itself runs on the top-k select.
+struct QuestArgs {
+  const void* q;              // [B, Hq, D]
+  const void* k;              // K cache, decode_attn_gqa layout
+  const int32_t* seq_lens;
+  const int32_t* page_table;  // or nullptr (contiguous)
+  void* kminmax;              // [B, Hkv, max_blocks, 2, D] k's type
+  float* upper;               // [B * Hq, max_blocks] fp32
+  int32_t* n_full;            // [B * Hq]: full blocks of the row's sequence
+  int32_t B, Hq, Hkv, D, G, page_size, log2_page, max_pages, max_blocks, first_block;
+  int32_t bf16;
+};
+
+hipError_t launch_quest_minmax(const QuestArgs& a, hipStream_t s);
+hipError_t launch_quest_bounds(const QuestArgs& a, hipStream_t s);
 
 struct CombineArgs {
   const float* part_o;    // [rows, splits, D]

@@ -27,7 +27,10 @@
 //             so indices come out ascending and ties go to the lower index.
 // Workgroup 0 of a row records each decision for the next launch.  Rows with
 // seq_len <= k are written directly by the first launch.  Nothing in the
-// workspace has to be cleared beforehand.
+// workspace has to be cleared beforehand.  When every row fits one chunk
+// (S_max <= 2048, e.g. a selection over 16-token pages), one workgroup owns a
+// row and runs the four levels and the write in a single launch, with the
+// histograms in LDS.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -231,30 +234,15 @@ __global__ __launch_bounds__(kTT) void topk_digit_kernel(const TopkArgs a) {
   }
 }
 
-__global__ __launch_bounds__(kTT) void topk_write_kernel(const TopkArgs a) {
-  __shared__ uint32_t wave_tot[kNW], res[2], red[kNW], eq_pre;
-  __shared__ uint32_t off_gt[kKPT * kNW], off_eq[kKPT * kNW];
-  const int c = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const RowWs w = row_ws(a, b);
-  uint32_t key[kKPT];
-  load_keys(a, b, c, key);
-  const uint32_t p24 = w.st[4], need2 = w.st[5];
-  uint32_t ab = 0;  // keys above T's top three bytes in the chunks before this one
-  for (int cc = tid; cc < c; cc += kTT) ab += w.above[cc];
-  const int L = row_len(a, b), K = a.k;
-  uint32_t tot, pre;
-  row_column_sums(a, w.h + (size_t)3 * a.n_chunks * kBins, L, c, tot, pre);
-  if (L <= K || c * kChunk >= L) return;
-  const uint32_t valid = valid_mask(c, L);
-  uint32_t need;
-  const uint32_t d0 = find_byte(tot, need2, wave_tot, res, need);
-  const uint32_t T = (p24 << 8) | d0;
-  const uint32_t bin = kBins - 1 - tid;
-  if (bin == d0) eq_pre = pre;
-  const uint32_t base_gt = block_sum(ab + (bin > d0 ? pre : 0u), red);  // syncs: eq_pre visible
-  const uint32_t base_eq = eq_pre;
-
+// Writes the taken keys of chunk c: those above T, and the first `need`
+// equal to T in row order, at ranks counted from base_gt / base_eq (the keys
+// above / equal to T in the chunks before this one), so that indices come out
+// ascending.
+__device__ __forceinline__ void rank_and_write(const TopkArgs& a, int b, int c, const uint32_t (&key)[kKPT],
+                                               uint32_t valid, uint32_t T, uint32_t need, uint32_t base_gt,
+                                               uint32_t base_eq, uint32_t* off_gt, uint32_t* off_eq) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int K = a.k;
   // per (column j, wave) counts, then exclusive offsets in token order
   uint64_t mg[kKPT], me[kKPT];
 #pragma unroll
@@ -302,6 +290,67 @@ __global__ __launch_bounds__(kTT) void topk_write_kernel(const TopkArgs a) {
   }
 }
 
+__global__ __launch_bounds__(kTT) void topk_write_kernel(const TopkArgs a) {
+  __shared__ uint32_t wave_tot[kNW], res[2], red[kNW], eq_pre;
+  __shared__ uint32_t off_gt[kKPT * kNW], off_eq[kKPT * kNW];
+  const int c = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const RowWs w = row_ws(a, b);
+  uint32_t key[kKPT];
+  load_keys(a, b, c, key);
+  const uint32_t p24 = w.st[4], need2 = w.st[5];
+  uint32_t ab = 0;  // keys above T's top three bytes in the chunks before this one
+  for (int cc = tid; cc < c; cc += kTT) ab += w.above[cc];
+  const int L = row_len(a, b), K = a.k;
+  uint32_t tot, pre;
+  row_column_sums(a, w.h + (size_t)3 * a.n_chunks * kBins, L, c, tot, pre);
+  if (L <= K || c * kChunk >= L) return;
+  const uint32_t valid = valid_mask(c, L);
+  uint32_t need;
+  const uint32_t d0 = find_byte(tot, need2, wave_tot, res, need);
+  const uint32_t T = (p24 << 8) | d0;
+  const uint32_t bin = kBins - 1 - tid;
+  if (bin == d0) eq_pre = pre;
+  const uint32_t base_gt = block_sum(ab + (bin > d0 ? pre : 0u), red);  // syncs: eq_pre visible
+  const uint32_t base_eq = eq_pre;
+
+  rank_and_write(a, b, c, key, valid, T, need, base_gt, base_eq, off_gt, off_eq);
+}
+
+// One workgroup per row when the row fits one chunk (S_max <= 2048): the four
+// byte levels run in LDS back to back, then the same ranked write, in one
+// launch.
+__global__ __launch_bounds__(kTT) void topk_single_kernel(const TopkArgs a) {
+  __shared__ uint32_t hist[kBins], wave_tot[kNW], res[2];
+  __shared__ uint32_t off_gt[kKPT * kNW], off_eq[kKPT * kNW];
+  const int b = blockIdx.y, tid = threadIdx.x;
+  uint32_t key[kKPT];
+  load_keys(a, b, 0, key);
+  const int L = row_len(a, b), K = a.k;
+  if (L <= K) {
+    int32_t* out = a.idx + (size_t)b * K;
+    for (int j = tid; j < K; j += kTT) out[j] = j < L ? j : -1;
+    return;
+  }
+  const uint32_t valid = valid_mask(0, L);
+  uint32_t prefix = 0, need = (uint32_t)K;
+#pragma unroll
+  for (int level = 0; level < 4; ++level) {
+    const int shift = 24 - 8 * level;
+    hist[tid] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kKPT; ++j) {
+      const bool m = ((valid >> j) & 1u) && (level == 0 || (key[j] >> (shift + 8)) == prefix);
+      hist_add(hist, m, (key[j] >> shift) & (kBins - 1));
+    }
+    __syncthreads();
+    uint32_t rest;
+    prefix = (prefix << 8) | find_byte(hist[kBins - 1 - tid], need, wave_tot, res, rest);
+    need = rest;
+  }
+  rank_and_write(a, b, 0, key, valid, prefix, need, 0u, 0u, off_gt, off_eq);
+}
+
 }  // namespace
 
 size_t topk_workspace_bytes(int B, int S_max) {
@@ -314,6 +363,10 @@ hipError_t launch_topk(const TopkArgs& a0, hipStream_t s) {
   a.n_chunks = (a.S_max + kChunk - 1) / kChunk;
   a.row_words = (int64_t)topk_row_words(a.n_chunks);
   const dim3 grid(a.n_chunks, a.B);
+  if (a.n_chunks == 1) {
+    topk_single_kernel<<<grid, kTT, 0, s>>>(a);
+    return hipGetLastError();
+  }
   topk_digit_kernel<0><<<grid, kTT, 0, s>>>(a);
   topk_digit_kernel<1><<<grid, kTT, 0, s>>>(a);
   topk_digit_kernel<2><<<grid, kTT, 0, s>>>(a);

@@ -130,26 +130,34 @@ def _paginate(g, k_log, v_log, seq_lens, page_size):
 
 def make_gqa(*, B, Hq, Hkv, D, seq_lens, dtype=torch.bfloat16, page_size=16,
              paged=True, window=0, n_sink=0, sink_key_scale=1.0, scale=None,
-             seed=0, name="") -> GQAInputs:
+             qk_int=0, seed=0, name="") -> GQAInputs:
     """Build a GQA/SWA decode workload.
 
     ``seq_lens`` is a list of per-sequence cached-token counts (the current
     token included).  ``sink_key_scale`` multiplies the key rows of tokens
     ``0..n_sink-1`` before rounding (a stand-in for the sink dominance of real
     models).  ``paged=False`` gives the contiguous cache ``[B, Hkv, S_max, D]``
-    (one page per sequence, page_size = S_max, no page table).
+    (one page per sequence, page_size = S_max, no page table).  ``qk_int`` > 0
+    draws q and K as integers uniform in [-qk_int, qk_int] (V stays N(0,1)),
+    so that dot products and page bounds are exact in fp32.
     """
     g = _gen(seed)
     seq_lens = [int(x) for x in seq_lens]
     assert len(seq_lens) == B
     S_max = max(1, max(seq_lens))
-    q = _normal(g, (B, Hq, D), dtype)
+    if qk_int > 0:
+        q = torch.randint(-qk_int, qk_int + 1, (B, Hq, D), generator=g).to(dtype)
+    else:
+        q = _normal(g, (B, Hq, D), dtype)
     k = torch.zeros(B, Hkv, S_max, D, dtype=dtype)
     v = torch.zeros(B, Hkv, S_max, D, dtype=dtype)
     for b, L in enumerate(seq_lens):
         if L == 0:
             continue
-        kb = torch.randn(Hkv, L, D, generator=g, dtype=torch.float32)
+        if qk_int > 0:
+            kb = torch.randint(-qk_int, qk_int + 1, (Hkv, L, D), generator=g).float()
+        else:
+            kb = torch.randn(Hkv, L, D, generator=g, dtype=torch.float32)
         if sink_key_scale != 1.0 and n_sink > 0:
             kb[:, : min(n_sink, L)] *= sink_key_scale
         k[b, :, :L] = kb.to(dtype)

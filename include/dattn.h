@@ -186,6 +186,71 @@ DATTN_EXPORT int kv_append_rows(const void* rows_new, void* cache, const int32_t
                   int32_t max_pages, int32_t dtype, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Query-aware page selection (Quest) over a GQA cache.
+ *
+ * Every query picks, per step, which pages of the cache it reads ("Long
+ * context, KV eviction and sparse attention", "Sparse attention: choosing
+ * dynamically at every step"; "Attention Optimizations", "Query-aware
+ * retrieval").  The cache is cut into blocks of 16 tokens (the pages of that
+ * passage); block p of (sequence b, KV head g) keeps kmin_p and kmax_p, the
+ * per-dimension minimum and maximum of its 16 keys.  Query head h bounds
+ * q . k over block p by
+ *   upper[h, p] = sum_d max(q_d kmin_p[d], q_d kmax_p[d])
+ * and attends to the `budget` full blocks with the largest bounds (ties go to
+ * the lower block) plus the last, partial block (L_b % 16 tokens, always
+ * kept); a sequence with at most `budget` full blocks attends to all of them.
+ * Each query head chooses its own blocks; query head h reads KV head
+ * h / (Hq / Hkv).
+ *
+ * quest_page_minmax: writes the summaries of blocks [first_block, L_b / 16)
+ *   of every sequence and KV head; other slots are left as they are.  After
+ *   appending token L_b - 1 a caller refreshes only the block it completed
+ *   (first_block = that block; summaries are pure functions of the keys, so
+ *   recomputing one is harmless).
+ *   k_cache    the decode_attn_gqa K layout and page table; paged caches need
+ *              a power-of-two page_size >= 16 (a block never straddles pages)
+ *   kminmax    [B, Hkv, n_blocks, 2, D] in dtype, n_blocks = page_size *
+ *              max_pages / 16 (contiguous: S_max / 16, max_pages = 1):
+ *              [.., 0, :] = kmin, [.., 1, :] = kmax (exact; min and max pick
+ *              cached values)
+ *   first_block >= 0
+ *
+ * decode_attn_quest: bounds, selection and attention in one call:
+ *   q, k_cache, v_cache, seq_lens, page_table, out, lse, dtype, scale,
+ *   num_splits   as for decode_attn_gqa (no window, no sinks); Hq / Hkv in
+ *                {1,2,4,8}; paged caches need page_size >= 16
+ *   kminmax      the summaries quest_page_minmax wrote, read-only
+ *   budget       blocks kept per query head, 1 <= budget <= 16384
+ *   selected     NULL, or device int32 [B, Hq, budget]: the chosen blocks in
+ *                ascending order, -1 padded (written)
+ *   B * Hq <= 65535
+ *   workspace    at least decode_attn_quest_workspace(...) bytes, 256-byte
+ *                aligned; no initialisation needed; calls sharing it must be
+ *                ordered on one stream
+ * Bounds run in fp32 on MFMAs (products of bf16 values exact, fp32 sums);
+ * the choice is the top-k select of dsa_topk over each query head's bounds.
+ * Errors: DATTN_EINVAL / DATTN_EUNSUPPORTED / DATTN_EWORKSPACE before any
+ * launch, DATTN_EHIP if a launch fails.
+ */
+DATTN_EXPORT int quest_page_minmax(const void* k_cache, const int32_t* seq_lens,
+                  const int32_t* page_table, void* kminmax, int32_t first_block,
+                  int32_t B, int32_t Hkv, int32_t D, int32_t page_size, int32_t max_pages,
+                  int32_t dtype, void* stream);
+
+DATTN_EXPORT int decode_attn_quest(const void* q, const void* k_cache, const void* v_cache,
+                  const void* kminmax, const int32_t* seq_lens, const int32_t* page_table,
+                  int32_t budget, void* out, float* lse, int32_t* selected,
+                  int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t page_size,
+                  int32_t max_pages, int32_t dtype, float scale, int32_t num_splits,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes decode_attn_quest needs (an upper bound over `selected`
+ * given or not); max_pages = 1 for a contiguous cache. */
+DATTN_EXPORT size_t decode_attn_quest_workspace(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                  int32_t page_size, int32_t max_pages, int32_t budget, int32_t dtype,
+                  int32_t num_splits);
+
+/* ------------------------------------------------------------------------ */
 /* Absorbed MLA decode attention over a latent cache.
  *
  * For each sequence b and head h: s_t = scale * q_absorbed[b,h] . row_t over

@@ -173,3 +173,55 @@ def test_append_rows_validation():
     # a latent row of 577 bf16 values is not a multiple of 16 bytes
     assert L.kv_append_rows(P(256), P(256), P(256), None, 2, 577, 100, 1, 1, None) == -2
     assert L.kv_append_rows(None, P(256), P(256), None, 2, 576, 100, 1, 1, None) == -1
+
+
+def _quest(**kw):
+    args = dict(q=256, k=256, v=256, kmm=256, seq_lens=256, page_table=256, budget=8, out=256,
+                lse=None, sel=None, B=2, Hq=8, Hkv=2, D=128, page_size=16, max_pages=64, dtype=1,
+                scale=0.0, num_splits=0, ws=None, ws_bytes=0)
+    args.update(kw)
+    P = lambda x: None if x is None else ctypes.c_void_p(x)
+    return api.lib().decode_attn_quest(
+        P(args["q"]), P(args["k"]), P(args["v"]), P(args["kmm"]), P(args["seq_lens"]),
+        P(args["page_table"]), args["budget"], P(args["out"]), P(args["lse"]), P(args["sel"]),
+        args["B"], args["Hq"], args["Hkv"], args["D"], args["page_size"], args["max_pages"],
+        args["dtype"], args["scale"], args["num_splits"], P(args["ws"]), args["ws_bytes"], None)
+
+
+# Every case fails before a launch: the last ones for want of a workspace.
+@pytest.mark.parametrize("kw,code", [
+    (dict(kmm=None), -1),
+    (dict(q=None), -1),
+    (dict(budget=0), -1),
+    (dict(budget=16385), -1),
+    (dict(page_size=8), -2),                 # a 16-token block would straddle pages
+    (dict(D=96), -2),
+    (dict(Hq=48, Hkv=2), -2),
+    (dict(B=4096, Hq=32, Hkv=8), -1),        # B * Hq rows above the select's grid
+    (dict(), -3),                            # bounds, select and partials need a workspace
+    (dict(page_table=None, page_size=1000, max_pages=1), -3),
+])
+def test_quest_validation(kw, code):
+    rc = _quest(**kw)
+    assert rc == code, api.lib().dattn_last_error()
+    assert api.lib().dattn_last_error()
+
+
+def test_quest_minmax_validation():
+    L = api.lib()
+    P = ctypes.c_void_p
+    # k_cache, seq_lens, page_table, kminmax, first_block, B, Hkv, D, page_size, max_pages, dtype
+    assert L.quest_page_minmax(None, P(256), None, P(256), 0, 2, 2, 128, 64, 1, 1, None) == -1
+    assert L.quest_page_minmax(P(256), P(256), None, P(256), -1, 2, 2, 128, 64, 1, 1, None) == -1
+    assert L.quest_page_minmax(P(256), P(256), P(256), P(256), 0, 2, 2, 128, 8, 4, 1, None) == -2
+    assert L.quest_page_minmax(P(256), P(256), None, P(256), 0, 2, 2, 128, 64, 1, 2, None) == -2
+
+
+def test_quest_workspace_sizes():
+    L = api.lib()
+    # rows x blocks fp32 bounds + per-row counts + selection + select workspace + partials
+    one = L.decode_attn_quest_workspace(2, 8, 2, 128, 16, 64, 8, 1, 1)
+    more = L.decode_attn_quest_workspace(2, 8, 2, 128, 16, 64, 8, 1, 4)
+    assert one >= 16 * 64 * 4 + 16 * 4 + 16 * 8 * 4
+    assert more - one == 16 * 4 * 128 * 4 + 256    # the split partials (o, then lse aligned)
+    assert L.decode_attn_quest_workspace(0, 8, 2, 128, 16, 64, 8, 1, 1) == 0
