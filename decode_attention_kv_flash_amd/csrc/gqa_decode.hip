@@ -17,8 +17,11 @@
 //   * a lane holds one 16-byte piece of a token row: LPR = row bytes / 16
 //     lanes cover a row, one wave load instruction reads 64 / LPR whole rows,
 //     and a lane holds 16 * LPR / 64 rows of a block for K and as many for V;
-//   * two register buffers per wave: the loads of the wave's next block are
-//     in flight while it computes the current one;
+//   * one register buffer per wave, loaded and then consumed; latency is
+//     hidden across waves (a small register footprint keeps several
+//     workgroups resident per CU, so one wave's loads overlap another's
+//     arithmetic), and the page of the wave's next block is looked up one
+//     step ahead;
 //   * scores are lane-partial dot products (v_dot2_f32_bf16 for bf16: the
 //     bf16 products are exact in fp32) summed over the row's lanes with DPP;
 //   * the softmax is the online one ("All the attentions", section 1: a
@@ -31,6 +34,11 @@
 //     (fp32 accumulation); for fp32 inputs it is plain fp32 FMA.
 // A split's result is (o / l, log2-sum-exp); lse_combine merges the splits
 // (lse = max + log2 sum 2^(lse_j - max), o = sum 2^(lse_j - lse) o_j).
+//
+// The same kernel attends a listed token set (query-aware page selection,
+// "Long context, KV eviction and sparse attention", "Sparse attention:
+// choosing dynamically at every step"): per query head a list of 16-token
+// blocks plus the partial last block, one query head per workgroup.
 #include "common.hpp"
 #include "internal.hpp"
 

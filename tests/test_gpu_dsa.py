@@ -140,6 +140,21 @@ def test_topk_long_and_ragged_rows(n_distinct, k):
     assert torch.equal(got, want)
 
 
+@pytest.mark.parametrize("n_distinct", [None, 1, 3])
+@pytest.mark.parametrize("k", [1, 100, 2047, 2048])
+def test_topk_rows_within_one_chunk(n_distinct, k):
+    """S_max <= 2048: one workgroup per row runs the whole select in one
+    launch; ragged, empty, all-equal and k >= length rows."""
+    lens = [0, 1, 99, 100, 1500, 2047, 2048]
+    say(f"[dsa] topk one chunk lens={lens} k={k} n_distinct={n_distinct}")
+    s = wl.make_scores(B=len(lens), seq_lens=lens, n_distinct=n_distinct, seed=k + 11)
+    assert s.shape[1] == 2048
+    sl = torch.tensor(lens, dtype=torch.int32)
+    got = api.dsa_topk(dev(s), dev(sl), k).cpu()
+    want = oracle.topk(s, sl, k)
+    assert torch.equal(got, want)
+
+
 def test_topk_ignores_workspace_contents():
     """The workspace holds no state between calls: garbage in it changes nothing."""
     lens = [9000, 20000, 5]
