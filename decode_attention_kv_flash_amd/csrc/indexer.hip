@@ -12,10 +12,10 @@
 // exact).
 //
 // Work split: each wave takes steps of its workgroup's token range (32
-// tokens in bf16, 64 in fp8: 8 KB either way) and keeps two of them in its
+// tokens in bf16, 64 in fp8: 8 KB either way) and keeps three of them in its
 // own LDS buffers: a step's keys go
 // from HBM to LDS by direct-to-LDS copies of whole 1 KB runs (full cache
-// lines), issued one step ahead.  The MFMA B fragments of lane l are token
+// lines), issued two steps ahead.  The MFMA B fragments of lane l are token
 // l % 32's dims (bf16: 16 kk + 8 (l / 32) .. + 7, one 16-byte LDS read per
 // k-step; fp8: 64 (l / 32) + 8 kk .. + 7, four 16-byte reads for all eight).
 // Rows keep their 16-byte chunks permuted by a row key (slot_key), so the
@@ -34,6 +34,11 @@ constexpr int kDi = 128;
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTokMma = 32;    // tokens per MFMA (the B operand's columns)
+// 8 KB step buffers per wave: two steps in flight while one is computed.
+// (96 KB of LDS per workgroup, one workgroup per CU; measured against two
+// buffers at two workgroups per CU and four or five at one: 24.1 us against
+// 25.9, 24.3 and 25.1 us for 8 x 65536 bf16 keys.)
+constexpr int kBufs = 3;
 
 template <bool FP8>
 struct IdxShape {
@@ -57,10 +62,22 @@ __device__ __forceinline__ int slot_key(int r) {
 // 32x32x16 fp8 MFMAs, the lane holds dims 64 half + 8 kk + [0, 8) (one
 // 64-byte run of the row); both operands use the same dims at the same
 // (lane, k-step, slot), so the contraction is the plain dot product.
+// Wait until at most `later` x COPIES vector-memory operations of this wave
+// are outstanding (later in [0, AHEAD]).
+template <int AHEAD, int COPIES>
+__device__ __forceinline__ void wait_copies_after(int later) {
+  static_assert(AHEAD * COPIES < 64, "vmcnt range");
+  if constexpr (AHEAD >= 4) if (later == 4) { wait_vmcnt<4 * COPIES>(); return; }
+  if constexpr (AHEAD >= 3) if (later == 3) { wait_vmcnt<3 * COPIES>(); return; }
+  if constexpr (AHEAD >= 2) if (later == 2) { wait_vmcnt<2 * COPIES>(); return; }
+  if constexpr (AHEAD >= 1) if (later == 1) { wait_vmcnt<COPIES>(); return; }
+  wait_vmcnt<0>();
+}
+
 template <int NMT, bool FP8>
 __global__ __launch_bounds__(kThreads) void indexer_kernel(const IndexerArgs a) {
   using S = IdxShape<FP8>;
-  __shared__ __attribute__((aligned(16))) char kbuf[kWaves][2][S::kStepBytes];
+  __shared__ __attribute__((aligned(16))) char kbuf[kWaves][kBufs][S::kStepBytes];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int half = lane >> 5;
@@ -113,17 +130,26 @@ __global__ __launch_bounds__(kThreads) void indexer_kernel(const IndexerArgs a) 
     }
   };
 
-  int buf = 0;
+  // The wave's steps j = 0 .. n_steps - 1 start at token t0 + (wave + kWaves j)
+  // kStep; step j lives in buffer j % kBufs and is requested kAhead steps
+  // before it is used.  Before using step j the wave waits until only the
+  // copies of the steps requested after it (at most kAhead) are in flight;
+  // the score stores it has issued meanwhile are not counted, which only
+  // makes the wait stricter.
   constexpr int kStep = S::kTokStep;
-  if (t0 + wave * kStep < t1) issue(t0 + wave * kStep, 0);
+  constexpr int kAhead = kBufs - 1;
+  const int first = t0 + wave * kStep;
+  const int n_steps = first < t1 ? (t1 - first + kWaves * kStep - 1) / (kWaves * kStep) : 0;
+#pragma unroll
+  for (int j = 0; j < kAhead; ++j)
+    if (j < n_steps) issue(first + j * kWaves * kStep, j);
+  int buf = 0, nbuf = kAhead;  // buffer of step j, and of step j + kAhead
 #pragma unroll 1
-  for (int tb = t0 + wave * kStep; tb < t1; tb += kWaves * kStep) {
-    if (tb + kWaves * kStep < t1) {
-      issue(tb + kWaves * kStep, buf ^ 1);
-      wait_vmcnt<S::kCopies>();  // this step's copies are in (the next step's may not be)
-    } else {
-      wait_vmcnt<0>();
-    }
+  for (int j = 0; j < n_steps; ++j) {
+    const int tb = first + j * kWaves * kStep;
+    if (j + kAhead < n_steps) issue(tb + kAhead * kWaves * kStep, nbuf);
+    const int later = min(kAhead, n_steps - 1 - j);  // steps requested after this one
+    wait_copies_after<kAhead, S::kCopies>(later);
 #pragma unroll
     for (int sub = 0; sub < kStep / kTokMma; ++sub) {
     const char* kb = &kbuf[wave][buf][0] + (kTokMma * sub + lj) * S::kRowBytes;
@@ -161,7 +187,8 @@ __global__ __launch_bounds__(kThreads) void indexer_kernel(const IndexerArgs a) 
     part += __shfl_xor(part, 32);
     if (half == 0 && t < a.S_max) out[t] = valid ? part : -__builtin_inff();
     }
-    buf ^= 1;
+    buf = buf == kBufs - 1 ? 0 : buf + 1;
+    nbuf = nbuf == kBufs - 1 ? 0 : nbuf + 1;
   }
 }
 
