@@ -236,7 +236,14 @@ def bench_quest(x, timer, steps, warmup, torch, lib, budget):
              None, x.B, x.Hq, x.Hkv, x.D, x.page_size, max_pages, dt, ctypes.c_float(x.scale), 0,
              ptr(ws), nbytes, stream) for r in range(R)]
     rec = timer.run(lambda i: check(lib, lib.decode_attn_quest(*args[i % R])), steps, warmup,
-                    ["quest_bounds", "topk_select", "gqa_split", "lse_combine"])
+                    ["quest_bounds", "topk_select", "quest_union", "gqa_split", "lse_combine"])
+    # the chosen blocks, for the bytes the attention reads once per KV head
+    sel = torch.empty(x.B, x.Hq, budget, dtype=torch.int32, device=dev)
+    a0 = list(args[0])
+    a0[9] = ptr(sel)
+    check(lib, lib.decode_attn_quest(*a0))
+    torch.cuda.synchronize()
+    rec["selected"] = sel.cpu()
     # the summary of every block, and the refresh of one block per sequence
     rec["minmax_full"] = timer.run(lambda i: check(lib, lib.quest_page_minmax(*mm[i % R])), steps,
                                    warmup // 4, ["quest_minmax"])
@@ -248,18 +255,27 @@ def bench_quest(x, timer, steps, warmup, torch, lib, budget):
     return rec
 
 
-def quest_bytes(x, budget):
+def quest_bytes(x, budget, selected=None):
     """Algorithmic bytes of one Quest step: block summaries, the bounds
-    written and read back by the select, and K/V of the chosen tokens per
-    query head."""
+    written and read back by the select, and K/V of the chosen tokens: per
+    query head, and (given the chosen blocks [B, Hq, budget]) once per KV head
+    for the union of its query heads' blocks."""
+    import torch
     esz = x.k.element_size()
-    summ = sel = bounds = 0
-    for L in x.seq_lens.tolist():
+    G = x.Hq // x.Hkv
+    row = 2 * x.D * esz  # K + V bytes of one token of one KV head
+    summ = per_head = bounds = union = 0
+    for b, L in enumerate(x.seq_lens.tolist()):
         nf = L // 16
         summ += x.Hkv * nf * 2 * x.D * esz
         bounds += 2 * x.Hq * nf * 4
-        sel += x.Hq * (min(budget, nf) * 16 + L % 16) * 2 * x.D * esz
-    return summ, bounds, sel
+        per_head += x.Hq * (min(budget, nf) * 16 + L % 16) * row
+        if selected is not None:
+            for g in range(x.Hkv):
+                s = selected[b, g * G:(g + 1) * G]
+                n = torch.unique(s[s >= 0]).numel()
+                union += (n * 16 + L % 16) * row
+    return summ, bounds, per_head, union
 
 
 def bench_append(timer, steps, warmup, torch, lib):
@@ -394,16 +410,18 @@ def main():
         log(f"[bench] quest on the gqa config, budget {budget} blocks")
         rq = bench_quest(x2, timer, steps, warmup, torch, lib, budget)
         kq = rq["kernels"]
-        summ, bnd, selb = quest_bytes(x2, budget)
+        summ, bnd, selb, unib = quest_bytes(x2, budget, rq.pop("selected"))
         kbytes = x2.k.element_size() * x2.Hkv * x2.D * int(x2.seq_lens.sum())
         mm_us = rq["minmax_full"]["kernels"]["quest_minmax"]["avg_us"]
         result["workloads"]["quest_llama3_8b_budget2048"] = {
             "step_us": round(rq["wall_ms"] * 1e3, 2),
             "dense_step_us": round(r2["wall_ms"] * 1e3, 2),
-            "bytes_per_step": summ + bnd + selb,
-            "GB/s": round((summ + bnd + selb) / (rq["wall_ms"] * 1e-3) / 1e9, 1),
+            "bytes_per_step": summ + bnd + unib,
+            "GB/s": round((summ + bnd + unib) / (rq["wall_ms"] * 1e-3) / 1e9, 1),
+            "kv_bytes_per_head_sum": selb,
+            "kv_bytes_union_per_kv_head": unib,
             "bounds_GB/s": round(gbs(summ, kq["quest_bounds"]["avg_us"]), 1),
-            "attention_GB/s": round(gbs(selb, kq["gqa_split"]["avg_us"]), 1),
+            "attention_GB/s": round(gbs(unib, kq["gqa_split"]["avg_us"]), 1),
             "topk_us": kq["topk_select"]["avg_us"],
             "kernels_us": {k: v["avg_us"] for k, v in kq.items()},
             "minmax_all_blocks_us": round(mm_us, 2),
@@ -518,7 +536,9 @@ def only(name, timer, steps, warmup, torch, lib, wl):
     elif name == "quest":
         x = wl.config2_llama3_8b_gqa()
         r = bench_quest(x, timer, steps, warmup, torch, lib, 128)
-        r["bytes_per_step"] = sum(quest_bytes(x, 128))
+        summ, bnd, selb, unib = quest_bytes(x, 128, r.pop("selected"))
+        r["bytes_per_step"] = summ + bnd + unib
+        r["kv_bytes_per_head_sum"], r["kv_bytes_union_per_kv_head"] = selb, unib
     else:
         d = wl.config5_dsa()
         r = bench_dsa(d, timer, steps, warmup, torch, lib)

@@ -576,26 +576,39 @@ dattn::QuestArgs quest_args(const void* q, const void* k, const void* kminmax, c
   return a;
 }
 
+// The attention reads each chosen block once per group of query heads (the
+// union of their choices) when the group has more than one head and the
+// per-head bitmaps fit the union kernel; else one query head per workgroup.
 struct QuestPlan {
+  bool uni;
   int splits;
-  size_t upper, n_full, sel, topk, parts, total;  // byte offsets of the workspace parts
+  int32_t cap;  // union entries per (sequence, KV head)
+  size_t upper, n_full, sel, topk, ulist, ucount, parts, total;  // byte offsets of the workspace parts
 };
 
-QuestPlan plan_quest(int32_t B, int32_t Hq, int32_t D, int64_t max_blocks, int32_t budget, bool bf16,
-                     int32_t num_splits, bool own_sel) {
+QuestPlan plan_quest(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int64_t max_blocks, int32_t budget,
+                     bool bf16, int32_t num_splits, bool own_sel) {
   QuestPlan p{};
+  const int G = Hq / Hkv;
   const int64_t rows = (int64_t)B * Hq;
   const int64_t kept = budget < max_blocks ? budget : max_blocks;
-  const int64_t max_tokens = 16 * (kept + 1);  // the chosen blocks and the partial one
+  p.uni = G > 1 && max_blocks > 0 && max_blocks <= dattn::kQuestUnionMaxBlocks;
+  p.cap = p.uni ? (int32_t)std::min<int64_t>((int64_t)G * budget, max_blocks) : 0;
+  const int64_t units = p.uni ? (int64_t)B * Hkv : rows;
+  const int64_t max_tokens = 16 * ((p.uni ? p.cap : kept) + 1);  // the chosen blocks and the partial one
   const int64_t slots =
-      num_splits > 0 ? 0 : (int64_t)std::max(dattn::gqa_listed_blocks_per_cu(bf16, D), 3) * dattn::device_cu_count();
-  p.splits = plan_gqa_splits((int32_t)B, Hq, max_tokens, num_splits, slots);
+      num_splits > 0 ? 0
+                     : (int64_t)std::max(dattn::gqa_listed_blocks_per_cu(bf16, D, G, p.uni), 3) *
+                           dattn::device_cu_count();
+  p.splits = plan_gqa_splits((int32_t)units, 1, max_tokens, num_splits, slots);
   const int64_t nb = max_blocks > 0 ? max_blocks : 1;
   p.upper = 0;
   p.n_full = p.upper + align256((size_t)rows * nb * sizeof(float));
   p.sel = p.n_full + align256((size_t)rows * sizeof(int32_t));
   p.topk = p.sel + (own_sel ? align256((size_t)rows * budget * sizeof(int32_t)) : 0);
-  p.parts = p.topk + dattn::topk_workspace_bytes((int)rows, (int)nb);
+  p.ulist = p.topk + dattn::topk_workspace_bytes((int)rows, (int)nb);
+  p.ucount = p.ulist + (p.uni ? align256((size_t)B * Hkv * p.cap * sizeof(int32_t)) : 0);
+  p.parts = p.ucount + (p.uni ? align256((size_t)B * Hkv * sizeof(int32_t)) : 0);
   p.total = p.parts + split_workspace(rows, p.splits, D);
   return p;
 }
@@ -624,7 +637,8 @@ size_t decode_attn_quest_workspace(int32_t B, int32_t Hq, int32_t Hkv, int32_t D
   if (B < 1 || Hq < 1 || Hkv < 1 || D < 1 || page_size < 1 || max_pages < 1 || budget < 1 ||
       num_splits < 0)
     return 0;
-  const QuestPlan p = plan_quest(B, Hq, D, quest_blocks(page_size, max_pages, true), budget,
+  if (Hq % Hkv != 0) return 0;
+  const QuestPlan p = plan_quest(B, Hq, Hkv, D, quest_blocks(page_size, max_pages, true), budget,
                                  dtype == DATTN_BF16, num_splits, true);
   return p.total;
 }
@@ -646,7 +660,7 @@ int decode_attn_quest(const void* q, const void* k_cache, const void* v_cache, c
   const bool paged = page_table != nullptr;
   dattn::QuestArgs qa = quest_args(q, k_cache, kminmax, seq_lens, page_table, B, Hq, Hkv, D, page_size,
                                    max_pages, dtype);
-  const QuestPlan p = plan_quest(B, Hq, D, qa.max_blocks, budget, dtype == DATTN_BF16, num_splits,
+  const QuestPlan p = plan_quest(B, Hq, Hkv, D, qa.max_blocks, budget, dtype == DATTN_BF16, num_splits,
                                  selected == nullptr);
   if ((rc = check_workspace(workspace, workspace_bytes, p.total))) return rc;
   char* ws = (char*)workspace;
@@ -658,6 +672,11 @@ int decode_attn_quest(const void* q, const void* k_cache, const void* v_cache, c
     if ((rc = launch("quest_bounds", s, [&] { return dattn::launch_quest_bounds(qa, s); }))) return rc;
     dattn::TopkArgs t{qa.upper, qa.n_full, sel, B * Hq, qa.max_blocks, budget, (uint32_t*)(ws + p.topk), 0, 0};
     if ((rc = launch("topk_select", s, [&] { return dattn::launch_topk(t, s); }))) return rc;
+  }
+  if (p.uni) {
+    dattn::QuestUnionArgs u{sel, seq_lens, (int32_t*)(ws + p.ulist), (int32_t*)(ws + p.ucount), B, Hq, Hkv,
+                            Hq / Hkv, budget, p.cap, qa.max_blocks};
+    if ((rc = launch("quest_union", s, [&] { return dattn::launch_quest_union(u, s); }))) return rc;
   }
 
   dattn::GqaArgs a{};
@@ -680,8 +699,14 @@ int decode_attn_quest(const void* q, const void* k_cache, const void* v_cache, c
   a.bf16 = dtype == DATTN_BF16;
   const float sc = scale > 0.f ? scale : 1.0f / std::sqrt((float)D);
   a.scale_log2 = sc * 1.4426950408889634f;
-  a.block_list = sel;
-  a.list_len = qa.max_blocks > 0 ? budget : 0;
+  if (p.uni) {
+    a.block_list = (const int32_t*)(ws + p.ulist);
+    a.list_len = p.cap;
+    a.list_count = (const int32_t*)(ws + p.ucount);
+  } else {
+    a.block_list = sel;
+    a.list_len = qa.max_blocks > 0 ? budget : 0;
+  }
   if (p.splits > 1) {
     a.part_o = (float*)(ws + p.parts);
     a.part_lse = (float*)(ws + p.parts + align256((size_t)B * Hq * p.splits * D * sizeof(float)));

@@ -38,7 +38,10 @@
 // The same kernel attends a listed token set (query-aware page selection,
 // "Long context, KV eviction and sparse attention", "Sparse attention:
 // choosing dynamically at every step"): per query head a list of 16-token
-// blocks plus the partial last block, one query head per workgroup.
+// blocks plus the partial last block, either one query head per workgroup
+// or, for a group of heads sharing a KV head, the union of their lists with
+// the heads that chose each block, so that a block two heads chose is read
+// once.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -85,11 +88,19 @@ __device__ __forceinline__ float row_sum(float x) {
 
 // PAGED_FAST: paged with page_size % 16 == 0, or contiguous (one lookup per
 // block); otherwise every token resolves its own page.
-// LISTED: the token set is a list of 16-token blocks per query head (the
-// pages a query-aware selection chose, ascending, -1 padded) plus the
-// partial last block; one query head per workgroup (G = 1), reading KV head
-// h / (Hq / Hkv).
-template <bool BF16, int D, int G, bool PAGED_FAST, bool LISTED = false>
+// SET: which tokens a query head attends.
+//   kSetWindow: [0, L) or window + sinks;
+//   kSetPerHead: a list of 16-token blocks per query head (the pages a
+//     query-aware selection chose, ascending, -1 padded) plus the partial
+//     last block; one query head per workgroup (G = 1), reading KV head
+//     h / (Hq / Hkv);
+//   kSetUnion: the union of the G heads' block lists, ascending, each entry
+//     block | heads << 24 (the heads that chose it), plus the partial last
+//     block: every chosen block is read once for the whole group and
+//     attended by the heads that chose it only.
+constexpr int kSetWindow = 0, kSetPerHead = 1, kSetUnion = 2;
+
+template <bool BF16, int D, int G, bool PAGED_FAST, int SET = kSetWindow>
 __global__ __launch_bounds__(kThreads) void gqa_split_kernel(const GqaArgs a) {
   using S = GqaShape<BF16, D>;
   constexpr int VEC = S::VEC, LPR = S::LPR, RPI = S::RPI, TPL = S::TPL;
@@ -100,9 +111,10 @@ __global__ __launch_bounds__(kThreads) void gqa_split_kernel(const GqaArgs a) {
   const int r = lane / LPR;  // token row within one wave load
   const int c = lane % LPR;  // 16-byte piece of the row
   const int split = blockIdx.x;
-  static_assert(!LISTED || G == 1, "a listed token set is per query head");
-  const int qh0 = LISTED ? (int)blockIdx.y : (int)blockIdx.y * G;  // first query head
-  const int kvh = LISTED ? (int)blockIdx.y / a.G : (int)blockIdx.y;
+  constexpr bool LISTED = SET != kSetWindow;
+  static_assert(SET != kSetPerHead || G == 1, "a per-head token set has one head per workgroup");
+  const int qh0 = SET == kSetPerHead ? (int)blockIdx.y : (int)blockIdx.y * G;  // first query head
+  const int kvh = SET == kSetPerHead ? (int)blockIdx.y / a.G : (int)blockIdx.y;
   const int b = blockIdx.z;
 
   // Token set [0, s_cnt) u [w_start, L) as 16-token blocks: sink blocks
@@ -115,12 +127,13 @@ __global__ __launch_bounds__(kThreads) void gqa_split_kernel(const GqaArgs a) {
     s_cnt = min(a.n_sink, w_start);
   }
   const int n_full = L / kStep;
-  const int n_sb = LISTED ? min(a.list_len, n_full) : (s_cnt + kStep - 1) / kStep;
+  const int n_listed = SET == kSetUnion ? a.list_count[b * a.Hkv + kvh] : a.list_len;
+  const int n_sb = LISTED ? min(n_listed, n_full) : (s_cnt + kStep - 1) / kStep;
   const int wb0 = w_start / kStep;
   const int n_wb = LISTED ? (L % kStep != 0) : L > 0 ? (L + kStep - 1) / kStep - wb0 : 0;
   const int n_blocks = n_sb + n_wb;
-  const cint32_t* list = LISTED ? (const cint32_t*)(uintptr_t)(a.block_list + ((size_t)b * a.Hq + qh0) * a.list_len)
-                                : nullptr;
+  const size_t list_row = SET == kSetUnion ? (size_t)b * a.Hkv + kvh : (size_t)b * a.Hq + qh0;
+  const cint32_t* list = LISTED ? (const cint32_t*)(uintptr_t)(a.block_list + list_row * a.list_len) : nullptr;
   const int per = (n_blocks + a.num_splits - 1) / a.num_splits;
   const int blk_begin = min(n_blocks, split * per);
   const int blk_end = min(n_blocks, blk_begin + per);
@@ -154,7 +167,8 @@ __global__ __launch_bounds__(kThreads) void gqa_split_kernel(const GqaArgs a) {
   const size_t lane_off = (size_t)c * 16;
 
   auto block_start = [&](int blk) {
-    if constexpr (LISTED) return (blk < n_sb ? max((int)list[blk], 0) : n_full) * kStep;
+    if constexpr (SET == kSetUnion) return (blk < n_sb ? (int)((uint32_t)list[blk] & 0xffffffu) : n_full) * kStep;
+    if constexpr (SET == kSetPerHead) return (blk < n_sb ? max((int)list[blk], 0) : n_full) * kStep;
     return blk < n_sb ? blk * kStep : (wb0 + blk - n_sb) * kStep;
   };
   // Attended token range [lo, hi) inside block blk (never empty for a block
@@ -209,6 +223,9 @@ __global__ __launch_bounds__(kThreads) void gqa_split_kernel(const GqaArgs a) {
     int lo, hi;
     block_range(blk, t0, lo, hi);
     if (blk >= blk_end) hi = lo;
+    // heads that attend this block (a union list names them; else all)
+    uint32_t heads = 0xffu;
+    if constexpr (SET == kSetUnion) heads = blk < n_sb ? (uint32_t)list[blk] >> 24 : 0xffu;
     // scores (log2 units) of the lane's TPL tokens
     float s[TPL][G];
 #pragma unroll
@@ -230,7 +247,7 @@ __global__ __launch_bounds__(kThreads) void gqa_split_kernel(const GqaArgs a) {
           acc = fmaf(__uint_as_float(R.k[u].w), __uint_as_float(qv[h].w), acc);
         }
         acc = row_sum<LPR>(acc) * a.scale_log2;
-        s[u][h] = valid ? acc : NEG_INF;
+        s[u][h] = valid && ((heads >> h) & 1u) ? acc : NEG_INF;
       }
     }
 
@@ -383,8 +400,19 @@ hipError_t launch_d(const GqaArgs& a, hipStream_t s) {
   const bool fast = !a.page_table || a.page_size % kStep == 0;
   if (a.block_list) {  // listed 16-token blocks: the page table (or contiguous cache) is block-aligned
     if (!fast) return hipErrorInvalidValue;
-    dim3 grid(a.num_splits, a.Hq, a.B), block(kThreads);
-    gqa_split_kernel<BF16, D, 1, true, true><<<grid, block, 0, s>>>(a);
+    if (!a.list_count) {
+      dim3 grid(a.num_splits, a.Hq, a.B), block(kThreads);
+      gqa_split_kernel<BF16, D, 1, true, kSetPerHead><<<grid, block, 0, s>>>(a);
+      return hipGetLastError();
+    }
+    dim3 grid(a.num_splits, a.Hkv, a.B), block(kThreads);
+    switch (a.G) {
+      case 1: gqa_split_kernel<BF16, D, 1, true, kSetUnion><<<grid, block, 0, s>>>(a); break;
+      case 2: gqa_split_kernel<BF16, D, 2, true, kSetUnion><<<grid, block, 0, s>>>(a); break;
+      case 4: gqa_split_kernel<BF16, D, 4, true, kSetUnion><<<grid, block, 0, s>>>(a); break;
+      case 8: gqa_split_kernel<BF16, D, 8, true, kSetUnion><<<grid, block, 0, s>>>(a); break;
+      default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
   }
   return fast ? launch_df<BF16, D, true>(a, s) : launch_df<BF16, D, false>(a, s);
@@ -403,16 +431,28 @@ int occupancy_one() {
   return n;
 }
 
-template <bool BF16, int D>
+template <bool BF16, int D, int G, int SET>
 int occupancy_listed() {
   static const int n = [] {
     int v = 0;
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, gqa_split_kernel<BF16, D, 1, true, true>, kThreads,
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, gqa_split_kernel<BF16, D, G, true, SET>, kThreads,
                                                         0) == hipSuccess
                ? v
                : 0;
   }();
   return n;
+}
+
+template <bool BF16, int D>
+int occupancy_set(int G, bool uni) {
+  if (!uni) return occupancy_listed<BF16, D, 1, kSetPerHead>();
+  switch (G) {
+    case 1: return occupancy_listed<BF16, D, 1, kSetUnion>();
+    case 2: return occupancy_listed<BF16, D, 2, kSetUnion>();
+    case 4: return occupancy_listed<BF16, D, 4, kSetUnion>();
+    case 8: return occupancy_listed<BF16, D, 8, kSetUnion>();
+    default: return 0;
+  }
 }
 
 template <bool BF16, int D, bool FAST>
@@ -499,9 +539,9 @@ hipError_t launch_gqa(const GqaArgs& a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-int gqa_listed_blocks_per_cu(bool bf16, int D) {
-  if (bf16) return D == 64 ? occupancy_listed<true, 64>() : occupancy_listed<true, 128>();
-  return D == 64 ? occupancy_listed<false, 64>() : occupancy_listed<false, 128>();
+int gqa_listed_blocks_per_cu(bool bf16, int D, int G, bool uni) {
+  if (bf16) return D == 64 ? occupancy_set<true, 64>(G, uni) : occupancy_set<true, 128>(G, uni);
+  return D == 64 ? occupancy_set<false, 64>(G, uni) : occupancy_set<false, 128>(G, uni);
 }
 
 int gqa_blocks_per_cu(bool bf16, int D, int G, bool paged, int page_size) {

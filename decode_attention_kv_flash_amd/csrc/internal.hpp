@@ -33,17 +33,22 @@ struct GqaArgs {
   // nullptr, or one sink logit per query head [Hq] (natural log): an extra
   // softmax-denominator term exp(sink) with a zero value
   const float* sink;
-  // nullptr, or per query head a list of 16-token blocks [B, Hq, list_len]
-  // (ascending, -1 padded) attended besides the partial last block; window
-  // and sinks are then unused and the grid runs one query head per workgroup
+  // nullptr, or 16-token blocks attended besides the partial last block
+  // (window and sinks are then unused):
+  //   list_count == nullptr: per query head [B, Hq, list_len], ascending,
+  //     -1 padded; the grid runs one query head per workgroup;
+  //   else per (sequence, KV head) [B, Hkv, list_len] entries block | heads
+  //     << 24 (bit h: query head h of the group attends the block), ascending,
+  //     list_count[b * Hkv + kvh] of them.
   const int32_t* block_list;
   int32_t list_len;
+  const int32_t* list_count;
 };
 
 hipError_t launch_gqa(const GqaArgs& a, hipStream_t s);
 // Resident workgroups per CU of the split kernel for this shape (0 if unknown).
 int gqa_blocks_per_cu(bool bf16, int D, int G, bool paged, int page_size);
-int gqa_listed_blocks_per_cu(bool bf16, int D);
+int gqa_listed_blocks_per_cu(bool bf16, int D, int G, bool uni);
 
 // Query-aware page selection (Quest): per-block key min/max summaries and the
 // per-query-head bounds; the choice itself runs on the top-k select.
@@ -61,6 +66,19 @@ struct QuestArgs {
 
 hipError_t launch_quest_minmax(const QuestArgs& a, hipStream_t s);
 hipError_t launch_quest_bounds(const QuestArgs& a, hipStream_t s);
+
+// Union of the chosen blocks of the G query heads of each (sequence, KV
+// head): sel [B * Hq, budget] (ascending, -1 padded) -> list [B * Hkv, cap]
+// entries block | heads << 24 ascending, count [B * Hkv].
+struct QuestUnionArgs {
+  const int32_t* sel;
+  const int32_t* seq_lens;
+  int32_t* list;
+  int32_t* count;
+  int32_t B, Hq, Hkv, G, budget, cap, max_blocks;
+};
+constexpr int kQuestUnionMaxBlocks = 8192;  // bitmap of 256 words per head in LDS
+hipError_t launch_quest_union(const QuestUnionArgs& a, hipStream_t s);
 
 struct CombineArgs {
   const float* part_o;    // [rows, splits, D]

@@ -201,6 +201,62 @@ __global__ __launch_bounds__(kThreads) void quest_bounds_kernel(const QuestArgs 
   }
 }
 
+// One workgroup per (sequence, KV head): the blocks the group's G query
+// heads chose become one bitmap per head in LDS.  Thread t owns word t of
+// their union and an exclusive prefix sum over the words' populations gives
+// each word's first position; then every thread places blocks of its own
+// (blk = t, t + 256, ...) at that position plus the union bits below it in
+// its word, so the union comes out ascending, each entry carrying the heads
+// that chose the block.
+__global__ __launch_bounds__(kThreads) void quest_union_kernel(const QuestUnionArgs a) {
+  constexpr int kWords = kQuestUnionMaxBlocks / 32;
+  static_assert(kWords == kThreads, "one bitmap word per thread");
+  __shared__ uint32_t bm[8][kWords];
+  __shared__ uint32_t uw[kWords], first[kWords];
+  __shared__ uint32_t wave_sum[kWaves];
+  const int kvh = blockIdx.x, b = blockIdx.y;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int L = max(a.seq_lens[b], 0);
+  const int n_full = min(L / kBlock, a.max_blocks);
+  const int kept = min(a.budget, n_full);
+  const int words = (n_full + 31) / 32;
+  for (int h = 0; h < a.G; ++h) bm[h][t] = 0u;
+  __syncthreads();
+  for (int i = t; i < a.G * kept; i += kThreads) {
+    const int h = i / kept, j = i - h * kept;
+    const int blk = a.sel[((size_t)b * a.Hq + kvh * a.G + h) * a.budget + j];
+    if (blk >= 0 && blk < n_full) atomicOr(&bm[h][blk >> 5], 1u << (blk & 31));
+  }
+  __syncthreads();
+  uint32_t u = 0u;
+  for (int h = 0; h < a.G; ++h) u |= bm[h][t];
+  const uint32_t cnt = __popc(u);
+  uint32_t inc = cnt;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t y = __shfl_up(inc, d);
+    if (lane >= d) inc += y;
+  }
+  if (lane == 63) wave_sum[wave] = inc;
+  __syncthreads();
+  uint32_t before = inc - cnt;
+  for (int w = 0; w < wave; ++w) before += wave_sum[w];
+  uw[t] = u;
+  first[t] = before;
+  if (t == kThreads - 1) a.count[(size_t)b * a.Hkv + kvh] = min((int)(before + cnt), a.cap);
+  __syncthreads();
+  int32_t* out = a.list + ((size_t)b * a.Hkv + kvh) * a.cap;
+  for (int blk = t; blk < 32 * words; blk += kThreads) {
+    const int w = blk >> 5, j = blk & 31;
+    const uint32_t x = uw[w];
+    if (!((x >> j) & 1u)) continue;
+    const uint32_t k = first[w] + __popc(x & ((1u << j) - 1u));
+    uint32_t heads = 0u;
+    for (int h = 0; h < a.G; ++h) heads |= ((bm[h][w] >> j) & 1u) << h;
+    if (k < (uint32_t)a.cap) out[k] = blk | (int32_t)(heads << 24);
+  }
+}
+
 template <bool BF16, int D>
 hipError_t minmax_d(const QuestArgs& a, hipStream_t s) {
   const int wgs = (a.max_blocks + kWaves - 1) / kWaves - a.first_block / kWaves;
@@ -223,6 +279,12 @@ hipError_t bounds_d(const QuestArgs& a, hipStream_t s) {
 hipError_t launch_quest_minmax(const QuestArgs& a, hipStream_t s) {
   if (a.bf16) return a.D == 64 ? minmax_d<true, 64>(a, s) : minmax_d<true, 128>(a, s);
   return a.D == 64 ? minmax_d<false, 64>(a, s) : minmax_d<false, 128>(a, s);
+}
+
+hipError_t launch_quest_union(const QuestUnionArgs& a, hipStream_t s) {
+  if (a.G > 8 || a.max_blocks > kQuestUnionMaxBlocks) return hipErrorInvalidValue;
+  quest_union_kernel<<<dim3(a.Hkv, a.B), kThreads, 0, s>>>(a);
+  return hipGetLastError();
 }
 
 hipError_t launch_quest_bounds(const QuestArgs& a, hipStream_t s) {

@@ -149,3 +149,23 @@ def test_quest_llama_shape_sampled_sequences():
             assert s[h].tolist() == c, f"b={b} h={h}"
         assert_rows_close(got[rows], want, tol_for(x.q.dtype), f"{x.name} b={b}")
         assert_lse_close(glse[rows], wlse, 1e-5, f"{x.name} b={b}")
+
+
+def test_quest_per_head_lists_when_the_table_is_wide():
+    """Above 8192 blocks per sequence the union bitmaps do not fit: each query
+    head then runs its own workgroup over its own list (groups of 4 here)."""
+    import torch.nn.functional as F
+    x = wl.make_gqa(B=3, Hq=8, Hkv=2, D=128, seq_lens=[300, 17, 1029], dtype=torch.bfloat16, page_size=16,
+                    qk_int=2, seed=87, name="quest_wide_table")
+    x.page_table = F.pad(x.page_table, (0, 8200 - x.page_table.shape[1]))
+    for budget in (3, 40):
+        check_quest(x, budget)
+
+
+def test_quest_union_at_the_bitmap_limit():
+    """8192 blocks per sequence, the most the union bitmaps hold: 131067
+    tokens, 4 query heads on one KV head, 700 blocks each."""
+    x = wl.make_gqa(B=1, Hq=4, Hkv=1, D=64, seq_lens=[131067], dtype=torch.bfloat16, page_size=16,
+                    qk_int=2, seed=88, name="quest_bitmap_limit")
+    assert x.page_table.shape[1] == 8192
+    check_quest(x, 700)
