@@ -229,6 +229,10 @@ DATTN_EXPORT int kv_append_rows(const void* rows_new, void* cache, const int32_t
  *                ordered on one stream
  * Bounds run in fp32 on MFMAs (products of bf16 values exact, fp32 sums);
  * the choice is the top-k select of dsa_topk over each query head's bounds.
+ * For a group of query heads sharing a KV head, each block any of them chose
+ * is read once and attended by the heads that chose it (the result is the
+ * per-head attention above); tables of more than 8192 blocks per sequence
+ * attend per head.
  * Errors: DATTN_EINVAL / DATTN_EUNSUPPORTED / DATTN_EWORKSPACE before any
  * launch, DATTN_EHIP if a launch fails.
  */
