@@ -199,6 +199,9 @@ int launch(const char* name, hipStream_t s, F&& f) {
   return DATTN_OK;
 }
 
+// Kernels move data in 16-byte vectors.
+bool aligned16(const void* p) { return (uintptr_t)p % 16 == 0; }
+
 int check_workspace(void* ws, size_t have, size_t need) {
   if (need == 0) return DATTN_OK;
   if (!ws) return fail(DATTN_EWORKSPACE, "workspace is NULL but %zu bytes are needed", need);
@@ -213,6 +216,8 @@ int validate_gqa(const void* q, const void* k, const void* v, const int32_t* seq
                  int32_t Hq, int32_t Hkv, int32_t D, int32_t page_size, int32_t max_pages,
                  int32_t dtype, float scale, int32_t num_splits) {
   if (!q || !k || !v || !seq_lens || !out) return fail(DATTN_EINVAL, "decode_attn_gqa: NULL pointer argument");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(DATTN_EINVAL, "decode_attn_gqa: q, k_cache, v_cache and out must be 16-byte aligned");
   if (B < 1 || Hq < 1 || Hkv < 1) return fail(DATTN_EINVAL, "decode_attn_gqa: B, Hq, Hkv must be >= 1");
   if (B > 65535 || Hkv > 65535) return fail(DATTN_EINVAL, "decode_attn_gqa: B and Hkv must be <= 65535");
   if (Hq % Hkv != 0) return fail(DATTN_EINVAL, "decode_attn_gqa: Hq (%d) is not a multiple of Hkv (%d)", Hq, Hkv);
@@ -236,6 +241,8 @@ int validate_mla_common(const char* fn, const void* q, const void* latent, const
                         int32_t H, int32_t d_latent, int32_t d_rope, int32_t S_max, int32_t dtype,
                         float scale, int32_t num_splits) {
   if (!q || !latent || !out) return fail(DATTN_EINVAL, "%s: NULL pointer argument", fn);
+  if (!aligned16(q) || !aligned16(latent) || !aligned16(out))
+    return fail(DATTN_EINVAL, "%s: q, latent_cache and out must be 16-byte aligned", fn);
   if (B < 1 || H < 1 || S_max < 1) return fail(DATTN_EINVAL, "%s: B, H, S_max must be >= 1", fn);
   if (B > 65535) return fail(DATTN_EINVAL, "%s: B must be <= 65535", fn);
   if (d_latent != 512 || d_rope != 64)
@@ -501,6 +508,8 @@ int dsa_indexer_topk(const void* q_i, const float* w, const void* k_i_cache, con
                      size_t workspace_bytes, void* stream) {
   if (!q_i || !w || !k_i_cache || !seq_lens || !topk_idx)
     return fail(DATTN_EINVAL, "dsa_indexer_topk: NULL pointer argument");
+  if (!aligned16(q_i) || !aligned16(k_i_cache))
+    return fail(DATTN_EINVAL, "dsa_indexer_topk: q_i and k_i_cache must be 16-byte aligned");
   if (B < 1 || S_max < 1) return fail(DATTN_EINVAL, "dsa_indexer_topk: B and S_max must be >= 1");
   if (B > 65535) return fail(DATTN_EINVAL, "dsa_indexer_topk: B must be <= 65535");
   if (k < 1 || k > kTopkMax) return fail(DATTN_EINVAL, "dsa_indexer_topk: k = %d outside [1, %d]", k, kTopkMax);
@@ -539,6 +548,7 @@ int validate_quest_cache(const char* fn, const void* k, const void* kminmax, con
                          const int32_t* page_table, int32_t B, int32_t Hkv, int32_t D,
                          int32_t page_size, int32_t max_pages, int32_t dtype) {
   if (!k || !kminmax || !seq_lens) return fail(DATTN_EINVAL, "%s: NULL pointer argument", fn);
+  if (!aligned16(k) || !aligned16(kminmax)) return fail(DATTN_EINVAL, "%s: k_cache and kminmax must be 16-byte aligned", fn);
   if (B < 1 || Hkv < 1) return fail(DATTN_EINVAL, "%s: B and Hkv must be >= 1", fn);
   if (B > 65535 || Hkv > 65535) return fail(DATTN_EINVAL, "%s: B and Hkv must be <= 65535", fn);
   if (D != 64 && D != 128) return fail(DATTN_EUNSUPPORTED, "%s: head dim %d not in {64,128}", fn, D);

@@ -468,11 +468,12 @@ int occupancy_g(int G) {
 
 // Merge split partials (o_j normalised, lse_j in log2 units):
 // lse = max + log2 sum_j 2^(lse_j - max); o = sum_j 2^(lse_j - lse) o_j.
-// One thread per output element; it loads its row's split log-sum-exps and
-// its split partials together (one memory round trip), then merges.  Splits
-// may also hand over unnormalised sums with their reference maximum and
-// softmax denominator (CombineArgs::part_l): the same merge with weights
-// 2^(m - M) on both the sums and the denominators.
+// One thread per four consecutive output elements of a row; it loads its
+// row's split log-sum-exps and its 16-byte pieces of the split partials
+// together (one memory round trip), then merges.  Splits may also hand over
+// unnormalised sums with their reference maximum and softmax denominator
+// (CombineArgs::part_l): the same merge with weights 2^(m - M) on both the
+// sums and the denominators.
 constexpr int kCombineThreads = 256;
 constexpr int kMaxCombineSplits = 256;
 constexpr int kCombineChunk = 16;
@@ -480,21 +481,24 @@ constexpr int kCombineChunk = 16;
 template <bool BF16>
 __global__ __launch_bounds__(kCombineThreads) void lse_combine_kernel(const CombineArgs a) {
   const float NEG_INF = -__builtin_inff();
+  const int D4 = a.D / 4;
   const size_t e = (size_t)blockIdx.x * kCombineThreads + threadIdx.x;
-  if (e >= (size_t)a.rows * a.D) return;
-  const int row = (int)(e / a.D), d = (int)(e % a.D);
+  if (e >= (size_t)a.rows * D4) return;
+  const int row = (int)(e / D4), d = 4 * (int)(e % D4);
   const int S = a.splits;
   const float* pl = a.part_lse + (size_t)row * S;
   const float* ps = a.part_l ? a.part_l + (size_t)row * S : nullptr;
-  const float* po = a.part_o + (size_t)row * S * a.D + d;
-  float M = NEG_INF, wsum = 0.f, acc = 0.f;
+  const float4* po = (const float4*)(a.part_o + (size_t)row * S * a.D + d);
+  float M = NEG_INF, wsum = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int j0 = 0; j0 < S; j0 += kCombineChunk) {
-    float x[kCombineChunk], v[kCombineChunk], l[kCombineChunk];
+    float x[kCombineChunk], l[kCombineChunk];
+    float4 v[kCombineChunk];
 #pragma unroll
     for (int u = 0; u < kCombineChunk; ++u) {
       const bool in = j0 + u < S;
       x[u] = in ? pl[j0 + u] : NEG_INF;
-      v[u] = in ? po[(size_t)(j0 + u) * a.D] : 0.f;
+      v[u] = in ? po[(size_t)(j0 + u) * D4] : make_float4(0.f, 0.f, 0.f, 0.f);
       l[u] = ps && in ? ps[j0 + u] : 1.f;
     }
     float Mc = M;
@@ -503,12 +507,18 @@ __global__ __launch_bounds__(kCombineThreads) void lse_combine_kernel(const Comb
     const float mu = Mc == NEG_INF ? 0.f : Mc;
     const float f = fast_exp2(M - mu);  // rescales the running sums (0 while M is -inf)
     wsum *= f;
-    acc *= f;
+    acc.x *= f;
+    acc.y *= f;
+    acc.z *= f;
+    acc.w *= f;
 #pragma unroll
     for (int u = 0; u < kCombineChunk; ++u) {
       const float w = fast_exp2(x[u] - mu);
       wsum = fmaf(w, l[u], wsum);
-      acc = fmaf(w, v[u], acc);
+      acc.x = fmaf(w, v[u].x, acc.x);
+      acc.y = fmaf(w, v[u].y, acc.y);
+      acc.z = fmaf(w, v[u].z, acc.z);
+      acc.w = fmaf(w, v[u].w, acc.w);
     }
     M = Mc;
   }
@@ -517,12 +527,20 @@ __global__ __launch_bounds__(kCombineThreads) void lse_combine_kernel(const Comb
     const float Mc = fmaxf(M, x);
     const float f = fast_exp2(M - Mc);  // 0 while M is -inf
     wsum = wsum * f + fast_exp2(x - Mc);
-    acc *= f;
+    acc.x *= f;
+    acc.y *= f;
+    acc.z *= f;
+    acc.w *= f;
     M = Mc;
   }
-  const float val = wsum > 0.f ? acc / wsum : 0.f;
-  if constexpr (BF16) ((uint16_t*)a.out)[e] = f32_to_bf16(val);
-  else ((float*)a.out)[e] = val;
+  const float o0 = wsum > 0.f ? acc.x / wsum : 0.f, o1 = wsum > 0.f ? acc.y / wsum : 0.f;
+  const float o2 = wsum > 0.f ? acc.z / wsum : 0.f, o3 = wsum > 0.f ? acc.w / wsum : 0.f;
+  const size_t o = (size_t)row * a.D + d;
+  if constexpr (BF16) {
+    *(uint2*)((uint16_t*)a.out + o) = make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
+  } else {
+    *(float4*)((float*)a.out + o) = make_float4(o0, o1, o2, o3);
+  }
   if (d == 0 && a.lse) a.lse[row] = wsum > 0.f ? (M + __log2f(wsum)) * kLn2 : NEG_INF;
 }
 
@@ -556,7 +574,8 @@ int gqa_blocks_per_cu(bool bf16, int D, int G, bool paged, int page_size) {
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   if (a.splits > kMaxCombineSplits) return hipErrorInvalidValue;
-  const size_t total = (size_t)a.rows * a.D;
+  if (a.D % 4 != 0) return hipErrorInvalidValue;
+  const size_t total = (size_t)a.rows * (a.D / 4);
   const unsigned blocks = (unsigned)((total + kCombineThreads - 1) / kCombineThreads);
   if (a.bf16) lse_combine_kernel<true><<<blocks, kCombineThreads, 0, s>>>(a);
   else lse_combine_kernel<false><<<blocks, kCombineThreads, 0, s>>>(a);

@@ -11,7 +11,9 @@
  *     (thread-local message); nothing is printed and nothing is launched;
  *   - launches its kernels asynchronously on `stream` and never synchronises;
  *     outputs are valid once the stream reaches that point;
- *   - fully overwrites every output (never accumulates into it).
+ *   - fully overwrites every output (never accumulates into it);
+ *   - moves data in 16-byte vectors: q, caches, outputs and summaries must
+ *     be 16-byte aligned (DATTN_EINVAL otherwise; allocator pointers are).
  * Contents of device-resident index arrays (seq_lens, page_table, topk_idx)
  * are a caller contract: they are not read on the host, so calls can be
  * captured into graphs.

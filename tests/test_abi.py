@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def _gqa(**kw):
-    args = dict(q=1, k=1, v=1, seq_lens=1, page_table=None, window=0, n_sink=0, out=1, lse=None,
+    args = dict(q=256, k=256, v=256, seq_lens=256, page_table=None, window=0, n_sink=0, out=256, lse=None,
                 B=2, Hq=8, Hkv=2, D=128, page_size=16, max_pages=4, dtype=1, scale=0.0,
                 num_splits=0, ws=None, ws_bytes=0)
     args.update(kw)
@@ -53,12 +53,14 @@ def _gqa(**kw):
     (dict(Hq=48, Hkv=2), -2),         # group 24 not built
     (dict(D=96), -2),
     (dict(dtype=7), -2),
-    (dict(page_table=1, page_size=24), -2),  # paged needs power-of-two pages
-    (dict(page_table=1, max_pages=0), -1),
+    (dict(page_table=256, page_size=24), -2),  # paged needs power-of-two pages
+    (dict(page_table=256, max_pages=0), -1),
     (dict(n_sink=-1), -1),
     (dict(num_splits=-3), -1),
     (dict(scale=float("nan")), -1),
-    (dict(page_table=1, num_splits=8), -3),  # 8 splits need a workspace
+    (dict(page_table=256, num_splits=8), -3),  # 8 splits need a workspace
+    (dict(k=264), -1),                          # not 16-byte aligned
+    (dict(out=258), -1),
 ])
 def test_gqa_validation(kw, code):
     rc = _gqa(**kw)
@@ -83,22 +85,26 @@ def test_mla_and_sparse_validation():
     L = api.lib()
     P = ctypes.c_void_p
     # bad latent width
-    rc = L.decode_attn_mla(P(1), P(1), P(1), None, P(1), None, 2, 128, 256, 64, 100, 100, 1, 1,
+    rc = L.decode_attn_mla(P(256), P(256), P(256), None, P(256), None, 2, 128, 256, 64, 100, 100, 1, 1,
                            0.0, 0, None, 0, None)
     assert rc == -2
     # fp32 MLA is not built
-    rc = L.decode_attn_mla(P(1), P(1), P(1), None, P(1), None, 2, 128, 512, 64, 100, 100, 1, 0,
+    rc = L.decode_attn_mla(P(256), P(256), P(256), None, P(256), None, 2, 128, 512, 64, 100, 100, 1, 0,
                            0.0, 0, None, 0, None)
     assert rc == -2
+    # the latent cache must be 16-byte aligned
+    rc = L.decode_attn_mla(P(256), P(258), P(256), None, P(256), None, 2, 128, 512, 64, 100, 100, 1, 1,
+                           0.0, 0, None, 0, None)
+    assert rc == -1
     # heads not a multiple of 64
-    rc = L.decode_attn_mla(P(1), P(1), P(1), None, P(1), None, 2, 96, 512, 64, 100, 100, 1, 1,
+    rc = L.decode_attn_mla(P(256), P(256), P(256), None, P(256), None, 2, 96, 512, 64, 100, 100, 1, 1,
                            0.0, 0, None, 0, None)
     assert rc == -2
     # sparse: k must be >= 1 and idx non-null
-    rc = L.sparse_mla_attn(P(1), P(1), None, 16, P(1), None, 2, 128, 512, 64, 100, 1, 0.0, 0,
+    rc = L.sparse_mla_attn(P(256), P(256), None, 16, P(256), None, 2, 128, 512, 64, 100, 1, 0.0, 0,
                            None, 0, None)
     assert rc == -1
-    rc = L.sparse_mla_attn(P(1), P(1), P(1), 0, P(1), None, 2, 128, 512, 64, 100, 1, 0.0, 0,
+    rc = L.sparse_mla_attn(P(256), P(256), P(256), 0, P(256), None, 2, 128, 512, 64, 100, 1, 0.0, 0,
                            None, 0, None)
     assert rc == -1
 
@@ -108,7 +114,7 @@ def test_dsa_validation():
     P = ctypes.c_void_p
     args = lambda **kw: dict(dict(k=2048, Hi=64, Di=128, dt=1), **kw)
     def call(a, scores=None, ws=None, ws_bytes=0):
-        return L.dsa_indexer_topk(P(1), P(1), P(1), P(1), a["k"], P(1), scores, 8, a["Hi"],
+        return L.dsa_indexer_topk(P(256), P(256), P(256), P(256), a["k"], P(256), scores, 8, a["Hi"],
                                   a["Di"], 65536, a["dt"], ws, ws_bytes, None)
     assert call(args(k=0)) == -1
     assert call(args(k=20000)) == -1
@@ -116,17 +122,19 @@ def test_dsa_validation():
     assert call(args(Hi=48)) == -2
     assert call(args(dt=0)) == -2
     assert call(args()) == -3                     # no scores buffer, no workspace
-    assert call(args(), scores=P(1)) == -3        # the selection always needs one
+    assert L.dsa_indexer_topk(P(264), P(256), P(256), P(256), 2048, P(256), None, 8, 64, 128, 65536, 1,
+                              None, 0, None) == -1   # q_i not 16-byte aligned
+    assert call(args(), scores=P(256)) == -3        # the selection always needs one
     # top-k workspace per row: 4 x 256 + 1 words per 2048-token chunk + 8, rounded to 64 words
     topk_ws = 8 * (((32 * 1025 + 8) + 63) // 64 * 64) * 4
     assert L.dsa_topk_workspace(8, 65536, 2048) == topk_ws
     assert L.dsa_indexer_topk_workspace(8, 65536, 2048) == 8 * 65536 * 4 + topk_ws
-    assert L.dsa_topk(P(1), P(1), 0, P(1), 8, 100, None, 0, None) == -1
-    assert L.dsa_topk(None, P(1), 4, P(1), 8, 100, None, 0, None) == -1
-    assert L.dsa_topk(P(1), P(1), 4, P(1), 70000, 100, None, 0, None) == -1   # B > 65535
-    assert L.dsa_topk(P(1), P(1), 4, P(1), 8, (1 << 30) + 1, None, 0, None) == -1
-    assert L.dsa_topk(P(1), P(1), 4, P(1), 8, 100, None, 0, None) == -3     # no workspace
-    assert L.dsa_topk(P(1), P(1), 4, P(1), 8, 100, P(256), 16, None) == -3  # too small
+    assert L.dsa_topk(P(256), P(256), 0, P(256), 8, 100, None, 0, None) == -1
+    assert L.dsa_topk(None, P(256), 4, P(256), 8, 100, None, 0, None) == -1
+    assert L.dsa_topk(P(256), P(256), 4, P(256), 70000, 100, None, 0, None) == -1   # B > 65535
+    assert L.dsa_topk(P(256), P(256), 4, P(256), 8, (1 << 30) + 1, None, 0, None) == -1
+    assert L.dsa_topk(P(256), P(256), 4, P(256), 8, 100, None, 0, None) == -3     # no workspace
+    assert L.dsa_topk(P(256), P(256), 4, P(256), 8, 100, P(256), 16, None) == -3  # too small
 
 
 def test_profile_calls_without_gpu():
@@ -195,6 +203,7 @@ def _quest(**kw):
     (dict(budget=0), -1),
     (dict(budget=16385), -1),
     (dict(page_size=8), -2),                 # a 16-token block would straddle pages
+    (dict(kmm=260), -1),                     # summaries not 16-byte aligned
     (dict(D=96), -2),
     (dict(Hq=48, Hkv=2), -2),
     (dict(B=4096, Hq=32, Hkv=8), -1),        # B * Hq rows above the select's grid
