@@ -26,9 +26,14 @@
 //     bf16 products are exact in fp32) summed over the row's lanes with DPP;
 //   * the softmax is the online one ("All the attentions", section 1: a
 //     running maximum and running sum, earlier partials rescaled), kept per
-//     lane; the reference maximum only moves when the new maximum exceeds it
-//     by more than 2^8, which bounds every exponential by 2^8 and makes
-//     rescaling rare without changing the result;
+//     token row of lanes; the reference maximum only moves when the new
+//     maximum exceeds it by more than 2^8, which bounds every exponential by
+//     2^8 and makes rescaling rare without changing the result;
+//   * with 16 lanes per row and 16 (token, head) scores per lane (D = 128
+//     bf16 or D = 64 fp32, four heads per KV head) the sum over the row is a
+//     transposing one that leaves each lane one score; the lane takes that
+//     score's exponential and the probabilities are broadcast back with DPP
+//     row broadcasts (one exponential per lane instead of sixteen);
 //   * P.V: for bf16 the probabilities of two tokens are rounded to bf16 and
 //     paired with the two tokens' values in one v_dot2_f32_bf16 per output
 //     (fp32 accumulation); for fp32 inputs it is plain fp32 FMA.
@@ -84,6 +89,40 @@ __device__ __forceinline__ float row_sum(float x) {
     x = group_sum<16>(x);
     return x + __shfl_xor(x, 16);
   }
+}
+
+// Broadcast of lane N of each 16-lane row to the whole row (DPP row_newbcast).
+template <int N>
+__device__ __forceinline__ float row_bcast(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + N, 0xF, 0xF, false));
+}
+template <int N>
+__device__ __forceinline__ uint32_t row_bcast_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x150 + N, 0xF, 0xF, false);
+}
+
+// Transposing sum over the 16 lanes of a row: lane c holds 16 partial values
+// v[0..16) and ends with the row's total of v[c].  Each step pairs the lane
+// with a partner that differs in one more index bit (3, 2, 1, 0 through
+// row_mirror, row_half_mirror and the two quad swaps), keeps the half of its
+// values that bit selects and adds the partner's copy of that half: 15 adds
+// instead of the 64 of a full sum of every value in every lane.
+template <int CTRL, int N>
+__device__ __forceinline__ void xpose_step(float (&v)[16], bool upper) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const float keep = upper ? v[i + N] : v[i];
+    const float send = upper ? v[i] : v[i + N];
+    v[i] = keep + dpp_f32<CTRL>(send);
+  }
+}
+
+__device__ __forceinline__ float xpose_sum16(float (&v)[16], int c) {
+  xpose_step<0x140, 8>(v, c & 8);  // partner 15 - c
+  xpose_step<0x141, 4>(v, c & 4);  // partner c ^ 7 within the 8-lane half
+  xpose_step<0x4E, 2>(v, c & 2);   // partner c ^ 2
+  xpose_step<0xB1, 1>(v, c & 1);   // partner c ^ 1
+  return v[0];
 }
 
 // PAGED_FAST: paged with page_size % 16 == 0, or contiguous (one lookup per
@@ -154,6 +193,13 @@ __global__ __launch_bounds__(kThreads) void gqa_split_kernel(const GqaArgs a) {
 #pragma unroll
     for (int e = 0; e < VEC; ++e) o[h][e] = 0.f;
   }
+  // With 16 lanes per token row and 16 (token row, head) scores per lane the
+  // softmax runs transposed: after the transposing sum, lane c of the row
+  // owns the score of head c / 4 and token row c % 4; it takes one
+  // exponential (not 16 copies of each), and the probabilities are
+  // broadcast back for P.V.  lc is the lane's share of the denominator.
+  constexpr bool kXpose = LPR == 16 && TPL * G == 16;
+  float lc = 0.f;
 
   const size_t head_stride = (size_t)a.page_size * D;
   const size_t page_stride = (size_t)a.Hkv * head_stride;
@@ -216,6 +262,103 @@ __global__ __launch_bounds__(kThreads) void gqa_split_kernel(const GqaArgs a) {
     }
   };
 
+  // The transposed path of compute (kXpose): tokens t0 + u RPI + r, u < 4.
+  auto compute_xpose = [&](int t0, int lo, int hi, uint32_t heads, const KvRegs<TPL>& R) {
+    if constexpr (kXpose) {
+      float v[16];  // v[4 h + u]: this lane's part of q_h . k_u
+#pragma unroll
+      for (int u = 0; u < TPL; ++u) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          float acc;
+          if constexpr (BF16) {
+            acc = dot2_bf16(R.k[u].x, qv[h].x, 0.f);
+            acc = dot2_bf16(R.k[u].y, qv[h].y, acc);
+            acc = dot2_bf16(R.k[u].z, qv[h].z, acc);
+            acc = dot2_bf16(R.k[u].w, qv[h].w, acc);
+          } else {
+            acc = __uint_as_float(R.k[u].x) * __uint_as_float(qv[h].x);
+            acc = fmaf(__uint_as_float(R.k[u].y), __uint_as_float(qv[h].y), acc);
+            acc = fmaf(__uint_as_float(R.k[u].z), __uint_as_float(qv[h].z), acc);
+            acc = fmaf(__uint_as_float(R.k[u].w), __uint_as_float(qv[h].w), acc);
+          }
+          v[4 * h + u] = acc;
+        }
+      }
+      const int hc = c >> 2, uc = c & 3;
+      const int t = t0 + uc * RPI + r;
+      const bool valid = t >= lo && t < hi && ((heads >> hc) & 1u);
+      // every lane of the row takes part in the cross-lane sum (a lane left
+      // out would hand its partners zeros): sum first, then mask
+      const float dot = xpose_sum16(v, c);
+      const float sc = valid ? dot * a.scale_log2 : NEG_INF;
+      // each head's maximum over the row's four tokens, then every head's
+      // in every lane (the reference maxima are kept per row, in every lane)
+      float mx = fmaxf(sc, dpp_f32<0xB1>(sc));
+      mx = fmaxf(mx, dpp_f32<0x4E>(mx));
+      float mxh[G];
+      mxh[0] = row_bcast<0>(mx);
+      mxh[1] = row_bcast<4>(mx);
+      mxh[2] = row_bcast<8>(mx);
+      mxh[3] = row_bcast<12>(mx);
+      float mine = m[0];
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        if (mxh[h] > m[h] + kTau) {
+          const float alpha = fast_exp2(m[h] - mxh[h]);  // 0 when m was -inf
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) o[h][e] *= alpha;
+          if (hc == h) lc *= alpha;
+          m[h] = mxh[h];
+        }
+        if (hc == h) mine = m[h];
+      }
+      const float p = fast_exp2(sc - (mine == NEG_INF ? 0.f : mine));
+      lc += p;
+      // (p_u, p_u+1) of a head in the lanes of even u, then to every lane
+      const uint32_t pk = pack_bf16x2(p, dpp_f32<0xB1>(p));
+      uint32_t pp[2][G];
+      pp[0][0] = row_bcast_u32<0>(pk);
+      pp[1][0] = row_bcast_u32<2>(pk);
+      pp[0][1] = row_bcast_u32<4>(pk);
+      pp[1][1] = row_bcast_u32<6>(pk);
+      pp[0][2] = row_bcast_u32<8>(pk);
+      pp[1][2] = row_bcast_u32<10>(pk);
+      pp[0][3] = row_bcast_u32<12>(pk);
+      pp[1][3] = row_bcast_u32<14>(pk);
+      if constexpr (BF16) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const uint32_t a0 = u4(R.v[2 * j], w), a1 = u4(R.v[2 * j + 1], w);
+            const uint32_t plo = pair_lo(a0, a1), phi = pair_hi(a0, a1);
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+              o[h][2 * w] = dot2_bf16(pp[j][h], plo, o[h][2 * w]);
+              o[h][2 * w + 1] = dot2_bf16(pp[j][h], phi, o[h][2 * w + 1]);
+            }
+          }
+        }
+      } else {
+        // fp32 values take fp32 probabilities: broadcast them unrounded
+        const float pf[TPL][G] = {
+            {row_bcast<0>(p), row_bcast<4>(p), row_bcast<8>(p), row_bcast<12>(p)},
+            {row_bcast<1>(p), row_bcast<5>(p), row_bcast<9>(p), row_bcast<13>(p)},
+            {row_bcast<2>(p), row_bcast<6>(p), row_bcast<10>(p), row_bcast<14>(p)},
+            {row_bcast<3>(p), row_bcast<7>(p), row_bcast<11>(p), row_bcast<15>(p)}};
+        (void)pp;
+#pragma unroll
+        for (int u = 0; u < TPL; ++u) {
+#pragma unroll
+          for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) o[h][e] = fmaf(pf[u][h], __uint_as_float(u4(R.v[u], e)), o[h][e]);
+        }
+      }
+    }
+  };
+
   // Scores, online softmax and P.V of block blk held in R; a block at or
   // past blk_end is empty (every row masked).
   auto compute = [&](int blk, const KvRegs<TPL>& R) {
@@ -226,6 +369,10 @@ __global__ __launch_bounds__(kThreads) void gqa_split_kernel(const GqaArgs a) {
     // heads that attend this block (a union list names them; else all)
     uint32_t heads = 0xffu;
     if constexpr (SET == kSetUnion) heads = blk < n_sb ? (uint32_t)list[blk] >> 24 : 0xffu;
+    if constexpr (kXpose) {
+      compute_xpose(t0, lo, hi, heads, R);
+      return;
+    }
     // scores (log2 units) of the lane's TPL tokens
     float s[TPL][G];
 #pragma unroll
@@ -314,6 +461,15 @@ __global__ __launch_bounds__(kThreads) void gqa_split_kernel(const GqaArgs a) {
     issue(blk, ph, R);
     if (paged_lookup && blk + kWaves < blk_end) ph = page_of(blk + kWaves);
     compute(blk, R);
+  }
+
+  if constexpr (kXpose) {  // each head's denominator, in every lane of the row
+    float ls = lc + dpp_f32<0xB1>(lc);
+    ls += dpp_f32<0x4E>(ls);
+    l[0] = row_bcast<0>(ls);
+    l[1] = row_bcast<4>(ls);
+    l[2] = row_bcast<8>(ls);
+    l[3] = row_bcast<12>(ls);
   }
 
   // merge the token rows of the wave (lanes c, c + LPR, ...)
