@@ -66,6 +66,7 @@ def test_zero_sink_tiny_fp32(splits):
 @pytest.mark.parametrize("Hq,Hkv,D,dtype,paged", [
     (32, 8, 128, torch.bfloat16, True),
     (8, 1, 64, torch.float32, False),
+    (8, 2, 64, torch.float32, True),
 ])
 @pytest.mark.parametrize("splits", [0, 1, 3])
 def test_learned_sinks_ragged(Hq, Hkv, D, dtype, paged, splits):
@@ -99,6 +100,8 @@ def test_sink_on_empty_sequences():
     (16, 2, 64, torch.float32, True),     # G = 8
     (4, 2, 128, torch.float32, False),
     (6, 3, 64, torch.bfloat16, True),     # G = 2, odd head counts
+    (8, 2, 64, torch.float32, True),      # G = 4 at 16 lanes per row in fp32: the transposed softmax
+    (16, 4, 128, torch.bfloat16, False),  # G = 4, contiguous
 ])
 @pytest.mark.parametrize("splits", [0, 1, 3])
 def test_gqa_ragged(Hq, Hkv, D, dtype, paged, splits):
