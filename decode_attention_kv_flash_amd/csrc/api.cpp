@@ -529,10 +529,12 @@ int dsa_indexer_topk(const void* q_i, const float* w, const void* k_i_cache, con
   float* scores = scores_out ? scores_out : (float*)workspace;
   uint32_t* topk_ws = (uint32_t*)((char*)workspace + align256((size_t)B * S_max * sizeof(float)));
   hipStream_t s = (hipStream_t)stream;
-  dattn::IndexerArgs ia{q_i, w, k_i_cache, seq_lens, scores, B, Hi, S_max, 0, dtype == DATTN_FP8_E4M3};
+  dattn::IndexerArgs ia{q_i,   w, k_i_cache, seq_lens, scores, B, Hi, S_max, 0, dtype == DATTN_FP8_E4M3,
+                        topk_ws, dattn::topk_row_words_of(S_max)};
   rc = launch("indexer_scores", s, [&] { return dattn::launch_indexer(ia, s); });
   if (rc) return rc;
   dattn::TopkArgs t{scores, seq_lens, topk_idx, B, S_max, k, topk_ws, 0, 0};
+  t.hist0_done = ia.hist0 != nullptr;  // the indexer wrote the first level
   rc = launch("topk_select", s, [&] { return dattn::launch_topk(t, s); });
   return rc ? rc : ok();
 }

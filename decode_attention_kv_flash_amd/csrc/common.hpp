@@ -77,6 +77,29 @@ __device__ __forceinline__ uint4 load_stream(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Order-preserving unsigned key of an fp32 score (-0.0 folded onto +0.0):
+// a > b as floats exactly when key(a) > key(b).
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// LDS histogram add of bin d for the lanes with act set; a wave whose active
+// lanes share one bin adds once (scores often crowd into one top byte).
+__device__ __forceinline__ void hist_add(uint32_t* h, bool act, uint32_t d) {
+  const uint64_t am = __ballot(act);
+  if (am == 0) return;
+  const int first = __ffsll((long long)am) - 1;
+  const uint32_t d0 = __shfl(d, first);
+  const uint64_t same = __ballot(act && d == d0);
+  if (same == am) {
+    if ((int)(threadIdx.x & 63) == first) atomicAdd(&h[d0], (uint32_t)__popcll(am));
+  } else if (act) {
+    atomicAdd(&h[d], 1u);
+  }
+}
+
 // exp2 of a value that may be -inf (gives 0).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

@@ -21,7 +21,9 @@
 // Rows keep their 16-byte chunks permuted by a row key (slot_key), so the
 // rows a read instruction serves per pass hit different bank groups.  The
 // epilogue applies ReLU, the head weights, sums a lane's 32 heads in
-// registers and the other 32 heads from lane l ^ 32.
+// registers and the other 32 heads from lane l ^ 32.  When a workgroup's
+// token range is one chunk of the top-k select, it also counts its scores'
+// top key bytes into the select's first-level histogram (one launch fewer).
 #include <type_traits>
 
 #include "common.hpp"
@@ -78,6 +80,11 @@ template <int NMT, bool FP8>
 __global__ __launch_bounds__(kThreads) void indexer_kernel(const IndexerArgs a) {
   using S = IdxShape<FP8>;
   __shared__ __attribute__((aligned(16))) char kbuf[kWaves][kBufs][S::kStepBytes];
+  __shared__ uint32_t hist[256];  // top key byte of this range's valid scores (a.hist0 only)
+  if (a.hist0) {
+    hist[threadIdx.x] = 0u;
+    barrier_in_flight<63>();  // LDS only: nothing else is waited for
+  }
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int half = lane >> 5;
@@ -186,9 +193,14 @@ __global__ __launch_bounds__(kThreads) void indexer_kernel(const IndexerArgs a) 
     }
     part += __shfl_xor(part, 32);
     if (half == 0 && t < a.S_max) out[t] = valid ? part : -__builtin_inff();
+    if (a.hist0 && half == 0 && valid) atomicAdd(&hist[order_key(part) >> 24], 1u);
     }
     buf = buf == kBufs - 1 ? 0 : buf + 1;
     nbuf = nbuf == kBufs - 1 ? 0 : nbuf + 1;
+  }
+  if (a.hist0) {
+    barrier_in_flight<63>();  // every wave's counts are in LDS
+    a.hist0[(size_t)b * a.hist_row_words + (size_t)blockIdx.x * 256 + threadIdx.x] = hist[threadIdx.x];
   }
 }
 
@@ -206,7 +218,7 @@ int resident_per_cu() {
 }
 
 template <int NMT, bool FP8>
-hipError_t launch_nmt(IndexerArgs a, hipStream_t s) {
+hipError_t launch_nmt(IndexerArgs& a, hipStream_t s) {
   // one round of resident workgroups: the token ranges (whole wave steps)
   // are sized so that B x ranges just fills the CUs, with no partial second round
   const int64_t slots = (int64_t)device_cu_count() * resident_per_cu<NMT, FP8>();
@@ -216,13 +228,15 @@ hipError_t launch_nmt(IndexerArgs a, hipStream_t s) {
   per = (per + kStep - 1) / kStep * kStep;
   if (per < kStep) per = kStep;
   a.tok_per_wg = (int32_t)per;
+  // the select's first level comes along only when the ranges are its chunks
+  if (per != kTopkChunk || a.S_max <= kTopkChunk) a.hist0 = nullptr;
   dim3 grid((unsigned)((a.S_max + per - 1) / per), a.B), block(kThreads);
   indexer_kernel<NMT, FP8><<<grid, block, 0, s>>>(a);
   return hipGetLastError();
 }
 
 template <bool FP8>
-hipError_t launch_type(const IndexerArgs& a, hipStream_t s) {
+hipError_t launch_type(IndexerArgs& a, hipStream_t s) {
   switch (a.Hi) {
     case 32: return launch_nmt<1, FP8>(a, s);
     case 64: return launch_nmt<2, FP8>(a, s);
@@ -234,7 +248,7 @@ hipError_t launch_type(const IndexerArgs& a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s) {
+hipError_t launch_indexer(IndexerArgs& a, hipStream_t s) {
   return a.fp8 ? launch_type<true>(a, s) : launch_type<false>(a, s);
 }
 

@@ -130,9 +130,18 @@ struct IndexerArgs {
   int32_t B, Hi, S_max;
   int32_t tok_per_wg;      // set by the launcher
   int32_t fp8;             // 1: q and k are fp8 e4m3 (OCP e4m3fn)
+  // nullptr, or the top-k workspace: when each workgroup's token range is
+  // one top-k chunk, the indexer also writes each chunk's histogram of the
+  // scores' top key byte (the select's first level) at hist0 + b *
+  // hist_row_words + chunk * 256.  The launcher clears hist0 when the ranges
+  // do not match the chunks.
+  uint32_t* hist0;
+  int64_t hist_row_words;
 };
 
-hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s);
+hipError_t launch_indexer(IndexerArgs& a, hipStream_t s);
+
+constexpr int kTopkChunk = 2048;  // tokens per top-k workgroup
 
 struct TopkArgs {
   const float* scores;     // [B, S_max]
@@ -142,9 +151,11 @@ struct TopkArgs {
   uint32_t* ws;            // topk_workspace_bytes(B, S_max), 256-byte aligned
   int32_t n_chunks;        // set by the launcher
   int64_t row_words;       // set by the launcher
+  int32_t hist0_done = 0;  // 1: the first level's chunk histograms are already in ws
 };
 
 size_t topk_workspace_bytes(int B, int S_max);
+int64_t topk_row_words_of(int S_max);  // 32-bit words of one row's workspace
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 
 // Cache append: one new row per (sequence, head) into one or two caches laid

@@ -27,7 +27,10 @@
 //             so indices come out ascending and ties go to the lower index.
 // Workgroup 0 of a row records each decision for the next launch.  Rows with
 // seq_len <= k are written directly by the first launch.  Nothing in the
-// workspace has to be cleared beforehand.  When every row fits one chunk
+// workspace has to be cleared beforehand.  The first level's histograms may
+// come from the producer of the scores instead (the indexer, when its
+// workgroups cover exactly these chunks); launch 0 is then skipped.  When
+// every row fits one chunk
 // (S_max <= 2048, e.g. a selection over 16-token pages), one workgroup owns a
 // row and runs the four levels and the write in a single launch, with the
 // histograms in LDS.
@@ -41,6 +44,7 @@ constexpr int kTT = 256;             // threads per workgroup
 constexpr int kNW = kTT / 64;        // waves per workgroup
 constexpr int kKPT = 8;              // keys per thread
 constexpr int kChunk = kTT * kKPT;   // tokens per workgroup
+static_assert(kChunk == kTopkChunk, "chunk size shared with the indexer");
 constexpr int kBins = 256;           // one byte of the key per launch
 constexpr int kColBatch = 16;        // chunk histograms loaded per batch
 
@@ -67,12 +71,6 @@ __device__ __forceinline__ RowWs row_ws(const TopkArgs& a, int b) {
 // seq_lens outside [0, S_max] are clamped into it
 __device__ __forceinline__ int row_len(const TopkArgs& a, int b) {
   return min(max(a.seq_lens[b], 0), a.S_max);
-}
-
-__device__ __forceinline__ uint32_t order_key(float f) {
-  uint32_t u = __float_as_uint(f);
-  if (u == 0x80000000u) u = 0u;  // -0.0 == +0.0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
 // This workgroup's keys, loaded without waiting for the row length (tokens
@@ -127,20 +125,6 @@ __device__ __forceinline__ void row_column_sums(const TopkArgs& a, const uint32_
     column_sums(h, a.n_chunks, nc, c, tot, pre);
   else
     column_sums(h, nc, nc, c, tot, pre);
-}
-
-// LDS histogram add; a wave whose active keys share one bin adds once.
-__device__ __forceinline__ void hist_add(uint32_t* h, bool act, uint32_t d) {
-  const uint64_t am = __ballot(act);
-  if (am == 0) return;
-  const int first = __ffsll((long long)am) - 1;
-  const uint32_t d0 = __shfl(d, first);
-  const uint64_t same = __ballot(act && d == d0);
-  if (same == am) {
-    if ((int)(threadIdx.x & 63) == first) atomicAdd(&h[d0], (uint32_t)__popcll(am));
-  } else if (act) {
-    atomicAdd(&h[d], 1u);
-  }
 }
 
 __device__ __forceinline__ uint32_t block_sum(uint32_t x, uint32_t* red) {
@@ -200,7 +184,7 @@ __global__ __launch_bounds__(kTT) void topk_digit_kernel(const TopkArgs a) {
     }
     row_column_sums(a, w.h + (size_t)(LEVEL - 1) * a.n_chunks * kBins, L, 0, tot, pre);
   }
-  if (LEVEL == 0 && L <= K) {
+  if ((LEVEL == 0 || (LEVEL == 1 && a.hist0_done)) && L <= K) {  // the first launch writes short rows
     int32_t* out = a.idx + (size_t)b * K;
     for (int j = c * kTT + tid; j < K; j += a.n_chunks * kTT) out[j] = j < L ? j : -1;
     return;
@@ -353,6 +337,10 @@ __global__ __launch_bounds__(kTT) void topk_single_kernel(const TopkArgs a) {
 
 }  // namespace
 
+int64_t topk_row_words_of(int S_max) {
+  return (int64_t)topk_row_words((S_max + kChunk - 1) / kChunk);
+}
+
 size_t topk_workspace_bytes(int B, int S_max) {
   const int nc = (S_max + kChunk - 1) / kChunk;
   return ((size_t)B * topk_row_words(nc) * 4 + 255) & ~(size_t)255;
@@ -367,7 +355,7 @@ hipError_t launch_topk(const TopkArgs& a0, hipStream_t s) {
     topk_single_kernel<<<grid, kTT, 0, s>>>(a);
     return hipGetLastError();
   }
-  topk_digit_kernel<0><<<grid, kTT, 0, s>>>(a);
+  if (!a.hist0_done) topk_digit_kernel<0><<<grid, kTT, 0, s>>>(a);
   topk_digit_kernel<1><<<grid, kTT, 0, s>>>(a);
   topk_digit_kernel<2><<<grid, kTT, 0, s>>>(a);
   topk_digit_kernel<3><<<grid, kTT, 0, s>>>(a);

@@ -115,6 +115,28 @@ def test_indexer_hand_worked_example():
         assert idx.cpu()[0].tolist() == want
 
 
+@pytest.mark.parametrize("fp8", [False, True])
+def test_indexer_hands_the_select_its_first_level(fp8):
+    """B x S_max = 4 x 131072 on 256 CUs: every indexer workgroup covers one
+    2048-token chunk of the select and counts its scores' top key bytes, so
+    the select skips its first launch.  Ragged rows, one shorter than k and
+    an empty one; the selection must equal the oracle's select over the same
+    scores, and the scores the oracle indexer on the first 4096 tokens."""
+    lens = [131072, 1000, 70001, 0]
+    x = wl.make_dsa(B=4, seq_lens=lens, Hi=32, topk=2048, H=64, seed=63, name="dsa_first_level")
+    say(f"[dsa] indexer + top-k, first level from the indexer, lens={lens} fp8={fp8}")
+    q, k = (x.q_i.to(torch.float8_e4m3fn), x.k_i.to(torch.float8_e4m3fn)) if fp8 else (x.q_i, x.k_i)
+    idx, sc = api.dsa_indexer_topk(dev(q), dev(x.w), dev(k), dev(x.seq_lens), 2048, return_scores=True)
+    torch.cuda.synchronize()
+    sc, idx = sc.cpu(), idx.cpu()
+    assert torch.equal(idx, oracle.topk(sc, x.seq_lens, 2048))
+    head = torch.clamp(x.seq_lens, max=4096)
+    want = oracle.indexer(x.q_i, x.w, x.k_i[:, :4096].contiguous(), head)
+    for b in range(4):
+        n = int(head[b])
+        assert torch.equal(sc[b, :n].double(), want[b, :n].double())
+
+
 @pytest.mark.parametrize("n_distinct", [None, 3, 50])
 @pytest.mark.parametrize("k", [1, 100, 2048])
 def test_topk_alone(n_distinct, k):
