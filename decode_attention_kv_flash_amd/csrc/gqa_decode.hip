@@ -199,6 +199,7 @@ __global__ __launch_bounds__(kThreads) void gqa_split_kernel(const GqaArgs a) {
   // exponential (not 16 copies of each), and the probabilities are
   // broadcast back for P.V.  lc is the lane's share of the denominator.
   constexpr bool kXpose = LPR == 16 && TPL * G == 16;
+  static_assert(!kXpose || (G == 4 && TPL == 4), "the transposed path is written for four heads and four rows");
   float lc = 0.f;
 
   const size_t head_stride = (size_t)a.page_size * D;
