@@ -29,11 +29,12 @@
 //     token row of lanes; the reference maximum only moves when the new
 //     maximum exceeds it by more than 2^8, which bounds every exponential by
 //     2^8 and makes rescaling rare without changing the result;
-//   * with 16 lanes per row and 16 (token, head) scores per lane (D = 128
-//     bf16 or D = 64 fp32, four heads per KV head) the sum over the row is a
-//     transposing one that leaves each lane one score; the lane takes that
-//     score's exponential and the probabilities are broadcast back with DPP
-//     row broadcasts (one exponential per lane instead of sixteen);
+//   * with 16 lanes per row (D = 128 bf16 or D = 64 fp32) and four or eight
+//     heads per KV head, the sum over the row is a transposing one that
+//     leaves each lane one score per block of four heads; the lane takes
+//     that score's exponential and the probabilities are broadcast back with
+//     DPP row broadcasts (one exponential per lane and block instead of
+//     sixteen);
 //   * P.V: for bf16 the probabilities of two tokens are rounded to bf16 and
 //     paired with the two tokens' values in one v_dot2_f32_bf16 per output
 //     (fp32 accumulation); for fp32 inputs it is plain fp32 FMA.
@@ -101,6 +102,31 @@ __device__ __forceinline__ uint32_t row_bcast_u32(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x150 + N, 0xF, 0xF, false);
 }
 
+// row_bcast_u32 by a lane index known after unrolling.
+__device__ __forceinline__ uint32_t row_bcast_at(uint32_t x, int n) {
+  switch (n) {
+    case 0: return row_bcast_u32<0>(x);
+    case 1: return row_bcast_u32<1>(x);
+    case 2: return row_bcast_u32<2>(x);
+    case 3: return row_bcast_u32<3>(x);
+    case 4: return row_bcast_u32<4>(x);
+    case 5: return row_bcast_u32<5>(x);
+    case 6: return row_bcast_u32<6>(x);
+    case 7: return row_bcast_u32<7>(x);
+    case 8: return row_bcast_u32<8>(x);
+    case 9: return row_bcast_u32<9>(x);
+    case 10: return row_bcast_u32<10>(x);
+    case 11: return row_bcast_u32<11>(x);
+    case 12: return row_bcast_u32<12>(x);
+    case 13: return row_bcast_u32<13>(x);
+    case 14: return row_bcast_u32<14>(x);
+    default: return row_bcast_u32<15>(x);
+  }
+}
+__device__ __forceinline__ float row_bcast_at(float x, int n) {
+  return __uint_as_float(row_bcast_at(__float_as_uint(x), n));
+}
+
 // Transposing sum over the 16 lanes of a row: lane c holds 16 partial values
 // v[0..16) and ends with the row's total of v[c].  Each step pairs the lane
 // with a partner that differs in one more index bit (3, 2, 1, 0 through
@@ -139,8 +165,10 @@ __device__ __forceinline__ float xpose_sum16(float (&v)[16], int c) {
 //     attended by the heads that chose it only.
 constexpr int kSetWindow = 0, kSetPerHead = 1, kSetUnion = 2;
 
+// (At least three waves per SIMD: only the eight-head instances are near
+// the limit, and three of them with a register or two spilled beat two.)
 template <bool BF16, int D, int G, bool PAGED_FAST, int SET = kSetWindow>
-__global__ __launch_bounds__(kThreads) void gqa_split_kernel(const GqaArgs a) {
+__global__ __launch_bounds__(kThreads, 3) void gqa_split_kernel(const GqaArgs a) {
   using S = GqaShape<BF16, D>;
   constexpr int VEC = S::VEC, LPR = S::LPR, RPI = S::RPI, TPL = S::TPL;
   const float NEG_INF = -__builtin_inff();
@@ -198,9 +226,11 @@ __global__ __launch_bounds__(kThreads) void gqa_split_kernel(const GqaArgs a) {
   // owns the score of head c / 4 and token row c % 4; it takes one
   // exponential (not 16 copies of each), and the probabilities are
   // broadcast back for P.V.  lc is the lane's share of the denominator.
-  constexpr bool kXpose = LPR == 16 && TPL * G == 16;
-  static_assert(!kXpose || (G == 4 && TPL == 4), "the transposed path is written for four heads and four rows");
-  float lc = 0.f;
+  constexpr bool kXpose = LPR == 16 && TPL == 4 && (G == 4 || G == 8);
+  constexpr int kNB = G >= 4 ? G / 4 : 1;  // blocks of 16 (token row, head) scores per lane
+  float lc[kNB];
+#pragma unroll
+  for (int k = 0; k < kNB; ++k) lc[k] = 0.f;
 
   const size_t head_stride = (size_t)a.page_size * D;
   const size_t page_stride = (size_t)a.Hkv * head_stride;
@@ -263,98 +293,107 @@ __global__ __launch_bounds__(kThreads) void gqa_split_kernel(const GqaArgs a) {
     }
   };
 
-  // The transposed path of compute (kXpose): tokens t0 + u RPI + r, u < 4.
+  // The transposed path of compute (kXpose): tokens t0 + u RPI + r, u < 4;
+  // block k of the lane's scores holds heads 4k .. 4k + 3.
   auto compute_xpose = [&](int t0, int lo, int hi, uint32_t heads, const KvRegs<TPL>& R) {
     if constexpr (kXpose) {
-      float v[16];  // v[4 h + u]: this lane's part of q_h . k_u
+      float dot[kNB];
+      // one block of four heads at a time: its 16 partial dot products are
+      // transposed before the next block's are formed (fewer live registers)
 #pragma unroll
-      for (int u = 0; u < TPL; ++u) {
+      for (int k = 0; k < kNB; ++k) {
+        float v[16];  // v[4 i + u]: this lane's part of q_{4k+i} . k_u
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          float acc;
-          if constexpr (BF16) {
-            acc = dot2_bf16(R.k[u].x, qv[h].x, 0.f);
-            acc = dot2_bf16(R.k[u].y, qv[h].y, acc);
-            acc = dot2_bf16(R.k[u].z, qv[h].z, acc);
-            acc = dot2_bf16(R.k[u].w, qv[h].w, acc);
-          } else {
-            acc = __uint_as_float(R.k[u].x) * __uint_as_float(qv[h].x);
-            acc = fmaf(__uint_as_float(R.k[u].y), __uint_as_float(qv[h].y), acc);
-            acc = fmaf(__uint_as_float(R.k[u].z), __uint_as_float(qv[h].z), acc);
-            acc = fmaf(__uint_as_float(R.k[u].w), __uint_as_float(qv[h].w), acc);
+        for (int u = 0; u < TPL; ++u) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int h = 4 * k + i;
+            float acc;
+            if constexpr (BF16) {
+              acc = dot2_bf16(R.k[u].x, qv[h].x, 0.f);
+              acc = dot2_bf16(R.k[u].y, qv[h].y, acc);
+              acc = dot2_bf16(R.k[u].z, qv[h].z, acc);
+              acc = dot2_bf16(R.k[u].w, qv[h].w, acc);
+            } else {
+              acc = __uint_as_float(R.k[u].x) * __uint_as_float(qv[h].x);
+              acc = fmaf(__uint_as_float(R.k[u].y), __uint_as_float(qv[h].y), acc);
+              acc = fmaf(__uint_as_float(R.k[u].z), __uint_as_float(qv[h].z), acc);
+              acc = fmaf(__uint_as_float(R.k[u].w), __uint_as_float(qv[h].w), acc);
+            }
+            v[4 * i + u] = acc;
           }
-          v[4 * h + u] = acc;
         }
+        // every lane of the row takes part in the cross-lane sum (a lane
+        // left out would hand its partners zeros): sum first, then mask
+        dot[k] = xpose_sum16(v, c);
       }
-      const int hc = c >> 2, uc = c & 3;
+      const int uc = c & 3;
       const int t = t0 + uc * RPI + r;
-      const bool valid = t >= lo && t < hi && ((heads >> hc) & 1u);
-      // every lane of the row takes part in the cross-lane sum (a lane left
-      // out would hand its partners zeros): sum first, then mask
-      const float dot = xpose_sum16(v, c);
-      const float sc = valid ? dot * a.scale_log2 : NEG_INF;
-      // each head's maximum over the row's four tokens, then every head's
-      // in every lane (the reference maxima are kept per row, in every lane)
-      float mx = fmaxf(sc, dpp_f32<0xB1>(sc));
-      mx = fmaxf(mx, dpp_f32<0x4E>(mx));
-      float mxh[G];
-      mxh[0] = row_bcast<0>(mx);
-      mxh[1] = row_bcast<4>(mx);
-      mxh[2] = row_bcast<8>(mx);
-      mxh[3] = row_bcast<12>(mx);
-      float mine = m[0];
+      const bool tvalid = t >= lo && t < hi;
+      // each head's maximum over the row's four tokens, then every head's in
+      // every lane (the reference maxima are kept per row, in every lane)
+      float sc[kNB], mxh[G];
+#pragma unroll
+      for (int k = 0; k < kNB; ++k) {
+        const int hc = 4 * k + (c >> 2);
+        sc[k] = tvalid && ((heads >> hc) & 1u) ? dot[k] * a.scale_log2 : NEG_INF;
+        float mx = fmaxf(sc[k], dpp_f32<0xB1>(sc[k]));
+        mx = fmaxf(mx, dpp_f32<0x4E>(mx));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mxh[4 * k + i] = row_bcast_at(mx, 4 * i);
+      }
+      float mine[kNB];
+#pragma unroll
+      for (int k = 0; k < kNB; ++k) mine[k] = m[4 * k];
 #pragma unroll
       for (int h = 0; h < G; ++h) {
+        const bool own = (c >> 2) == (h & 3);  // this lane holds head h in block h / 4
         if (mxh[h] > m[h] + kTau) {
           const float alpha = fast_exp2(m[h] - mxh[h]);  // 0 when m was -inf
 #pragma unroll
           for (int e = 0; e < VEC; ++e) o[h][e] *= alpha;
-          if (hc == h) lc *= alpha;
+          if (own) lc[h / 4] *= alpha;
           m[h] = mxh[h];
         }
-        if (hc == h) mine = m[h];
+        if (own) mine[h / 4] = m[h];
       }
-      const float p = fast_exp2(sc - (mine == NEG_INF ? 0.f : mine));
-      lc += p;
-      // (p_u, p_u+1) of a head in the lanes of even u, then to every lane
-      const uint32_t pk = pack_bf16x2(p, dpp_f32<0xB1>(p));
-      uint32_t pp[2][G];
-      pp[0][0] = row_bcast_u32<0>(pk);
-      pp[1][0] = row_bcast_u32<2>(pk);
-      pp[0][1] = row_bcast_u32<4>(pk);
-      pp[1][1] = row_bcast_u32<6>(pk);
-      pp[0][2] = row_bcast_u32<8>(pk);
-      pp[1][2] = row_bcast_u32<10>(pk);
-      pp[0][3] = row_bcast_u32<12>(pk);
-      pp[1][3] = row_bcast_u32<14>(pk);
+      float p[kNB];
+#pragma unroll
+      for (int k = 0; k < kNB; ++k) {
+        p[k] = fast_exp2(sc[k] - (mine[k] == NEG_INF ? 0.f : mine[k]));
+        lc[k] += p[k];
+      }
       if constexpr (BF16) {
+        // (p_u, p_u+1) of a head in the lanes of even u, then to every lane
+        uint32_t pk[kNB];
+#pragma unroll
+        for (int k = 0; k < kNB; ++k) pk[k] = pack_bf16x2(p[k], dpp_f32<0xB1>(p[k]));
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
+          uint32_t pp[G];
+#pragma unroll
+          for (int h = 0; h < G; ++h) pp[h] = row_bcast_at(pk[h / 4], 4 * (h % 4) + 2 * j);
 #pragma unroll
           for (int w = 0; w < 4; ++w) {
             const uint32_t a0 = u4(R.v[2 * j], w), a1 = u4(R.v[2 * j + 1], w);
             const uint32_t plo = pair_lo(a0, a1), phi = pair_hi(a0, a1);
 #pragma unroll
             for (int h = 0; h < G; ++h) {
-              o[h][2 * w] = dot2_bf16(pp[j][h], plo, o[h][2 * w]);
-              o[h][2 * w + 1] = dot2_bf16(pp[j][h], phi, o[h][2 * w + 1]);
+              o[h][2 * w] = dot2_bf16(pp[h], plo, o[h][2 * w]);
+              o[h][2 * w + 1] = dot2_bf16(pp[h], phi, o[h][2 * w + 1]);
             }
           }
         }
       } else {
         // fp32 values take fp32 probabilities: broadcast them unrounded
-        const float pf[TPL][G] = {
-            {row_bcast<0>(p), row_bcast<4>(p), row_bcast<8>(p), row_bcast<12>(p)},
-            {row_bcast<1>(p), row_bcast<5>(p), row_bcast<9>(p), row_bcast<13>(p)},
-            {row_bcast<2>(p), row_bcast<6>(p), row_bcast<10>(p), row_bcast<14>(p)},
-            {row_bcast<3>(p), row_bcast<7>(p), row_bcast<11>(p), row_bcast<15>(p)}};
-        (void)pp;
 #pragma unroll
         for (int u = 0; u < TPL; ++u) {
 #pragma unroll
-          for (int h = 0; h < G; ++h)
+          for (int h = 0; h < G; ++h) {
+            const float pu = row_bcast_at(p[h / 4], 4 * (h % 4) + u);
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) o[h][e] = fmaf(pf[u][h], __uint_as_float(u4(R.v[u], e)), o[h][e]);
+            for (int e = 0; e < VEC; ++e) o[h][e] = fmaf(pu, __uint_as_float(u4(R.v[u], e)), o[h][e]);
+          }
         }
       }
     }
@@ -465,12 +504,13 @@ __global__ __launch_bounds__(kThreads) void gqa_split_kernel(const GqaArgs a) {
   }
 
   if constexpr (kXpose) {  // each head's denominator, in every lane of the row
-    float ls = lc + dpp_f32<0xB1>(lc);
-    ls += dpp_f32<0x4E>(ls);
-    l[0] = row_bcast<0>(ls);
-    l[1] = row_bcast<4>(ls);
-    l[2] = row_bcast<8>(ls);
-    l[3] = row_bcast<12>(ls);
+#pragma unroll
+    for (int k = 0; k < kNB; ++k) {
+      float ls = lc[k] + dpp_f32<0xB1>(lc[k]);
+      ls += dpp_f32<0x4E>(ls);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) l[4 * k + i] = row_bcast_at(ls, 4 * i);
+    }
   }
 
   // merge the token rows of the wave (lanes c, c + LPR, ...)
