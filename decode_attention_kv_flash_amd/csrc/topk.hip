@@ -46,7 +46,7 @@ constexpr int kKPT = 8;              // keys per thread
 constexpr int kChunk = kTT * kKPT;   // tokens per workgroup
 static_assert(kChunk == kTopkChunk, "chunk size shared with the indexer");
 constexpr int kBins = 256;           // one byte of the key per launch
-constexpr int kColBatch = 16;        // chunk histograms loaded per batch
+constexpr int kColBatch = 32;        // chunk histograms loaded per batch
 
 // One row's workspace, in 32-bit words.
 struct RowWs {
