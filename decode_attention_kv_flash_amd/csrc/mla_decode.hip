@@ -386,42 +386,47 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_split_kernel(const MlaArgs a) 
   // Prologue: tiles 0..2 requested, tile 0 scored and its softmax taken,
   // tile 1 complete in LDS.  (A prologue never votes: its reference is unset
   // or already the largest score seen.)
+  // Tiles past the split are never copied (their positions are all masked,
+  // so whatever their buffers hold never reaches a result).
   auto prime = [&]() {
     issue(0);
-    issue(1);
-    issue(2);
-    barrier_in_flight<2 * kDmaPerWave>();
+    if (n_tiles > 1) issue(1);
+    if (n_tiles > 2) issue(2);
+    if (n_tiles > 2) barrier_in_flight<2 * kDmaPerWave>();  // tile 0 complete
+    else if (n_tiles > 1) barrier_in_flight<kDmaPerWave>();
+    else barrier_in_flight<0>();
     softmax(scores(std::false_type{}, buffer(0), 0u), 0, 0);
-    barrier_in_flight<kDmaPerWave>();
+    if (n_tiles > 2) barrier_in_flight<kDmaPerWave>();  // tile 1 complete
+    else barrier_in_flight<0>();
   };
 
-  // Iteration t: request tile t + 3 (into the buffer tile t - 1 freed),
-  // P.V of tile t alternated with the scores of tile t + 1 (for the last t
-  // a padding tile, all flagged: its softmax changes nothing), then the
-  // softmax of tile t + 1.  No branches around tiles.  A restart leaves the
-  // tile loop and runs the prologue again.
+  // Iteration t: request tile t + 3 if the split has it (into the buffer
+  // tile t - 1 freed), P.V of tile t alternated with the scores of tile t + 1
+  // (for the last t a padding tile, all flagged: its softmax changes
+  // nothing), then the softmax of tile t + 1.  Once no tile is requested the
+  // barrier waits for every copy, so none is in flight when the workgroup
+  // ends.  A restart leaves the tile loop and runs the prologue again.
   while (n_tiles > 0) {
     prime();
     int slot = 0;
     bool again = false;
     for (int t = 0; t < n_tiles; ++t) {
       if (threadIdx.x == 0) restart_vote[slot == 2 ? 0 : slot + 1] = 0;  // iteration t - 2's
-      issue(t + 3);
+      const bool more = t + 3 < n_tiles;
+      if (more) issue(t + 3);
       const f32x16_t s = scores(std::true_type{}, buffer(t + 1), buffer(t));
       softmax(s, t + 1, slot);
       // tile t + 2 complete in LDS for every wave (only tile t + 3 may still
       // be in flight); buffer of tile t free for reuse
-      barrier_in_flight<kDmaPerWave>();
+      if (more) barrier_in_flight<kDmaPerWave>();
+      else barrier_in_flight<0>();
       if (restart_vote[slot]) {
         again = true;
         break;
       }
       slot = slot == 2 ? 0 : slot + 1;
     }
-    if (!again) {
-      wait_vmcnt<0>();  // the prefetches past the end land before the workgroup ends
-      break;
-    }
+    if (!again) break;
     // some head's maximum jumped: redo the split with every head's reference
     // at the largest score it has seen (each restart raises a reference by
     // more than kTau, so restarts are few)
