@@ -274,7 +274,8 @@ def decode_attn_quest(q, k_cache, v_cache, kminmax, seq_lens, budget, page_table
 
 
 def decode_attn_mla(q_absorbed, latent_cache, seq_lens, page_table=None, *, d_latent=512,
-                    scale=None, num_splits=0, out=None, lse=None, want_lse=True, stream=None):
+                    scale=None, num_splits=0, out=None, lse=None, want_lse=True, workspace=None,
+                    stream=None):
     """Absorbed MLA decode attention.  latent_cache [B, S_max, 576] (contiguous)
     or [num_pages, page_size, 576] with page_table.  Returns (out [B,H,512], lse)."""
     for t, n in ((q_absorbed, "q_absorbed"), (latent_cache, "latent_cache"), (seq_lens, "seq_lens")):
@@ -292,7 +293,11 @@ def decode_attn_mla(q_absorbed, latent_cache, seq_lens, page_table=None, *, d_la
     if lse is None and want_lse:
         lse = torch.empty(B, H, dtype=torch.float32, device=q_absorbed.device)
     nbytes = lib().decode_attn_mla_workspace(B, H, d_latent, S_max, int(num_splits))
-    ws = _workspace(nbytes, q_absorbed.device)
+    if workspace is not None:
+        _dev(workspace, "workspace")
+        ws, nbytes = workspace, workspace.numel() * workspace.element_size()
+    else:
+        ws = _workspace(nbytes, q_absorbed.device)
     _check(lib().decode_attn_mla(
         _ptr(q_absorbed), _ptr(latent_cache), _ptr(seq_lens), _ptr(page_table), _ptr(out),
         _ptr(lse), B, H, d_latent, d_rope, S_max, page_size, max_pages, _dtype_code(q_absorbed),
@@ -301,7 +306,7 @@ def decode_attn_mla(q_absorbed, latent_cache, seq_lens, page_table=None, *, d_la
 
 
 def dsa_indexer_topk(q_i, w, k_i_cache, seq_lens, k, *, topk_idx=None, return_scores=False,
-                     stream=None):
+                     workspace=None, stream=None):
     """Indexer scores + top-k.  Returns topk_idx [B,k] (and scores [B,S_max])."""
     for t, n in ((q_i, "q_i"), (w, "w"), (k_i_cache, "k_i_cache"), (seq_lens, "seq_lens")):
         _dev(t, n)
@@ -315,14 +320,18 @@ def dsa_indexer_topk(q_i, w, k_i_cache, seq_lens, k, *, topk_idx=None, return_sc
         topk_idx = torch.empty(B, k, dtype=torch.int32, device=q_i.device)
     scores = torch.empty(B, S_max, dtype=torch.float32, device=q_i.device) if return_scores else None
     nbytes = lib().dsa_indexer_topk_workspace(B, S_max, k)
-    ws = _workspace(nbytes, q_i.device)
+    if workspace is not None:
+        _dev(workspace, "workspace")
+        ws, nbytes = workspace, workspace.numel() * workspace.element_size()
+    else:
+        ws = _workspace(nbytes, q_i.device)
     _check(lib().dsa_indexer_topk(
         _ptr(q_i), _ptr(w), _ptr(k_i_cache), _ptr(seq_lens), int(k), _ptr(topk_idx), _ptr(scores),
         B, Hi, Di, S_max, _dtype_code(q_i), _ptr(ws), nbytes, _stream(stream)))
     return (topk_idx, scores) if return_scores else topk_idx
 
 
-def dsa_topk(scores, seq_lens, k, *, topk_idx=None, stream=None):
+def dsa_topk(scores, seq_lens, k, *, topk_idx=None, workspace=None, stream=None):
     """Top-k of fp32 scores [B, S_max]; ties to the lower index; ascending; -1 padded."""
     _dev(scores, "scores")
     _dev(seq_lens, "seq_lens")
@@ -332,14 +341,18 @@ def dsa_topk(scores, seq_lens, k, *, topk_idx=None, stream=None):
     if topk_idx is None:
         topk_idx = torch.empty(B, k, dtype=torch.int32, device=scores.device)
     nbytes = lib().dsa_topk_workspace(B, S_max, k)
-    ws = _workspace(nbytes, scores.device)
+    if workspace is not None:
+        _dev(workspace, "workspace")
+        ws, nbytes = workspace, workspace.numel() * workspace.element_size()
+    else:
+        ws = _workspace(nbytes, scores.device)
     _check(lib().dsa_topk(_ptr(scores), _ptr(seq_lens), int(k), _ptr(topk_idx), B, S_max,
                           _ptr(ws), nbytes, _stream(stream)))
     return topk_idx
 
 
 def sparse_mla_attn(q, latent_cache, topk_idx, *, d_latent=512, scale=None, num_splits=0,
-                    out=None, lse=None, want_lse=True, stream=None):
+                    out=None, lse=None, want_lse=True, workspace=None, stream=None):
     """MLA over the rows listed in topk_idx [B,k] (-1 = skip).  Returns (out, lse)."""
     for t, n in ((q, "q"), (latent_cache, "latent_cache"), (topk_idx, "topk_idx")):
         _dev(t, n)
@@ -351,7 +364,11 @@ def sparse_mla_attn(q, latent_cache, topk_idx, *, d_latent=512, scale=None, num_
     if lse is None and want_lse:
         lse = torch.empty(B, H, dtype=torch.float32, device=q.device)
     nbytes = lib().sparse_mla_attn_workspace(B, H, d_latent, k, int(num_splits))
-    ws = _workspace(nbytes, q.device)
+    if workspace is not None:
+        _dev(workspace, "workspace")
+        ws, nbytes = workspace, workspace.numel() * workspace.element_size()
+    else:
+        ws = _workspace(nbytes, q.device)
     _check(lib().sparse_mla_attn(
         _ptr(q), _ptr(latent_cache), _ptr(topk_idx), k, _ptr(out), _ptr(lse), B, H, d_latent,
         Dq - d_latent, S_max, _dtype_code(q), float(scale or 0.0), int(num_splits), _ptr(ws),
