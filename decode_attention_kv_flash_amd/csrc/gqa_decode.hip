@@ -29,12 +29,12 @@
 //     token row of lanes; the reference maximum only moves when the new
 //     maximum exceeds it by more than 2^8, which bounds every exponential by
 //     2^8 and makes rescaling rare without changing the result;
-//   * with 16 lanes per row (D = 128 bf16 or D = 64 fp32) and four or eight
-//     heads per KV head, the sum over the row is a transposing one that
-//     leaves each lane one score per block of four heads; the lane takes
-//     that score's exponential and the probabilities are broadcast back with
-//     DPP row broadcasts (one exponential per lane and block instead of
-//     sixteen);
+//   * with 16 lanes per token row (D = 128 bf16 or D = 64 fp32) or 8 (D = 64
+//     bf16) and four or eight heads per KV head, the sum over the row is a
+//     transposing one that leaves each lane one score per block of four
+//     heads; the lane takes that score's exponential and the probabilities
+//     are broadcast back with DPP (one exponential per lane and block instead
+//     of one per score of the block);
 //   * P.V: for bf16 the probabilities of two tokens are rounded to bf16 and
 //     paired with the two tokens' values in one v_dot2_f32_bf16 per output
 //     (fp32 accumulation); for fp32 inputs it is plain fp32 FMA.
@@ -127,14 +127,53 @@ __device__ __forceinline__ float row_bcast_at(float x, int n) {
   return __uint_as_float(row_bcast_at(__float_as_uint(x), n));
 }
 
-// Transposing sum over the 16 lanes of a row: lane c holds 16 partial values
-// v[0..16) and ends with the row's total of v[c].  Each step pairs the lane
-// with a partner that differs in one more index bit (3, 2, 1, 0 through
-// row_mirror, row_half_mirror and the two quad swaps), keeps the half of its
-// values that bit selects and adds the partner's copy of that half: 15 adds
-// instead of the 64 of a full sum of every value in every lane.
-template <int CTRL, int N>
-__device__ __forceinline__ void xpose_step(float (&v)[16], bool upper) {
+// Broadcast of lane N of each 8-lane group to the group: a quad broadcast
+// (quad_perm [N, N, N, N] mod 4), after which the group's other quad takes
+// the value from four lanes away (a row shift written to that quad's DPP
+// banks only; bank k is lanes 4k .. 4k + 3 of a 16-lane row).
+template <int N>
+__device__ __forceinline__ uint32_t half_bcast_u32(uint32_t x) {
+  const int y = __builtin_amdgcn_update_dpp(0, (int)x, (N & 3) * 0x55, 0xF, 0xF, false);
+  if constexpr (N < 4)  // lanes 4..7 of the group read lane j - 4 (row_shr:4)
+    return (uint32_t)__builtin_amdgcn_update_dpp(y, y, 0x114, 0xF, 0xA, false);
+  else  // lanes 0..3 read lane j + 4 (row_shl:4)
+    return (uint32_t)__builtin_amdgcn_update_dpp(y, y, 0x104, 0xF, 0x5, false);
+}
+
+__device__ __forceinline__ uint32_t half_bcast_at(uint32_t x, int n) {
+  switch (n) {
+    case 0: return half_bcast_u32<0>(x);
+    case 1: return half_bcast_u32<1>(x);
+    case 2: return half_bcast_u32<2>(x);
+    case 3: return half_bcast_u32<3>(x);
+    case 4: return half_bcast_u32<4>(x);
+    case 5: return half_bcast_u32<5>(x);
+    case 6: return half_bcast_u32<6>(x);
+    default: return half_bcast_u32<7>(x);
+  }
+}
+
+// Lane n of each LPR-lane group (a token row) to the whole group.
+template <int LPR>
+__device__ __forceinline__ uint32_t group_bcast_at(uint32_t x, int n) {
+  static_assert(LPR == 8 || LPR == 16, "group of 8 or 16 lanes");
+  if constexpr (LPR == 16) return row_bcast_at(x, n);
+  else return half_bcast_at(x, n);
+}
+template <int LPR>
+__device__ __forceinline__ float group_bcast_at(float x, int n) {
+  return __uint_as_float(group_bcast_at<LPR>(__float_as_uint(x), n));
+}
+
+// Transposing sum over the NV = 16 (or 8) lanes of a row: lane c holds NV
+// partial values v[0..NV) and ends with the row's total of v[c].  Each step
+// pairs the lane with a partner that differs in one more index bit (3, 2, 1,
+// 0 through row_mirror, row_half_mirror and the two quad swaps; with eight
+// lanes the first is left out), keeps the half of its values that bit
+// selects and adds the partner's copy of that half: NV - 1 adds instead of
+// the NV log2(NV) of a full sum of every value in every lane.
+template <int CTRL, int N, int NV>
+__device__ __forceinline__ void xpose_step(float (&v)[NV], bool upper) {
 #pragma unroll
   for (int i = 0; i < N; ++i) {
     const float keep = upper ? v[i + N] : v[i];
@@ -143,8 +182,10 @@ __device__ __forceinline__ void xpose_step(float (&v)[16], bool upper) {
   }
 }
 
-__device__ __forceinline__ float xpose_sum16(float (&v)[16], int c) {
-  xpose_step<0x140, 8>(v, c & 8);  // partner 15 - c
+template <int NV>
+__device__ __forceinline__ float xpose_sum(float (&v)[NV], int c) {
+  static_assert(NV == 8 || NV == 16, "eight or sixteen lanes");
+  if constexpr (NV == 16) xpose_step<0x140, 8>(v, c & 8);  // partner 15 - c
   xpose_step<0x141, 4>(v, c & 4);  // partner c ^ 7 within the 8-lane half
   xpose_step<0x4E, 2>(v, c & 2);   // partner c ^ 2
   xpose_step<0xB1, 1>(v, c & 1);   // partner c ^ 1
@@ -221,13 +262,15 @@ __global__ __launch_bounds__(kThreads, 3) void gqa_split_kernel(const GqaArgs a)
 #pragma unroll
     for (int e = 0; e < VEC; ++e) o[h][e] = 0.f;
   }
-  // With 16 lanes per token row and 16 (token row, head) scores per lane the
-  // softmax runs transposed: after the transposing sum, lane c of the row
-  // owns the score of head c / 4 and token row c % 4; it takes one
-  // exponential (not 16 copies of each), and the probabilities are
-  // broadcast back for P.V.  lc is the lane's share of the denominator.
-  constexpr bool kXpose = LPR == 16 && TPL == 4 && (G == 4 || G == 8);
-  constexpr int kNB = G >= 4 ? G / 4 : 1;  // blocks of 16 (token row, head) scores per lane
+  // With LPR = 16 (or 8) lanes per token row and as many (token row, head)
+  // scores per lane and block of four heads (four heads times TPL = LPR / 4
+  // token rows) the softmax runs transposed: after the transposing sum,
+  // lane c of the row owns the score of head c / TPL and token row c % TPL;
+  // it takes one exponential (not LPR copies of each), and the
+  // probabilities are broadcast back for P.V.  lc is the lane's share of
+  // the denominator.
+  constexpr bool kXpose = (LPR == 16 || LPR == 8) && LPR == 4 * TPL && (G == 4 || G == 8);
+  constexpr int kNB = G >= 4 ? G / 4 : 1;  // blocks of LPR (token row, head) scores per lane
   float lc[kNB];
 #pragma unroll
   for (int k = 0; k < kNB; ++k) lc[k] = 0.f;
@@ -293,16 +336,16 @@ __global__ __launch_bounds__(kThreads, 3) void gqa_split_kernel(const GqaArgs a)
     }
   };
 
-  // The transposed path of compute (kXpose): tokens t0 + u RPI + r, u < 4;
+  // The transposed path of compute (kXpose): tokens t0 + u RPI + r, u < TPL;
   // block k of the lane's scores holds heads 4k .. 4k + 3.
   auto compute_xpose = [&](int t0, int lo, int hi, uint32_t heads, const KvRegs<TPL>& R) {
     if constexpr (kXpose) {
       float dot[kNB];
-      // one block of four heads at a time: its 16 partial dot products are
+      // one block of four heads at a time: its LPR partial dot products are
       // transposed before the next block's are formed (fewer live registers)
 #pragma unroll
       for (int k = 0; k < kNB; ++k) {
-        float v[16];  // v[4 i + u]: this lane's part of q_{4k+i} . k_u
+        float v[LPR];  // v[TPL i + u]: this lane's part of q_{4k+i} . k_u
 #pragma unroll
         for (int u = 0; u < TPL; ++u) {
 #pragma unroll
@@ -320,34 +363,34 @@ __global__ __launch_bounds__(kThreads, 3) void gqa_split_kernel(const GqaArgs a)
               acc = fmaf(__uint_as_float(R.k[u].z), __uint_as_float(qv[h].z), acc);
               acc = fmaf(__uint_as_float(R.k[u].w), __uint_as_float(qv[h].w), acc);
             }
-            v[4 * i + u] = acc;
+            v[TPL * i + u] = acc;
           }
         }
         // every lane of the row takes part in the cross-lane sum (a lane
         // left out would hand its partners zeros): sum first, then mask
-        dot[k] = xpose_sum16(v, c);
+        dot[k] = xpose_sum<LPR>(v, c);
       }
-      const int uc = c & 3;
+      const int uc = c % TPL;
       const int t = t0 + uc * RPI + r;
       const bool tvalid = t >= lo && t < hi;
-      // each head's maximum over the row's four tokens, then every head's in
+      // each head's maximum over the row's TPL tokens, then every head's in
       // every lane (the reference maxima are kept per row, in every lane)
       float sc[kNB], mxh[G];
 #pragma unroll
       for (int k = 0; k < kNB; ++k) {
-        const int hc = 4 * k + (c >> 2);
+        const int hc = 4 * k + c / TPL;
         sc[k] = tvalid && ((heads >> hc) & 1u) ? dot[k] * a.scale_log2 : NEG_INF;
         float mx = fmaxf(sc[k], dpp_f32<0xB1>(sc[k]));
-        mx = fmaxf(mx, dpp_f32<0x4E>(mx));
+        if constexpr (TPL == 4) mx = fmaxf(mx, dpp_f32<0x4E>(mx));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) mxh[4 * k + i] = row_bcast_at(mx, 4 * i);
+        for (int i = 0; i < 4; ++i) mxh[4 * k + i] = group_bcast_at<LPR>(mx, TPL * i);
       }
       float mine[kNB];
 #pragma unroll
       for (int k = 0; k < kNB; ++k) mine[k] = m[4 * k];
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const bool own = (c >> 2) == (h & 3);  // this lane holds head h in block h / 4
+        const bool own = c / TPL == (h & 3);  // this lane holds head h in block h / 4
         if (mxh[h] > m[h] + kTau) {
           const float alpha = fast_exp2(m[h] - mxh[h]);  // 0 when m was -inf
 #pragma unroll
@@ -369,10 +412,10 @@ __global__ __launch_bounds__(kThreads, 3) void gqa_split_kernel(const GqaArgs a)
 #pragma unroll
         for (int k = 0; k < kNB; ++k) pk[k] = pack_bf16x2(p[k], dpp_f32<0xB1>(p[k]));
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < TPL / 2; ++j) {
           uint32_t pp[G];
 #pragma unroll
-          for (int h = 0; h < G; ++h) pp[h] = row_bcast_at(pk[h / 4], 4 * (h % 4) + 2 * j);
+          for (int h = 0; h < G; ++h) pp[h] = group_bcast_at<LPR>(pk[h / 4], TPL * (h % 4) + 2 * j);
 #pragma unroll
           for (int w = 0; w < 4; ++w) {
             const uint32_t a0 = u4(R.v[2 * j], w), a1 = u4(R.v[2 * j + 1], w);
@@ -390,7 +433,7 @@ __global__ __launch_bounds__(kThreads, 3) void gqa_split_kernel(const GqaArgs a)
         for (int u = 0; u < TPL; ++u) {
 #pragma unroll
           for (int h = 0; h < G; ++h) {
-            const float pu = row_bcast_at(p[h / 4], 4 * (h % 4) + u);
+            const float pu = group_bcast_at<LPR>(p[h / 4], TPL * (h % 4) + u);
 #pragma unroll
             for (int e = 0; e < VEC; ++e) o[h][e] = fmaf(pu, __uint_as_float(u4(R.v[u], e)), o[h][e]);
           }
@@ -507,9 +550,9 @@ __global__ __launch_bounds__(kThreads, 3) void gqa_split_kernel(const GqaArgs a)
 #pragma unroll
     for (int k = 0; k < kNB; ++k) {
       float ls = lc[k] + dpp_f32<0xB1>(lc[k]);
-      ls += dpp_f32<0x4E>(ls);
+      if constexpr (TPL == 4) ls += dpp_f32<0x4E>(ls);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) l[4 * k + i] = row_bcast_at(ls, 4 * i);
+      for (int i = 0; i < 4; ++i) l[4 * k + i] = group_bcast_at<LPR>(ls, TPL * i);
     }
   }
 

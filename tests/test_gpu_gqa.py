@@ -67,6 +67,7 @@ def test_zero_sink_tiny_fp32(splits):
     (32, 8, 128, torch.bfloat16, True),
     (8, 1, 64, torch.float32, False),
     (8, 2, 64, torch.float32, True),
+    (64, 8, 64, torch.bfloat16, True),
 ])
 @pytest.mark.parametrize("splits", [0, 1, 3])
 def test_learned_sinks_ragged(Hq, Hkv, D, dtype, paged, splits):
@@ -83,6 +84,15 @@ def test_learned_sinks_with_window(splits):
     x = wl.make_gqa(B=3, Hq=32, Hkv=8, D=128, seq_lens=[3, 700, 5000], dtype=torch.bfloat16,
                     page_size=16, paged=True, window=512, n_sink=4, seed=32, name="sinks_window")
     check_sink(x, [float(h % 7) - 3.0 for h in range(32)], splits)
+
+
+@pytest.mark.parametrize("splits", [0, 2])
+def test_learned_sinks_window_d64_eight_heads(splits):
+    """64 q / 8 KV heads, D64 bf16, a 128-token window and a sink logit per
+    head: the eight-head transposed softmax at 8 lanes per token row."""
+    x = wl.make_gqa(B=3, Hq=64, Hkv=8, D=64, seq_lens=[5, 130, 2000], dtype=torch.bfloat16,
+                    page_size=16, paged=True, window=128, seed=35, name="sinks_window_d64")
+    check_sink(x, [float(h % 9) - 4.0 for h in range(64)], splits)
 
 
 def test_sink_on_empty_sequences():
@@ -102,6 +112,8 @@ def test_sink_on_empty_sequences():
     (6, 3, 64, torch.bfloat16, True),     # G = 2, odd head counts
     (8, 2, 64, torch.float32, True),      # G = 4 at 16 lanes per row in fp32: the transposed softmax
     (16, 4, 128, torch.bfloat16, False),  # G = 4, contiguous
+    (8, 2, 64, torch.bfloat16, True),     # G = 4 at 8 lanes per row: the transposed softmax
+    (64, 8, 64, torch.bfloat16, False),   # G = 8 at 8 lanes per row, contiguous
 ])
 @pytest.mark.parametrize("splits", [0, 1, 3])
 def test_gqa_ragged(Hq, Hkv, D, dtype, paged, splits):
