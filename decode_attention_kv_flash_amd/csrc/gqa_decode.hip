@@ -165,15 +165,37 @@ __device__ __forceinline__ float group_bcast_at(float x, int n) {
   return __uint_as_float(group_bcast_at<LPR>(__float_as_uint(x), n));
 }
 
-// Transposing sum over the NV = 16 (or 8) lanes of a row: lane c holds NV
-// partial values v[0..NV) and ends with the row's total of v[c].  Each step
-// pairs the lane with a partner that differs in one more index bit (3, 2, 1,
-// 0 through row_mirror, row_half_mirror and the two quad swaps; with eight
-// lanes the first is left out), keeps the half of its values that bit
-// selects and adds the partner's copy of that half: NV - 1 adds instead of
-// the NV log2(NV) of a full sum of every value in every lane.
+// Transposing sum over the NV = 16 (or 8) lanes of a row of values
+// numbered TPL i + u (head i < 4 of a block, token row u < TPL = NV / 4).
+// Each step pairs a lane with a partner (15 - c by row_mirror, c ^ 7 within
+// the 8-lane half by row_half_mirror, then the quad swaps c ^ 2 and c ^ 1;
+// with eight lanes the first step is left out) and halves the values the
+// lane holds, so that it ends with the row's total of one of them: NV - 1
+// adds instead of the NV log2(NV) of summing every value in every lane.
+//   * The first two steps split the heads.  Lane c keeps its values in the
+//     order v[TPL i + u] = (its part of head i ^ gray(c / TPL), token row u),
+//     fixed per lane by the order it loads its query rows in (gray(q) = q ^
+//     (q >> 1)); with that order the partners' upper halves always hold the
+//     lane's lower half's heads, and the lane just adds them.
+//   * The last steps split the token rows between the TPL lanes of a head:
+//     there the lane keeps the half its own bit selects and adds the
+//     partner's copy of that half.
+// Lane c ends with head gray(c / TPL), token row c % TPL; xpose_lane(i, u)
+// is the lane that ends with head i, token row u.
+__host__ __device__ constexpr int gray2(int q) { return q ^ (q >> 1); }
+template <int TPL>
+__host__ __device__ constexpr int xpose_lane(int i, int u) {
+  return TPL * gray2(i) + u;  // gray2 is its own inverse on two bits
+}
+
 template <int CTRL, int N, int NV>
-__device__ __forceinline__ void xpose_step(float (&v)[NV], bool upper) {
+__device__ __forceinline__ void xpose_add(float (&v)[NV]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += dpp_f32<CTRL>(v[i + N]);
+}
+
+template <int CTRL, int N, int NV>
+__device__ __forceinline__ void xpose_keep(float (&v)[NV], bool upper) {
 #pragma unroll
   for (int i = 0; i < N; ++i) {
     const float keep = upper ? v[i + N] : v[i];
@@ -185,10 +207,15 @@ __device__ __forceinline__ void xpose_step(float (&v)[NV], bool upper) {
 template <int NV>
 __device__ __forceinline__ float xpose_sum(float (&v)[NV], int c) {
   static_assert(NV == 8 || NV == 16, "eight or sixteen lanes");
-  if constexpr (NV == 16) xpose_step<0x140, 8>(v, c & 8);  // partner 15 - c
-  xpose_step<0x141, 4>(v, c & 4);  // partner c ^ 7 within the 8-lane half
-  xpose_step<0x4E, 2>(v, c & 2);   // partner c ^ 2
-  xpose_step<0xB1, 1>(v, c & 1);   // partner c ^ 1
+  if constexpr (NV == 16) {
+    xpose_add<0x140, 8>(v);      // partner 15 - c: heads
+    xpose_add<0x141, 4>(v);      // partner c ^ 7 within the half: heads
+    xpose_keep<0x4E, 2>(v, c & 2);  // partner c ^ 2: token rows
+  } else {
+    xpose_add<0x141, 4>(v);      // partner c ^ 7: heads
+    xpose_add<0x4E, 2>(v);       // partner c ^ 2: heads
+  }
+  xpose_keep<0xB1, 1>(v, c & 1);  // partner c ^ 1: token rows
   return v[0];
 }
 
@@ -246,12 +273,27 @@ __global__ __launch_bounds__(kThreads, 3) void gqa_split_kernel(const GqaArgs a)
   const int blk_begin = min(n_blocks, split * per);
   const int blk_end = min(n_blocks, blk_begin + per);
 
+  // With LPR = 16 (or 8) lanes per token row and as many (token row, head)
+  // scores per lane and block of four heads (four heads times TPL = LPR / 4
+  // token rows) the softmax runs transposed: after the transposing sum,
+  // lane c of the row owns one score of each block of four heads: head
+  // xi = gray(c / TPL) of the block, token row xu = c % TPL of the step.  It
+  // takes one exponential (not LPR copies of each), and the probabilities
+  // are broadcast back for P.V.  For the sum, the lane's query slot i holds
+  // head i ^ xi of each block.
+  constexpr bool kXpose = (LPR == 16 || LPR == 8) && LPR == 4 * TPL && (G == 4 || G == 8);
+  constexpr int kNB = G >= 4 ? G / 4 : 1;  // blocks of LPR (token row, head) scores per lane
+  const int xu = kXpose ? c % TPL : 0, xi = kXpose ? gray2(c / TPL) : 0;
+
   // This lane's piece of each of the G query rows: dims c*VEC + [0, VEC).
   uint4 qv[G];
   {
     const char* qb = (const char*)a.q + ((size_t)(b * a.Hq + qh0) * D + c * VEC) * S::ESZ;
 #pragma unroll
-    for (int h = 0; h < G; ++h) qv[h] = *(const uint4*)(qb + (size_t)h * D * S::ESZ);
+    for (int h = 0; h < G; ++h) {
+      const int hs = kXpose ? (h & ~3) | ((h & 3) ^ xi) : h;
+      qv[h] = *(const uint4*)(qb + (size_t)hs * D * S::ESZ);
+    }
   }
 
   float m[G], l[G], o[G][VEC];
@@ -262,18 +304,14 @@ __global__ __launch_bounds__(kThreads, 3) void gqa_split_kernel(const GqaArgs a)
 #pragma unroll
     for (int e = 0; e < VEC; ++e) o[h][e] = 0.f;
   }
-  // With LPR = 16 (or 8) lanes per token row and as many (token row, head)
-  // scores per lane and block of four heads (four heads times TPL = LPR / 4
-  // token rows) the softmax runs transposed: after the transposing sum,
-  // lane c of the row owns the score of head c / TPL and token row c % TPL;
-  // it takes one exponential (not LPR copies of each), and the
-  // probabilities are broadcast back for P.V.  lc is the lane's share of
-  // the denominator.
-  constexpr bool kXpose = (LPR == 16 || LPR == 8) && LPR == 4 * TPL && (G == 4 || G == 8);
-  constexpr int kNB = G >= 4 ? G / 4 : 1;  // blocks of LPR (token row, head) scores per lane
-  float lc[kNB];
+  // Transposed softmax: lc is the lane's share of its head's denominator,
+  // mo the reference maximum of its head (m of that head).
+  float lc[kNB], mo[kNB];
 #pragma unroll
-  for (int k = 0; k < kNB; ++k) lc[k] = 0.f;
+  for (int k = 0; k < kNB; ++k) {
+    lc[k] = 0.f;
+    mo[k] = NEG_INF;
+  }
 
   const size_t head_stride = (size_t)a.page_size * D;
   const size_t page_stride = (size_t)a.Hkv * head_stride;
@@ -306,38 +344,64 @@ __global__ __launch_bounds__(kThreads, 3) void gqa_split_kernel(const GqaArgs a)
   // Physical page of a block (wave-uniform; PAGED_FAST with a page table).
   auto page_of = [&](int blk) { return (int)pt[block_start(blk) >> a.log2_page]; };
 
-  // Issue the K/V loads of block blk (< blk_end) into R.  A lane whose token
-  // is outside the attended range loads the nearest attended row of the block
-  // instead: every address stays inside a page the table names (or inside the
-  // contiguous sequence), nothing past L_b is read, and the row is masked at
-  // compute time, so the loads need no branches.
+  // Byte offsets of the lane's rows inside a 16-token block (the rows of a
+  // block are contiguous in the page).
+  uint32_t roff[TPL];
+#pragma unroll
+  for (int u = 0; u < TPL; ++u) roff[u] = (uint32_t)(((u * RPI + r) * D) * S::ESZ) + (uint32_t)lane_off;
+
+  // Issue the K/V loads of block blk (< blk_end) into R.  In a partial block
+  // a lane whose token is outside the attended range loads the nearest
+  // attended row of the block instead: every address stays inside a page the
+  // table names (or inside the contiguous sequence), nothing past L_b is
+  // read, and the row is masked at compute time, so the loads need no
+  // branches.  A whole block takes the lane's fixed row offsets from one
+  // wave-uniform base.
   auto issue = [&](int blk, int phys, KvRegs<TPL>& R) {
     const int t0 = block_start(blk);
     int lo, hi;
     block_range(blk, t0, lo, hi);
-    size_t base_fast = 0;
     if constexpr (PAGED_FAST) {
-      base_fast = pt ? (size_t)phys * page_stride + (size_t)kvh * head_stride + (size_t)(t0 & (a.page_size - 1)) * D
-                     : contig_base + (size_t)t0 * D;
-    }
+      const size_t base = (pt ? (size_t)phys * page_stride + (size_t)kvh * head_stride +
+                                    (size_t)(t0 & (a.page_size - 1)) * D
+                              : contig_base + (size_t)t0 * D) * S::ESZ;
+      const char* kp = kb + base;
+      const char* vp = vb + base;
+      if (lo == t0 && hi == t0 + kStep) {
 #pragma unroll
-    for (int u = 0; u < TPL; ++u) {
-      const int t = min(max(t0 + u * RPI + r, lo), hi - 1);
-      size_t off;
-      if constexpr (PAGED_FAST) {
-        off = (base_fast + (size_t)(t - t0) * D) * S::ESZ + lane_off;
-      } else {
-        const int ph = a.page_table[(size_t)b * a.max_pages + (t >> a.log2_page)];
-        off = ((size_t)ph * page_stride + (size_t)kvh * head_stride + (size_t)(t & (a.page_size - 1)) * D) *
-                  S::ESZ + lane_off;
+        for (int u = 0; u < TPL; ++u) {
+          // (an empty asm keeps the 32-bit offset in the loop, so that each
+          // load takes the scalar base plus the lane's 32-bit offset)
+          uint32_t ro = roff[u];
+          asm volatile("" : "+v"(ro));
+          R.k[u] = load_stream(kp + ro);
+          R.v[u] = load_stream(vp + ro);
+        }
+        return;
       }
-      R.k[u] = load_stream(kb + off);
-      R.v[u] = load_stream(vb + off);
+#pragma unroll
+      for (int u = 0; u < TPL; ++u) {
+        const size_t off = (size_t)(min(max(t0 + u * RPI + r, lo), hi - 1) - t0) * D * S::ESZ + lane_off;
+        R.k[u] = load_stream(kp + off);
+        R.v[u] = load_stream(vp + off);
+      }
+    } else {
+      auto off_of = [&](int t) {
+        const int ph = a.page_table[(size_t)b * a.max_pages + (t >> a.log2_page)];
+        return ((size_t)ph * page_stride + (size_t)kvh * head_stride + (size_t)(t & (a.page_size - 1)) * D) *
+                   S::ESZ + lane_off;
+      };
+#pragma unroll
+      for (int u = 0; u < TPL; ++u) {
+        const size_t off = off_of(min(max(t0 + u * RPI + r, lo), hi - 1));
+        R.k[u] = load_stream(kb + off);
+        R.v[u] = load_stream(vb + off);
+      }
     }
   };
 
   // The transposed path of compute (kXpose): tokens t0 + u RPI + r, u < TPL;
-  // block k of the lane's scores holds heads 4k .. 4k + 3.
+  // block k of the scores holds heads 4k .. 4k + 3.
   auto compute_xpose = [&](int t0, int lo, int hi, uint32_t heads, const KvRegs<TPL>& R) {
     if constexpr (kXpose) {
       float dot[kNB];
@@ -345,7 +409,7 @@ __global__ __launch_bounds__(kThreads, 3) void gqa_split_kernel(const GqaArgs a)
       // transposed before the next block's are formed (fewer live registers)
 #pragma unroll
       for (int k = 0; k < kNB; ++k) {
-        float v[LPR];  // v[TPL i + u]: this lane's part of q_{4k+i} . k_u
+        float v[LPR];  // v[TPL i + u]: this lane's part of q_{4k + (i ^ xi)} . k_u
 #pragma unroll
         for (int u = 0; u < TPL; ++u) {
 #pragma unroll
@@ -370,40 +434,46 @@ __global__ __launch_bounds__(kThreads, 3) void gqa_split_kernel(const GqaArgs a)
         // left out would hand its partners zeros): sum first, then mask
         dot[k] = xpose_sum<LPR>(v, c);
       }
-      const int uc = c % TPL;
-      const int t = t0 + uc * RPI + r;
+      const int t = t0 + xu * RPI + r;
       const bool tvalid = t >= lo && t < hi;
-      // each head's maximum over the row's TPL tokens, then every head's in
-      // every lane (the reference maxima are kept per row, in every lane)
-      float sc[kNB], mxh[G];
+      float sc[kNB];
+      bool up = false;
 #pragma unroll
       for (int k = 0; k < kNB; ++k) {
-        const int hc = 4 * k + c / TPL;
-        sc[k] = tvalid && ((heads >> hc) & 1u) ? dot[k] * a.scale_log2 : NEG_INF;
-        float mx = fmaxf(sc[k], dpp_f32<0xB1>(sc[k]));
-        if constexpr (TPL == 4) mx = fmaxf(mx, dpp_f32<0x4E>(mx));
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mxh[4 * k + i] = group_bcast_at<LPR>(mx, TPL * i);
+        sc[k] = tvalid && ((heads >> (4 * k + xi)) & 1u) ? dot[k] * a.scale_log2 : NEG_INF;
+        up = up || sc[k] > mo[k] + kTau;
       }
-      float mine[kNB];
+      // The reference maxima move only when a score passes its head's by
+      // more than kTau, which is rare after the first block: the wave takes
+      // the branch only then.  In it each head's maximum over the row's TPL
+      // tokens goes to every lane of the row (the maxima are kept per row,
+      // in every lane).
+      if (__builtin_amdgcn_ballot_w64(up) != 0) {
+        float mxh[G];
 #pragma unroll
-      for (int k = 0; k < kNB; ++k) mine[k] = m[4 * k];
+        for (int k = 0; k < kNB; ++k) {
+          float mx = fmaxf(sc[k], dpp_f32<0xB1>(sc[k]));
+          if constexpr (TPL == 4) mx = fmaxf(mx, dpp_f32<0x4E>(mx));
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const bool own = c / TPL == (h & 3);  // this lane holds head h in block h / 4
-        if (mxh[h] > m[h] + kTau) {
-          const float alpha = fast_exp2(m[h] - mxh[h]);  // 0 when m was -inf
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) o[h][e] *= alpha;
-          if (own) lc[h / 4] *= alpha;
-          m[h] = mxh[h];
+          for (int i = 0; i < 4; ++i) mxh[4 * k + i] = group_bcast_at<LPR>(mx, xpose_lane<TPL>(i, 0));
         }
-        if (own) mine[h / 4] = m[h];
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const bool own = xi == (h & 3);  // this lane holds head h in block h / 4
+          if (mxh[h] > m[h] + kTau) {
+            const float alpha = fast_exp2(m[h] - mxh[h]);  // 0 when m was -inf
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) o[h][e] *= alpha;
+            if (own) lc[h / 4] *= alpha;
+            m[h] = mxh[h];
+          }
+          if (own) mo[h / 4] = m[h];
+        }
       }
       float p[kNB];
 #pragma unroll
       for (int k = 0; k < kNB; ++k) {
-        p[k] = fast_exp2(sc[k] - (mine[k] == NEG_INF ? 0.f : mine[k]));
+        p[k] = fast_exp2(sc[k] - (mo[k] == NEG_INF ? 0.f : mo[k]));
         lc[k] += p[k];
       }
       if constexpr (BF16) {
@@ -415,7 +485,8 @@ __global__ __launch_bounds__(kThreads, 3) void gqa_split_kernel(const GqaArgs a)
         for (int j = 0; j < TPL / 2; ++j) {
           uint32_t pp[G];
 #pragma unroll
-          for (int h = 0; h < G; ++h) pp[h] = group_bcast_at<LPR>(pk[h / 4], TPL * (h % 4) + 2 * j);
+          for (int h = 0; h < G; ++h)
+            pp[h] = group_bcast_at<LPR>(pk[h / 4], xpose_lane<TPL>(h % 4, 2 * j));
 #pragma unroll
           for (int w = 0; w < 4; ++w) {
             const uint32_t a0 = u4(R.v[2 * j], w), a1 = u4(R.v[2 * j + 1], w);
@@ -433,7 +504,7 @@ __global__ __launch_bounds__(kThreads, 3) void gqa_split_kernel(const GqaArgs a)
         for (int u = 0; u < TPL; ++u) {
 #pragma unroll
           for (int h = 0; h < G; ++h) {
-            const float pu = group_bcast_at<LPR>(p[h / 4], TPL * (h % 4) + u);
+            const float pu = group_bcast_at<LPR>(p[h / 4], xpose_lane<TPL>(h % 4, u));
 #pragma unroll
             for (int e = 0; e < VEC; ++e) o[h][e] = fmaf(pu, __uint_as_float(u4(R.v[u], e)), o[h][e]);
           }
@@ -552,7 +623,7 @@ __global__ __launch_bounds__(kThreads, 3) void gqa_split_kernel(const GqaArgs a)
       float ls = lc[k] + dpp_f32<0xB1>(lc[k]);
       if constexpr (TPL == 4) ls += dpp_f32<0x4E>(ls);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) l[4 * k + i] = group_bcast_at<LPR>(ls, TPL * i);
+      for (int i = 0; i < 4; ++i) l[4 * k + i] = group_bcast_at<LPR>(ls, xpose_lane<TPL>(i, 0));
     }
   }
 
