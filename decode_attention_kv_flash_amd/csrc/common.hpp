@@ -115,6 +115,15 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                          __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
+// a.lo*b.lo + a.hi*b.hi with nothing to accumulate: the three-operand form
+// with an inline zero (the compiler's choice, the accumulating two-operand
+// form, would first move a zero into the destination).
+__device__ __forceinline__ float dot2_bf16_first(uint32_t a, uint32_t b) {
+  float d;
+  asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(d) : "v"(a), "v"(b));
+  return d;
+}
+
 // ---- direct-to-LDS copies and the waits around them
 
 typedef __attribute__((address_space(3))) char lds_char;

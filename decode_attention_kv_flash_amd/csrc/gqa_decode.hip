@@ -417,7 +417,7 @@ __global__ __launch_bounds__(kThreads, 3) void gqa_split_kernel(const GqaArgs a)
             const int h = 4 * k + i;
             float acc;
             if constexpr (BF16) {
-              acc = dot2_bf16(R.k[u].x, qv[h].x, 0.f);
+              acc = dot2_bf16_first(R.k[u].x, qv[h].x);
               acc = dot2_bf16(R.k[u].y, qv[h].y, acc);
               acc = dot2_bf16(R.k[u].z, qv[h].z, acc);
               acc = dot2_bf16(R.k[u].w, qv[h].w, acc);
@@ -537,7 +537,7 @@ __global__ __launch_bounds__(kThreads, 3) void gqa_split_kernel(const GqaArgs a)
       for (int h = 0; h < G; ++h) {
         float acc;
         if constexpr (BF16) {
-          acc = dot2_bf16(R.k[u].x, qv[h].x, 0.f);
+          acc = dot2_bf16_first(R.k[u].x, qv[h].x);
           acc = dot2_bf16(R.k[u].y, qv[h].y, acc);
           acc = dot2_bf16(R.k[u].z, qv[h].z, acc);
           acc = dot2_bf16(R.k[u].w, qv[h].w, acc);
