@@ -98,13 +98,17 @@ int plan_gqa_splits(int32_t B, int32_t Hkv, int64_t max_tokens, int32_t req, int
 // Split-kernel workgroups to keep resident on the current device: what the
 // occupancy allows, at most 4 per CU (four waves per SIMD; a fifth bought
 // nothing on the GQA layer, 8 splits 86.1 us against 10 splits 87.4 us);
-// 3 per CU on 256 CUs when the device cannot be queried.
+// 3 per CU on 256 CUs when the device cannot be queried.  Eight heads per
+// KV head (a full register file: three waves per SIMD fit) run best at two
+// per CU: 64 q / 8 KV heads, 16 x 8192 tokens, D128, 90.7 us at 4 splits
+// against 92.3 us at 6; D64 and 16384 tokens, 93.1 against 95.5 us.
 constexpr int kMaxSplitWgPerCu = 4;
 int64_t gqa_slots(bool bf16, int D, int G, bool paged, int page_size) {
   const int cus = dattn::device_cu_count();
   int per = dattn::gqa_blocks_per_cu(bf16, D, G, paged, page_size);
   if (per < 1) per = 3;
   if (per > kMaxSplitWgPerCu) per = kMaxSplitWgPerCu;
+  if (G >= 8 && per > 2) per = 2;
   return (int64_t)per * cus;
 }
 

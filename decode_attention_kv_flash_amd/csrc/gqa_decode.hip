@@ -235,8 +235,14 @@ constexpr int kSetWindow = 0, kSetPerHead = 1, kSetUnion = 2;
 
 // (At least three waves per SIMD: only the eight-head instances are near
 // the limit, and three of them with a register or two spilled beat two.)
+// Eight bf16 heads per KV head keep two register buffers per wave (see the
+// main loop) and run two waves per SIMD.
+template <bool BF16, int G>
+constexpr bool gqa_double_buffer() { return BF16 && G >= 8; }
+
 template <bool BF16, int D, int G, bool PAGED_FAST, int SET = kSetWindow>
-__global__ __launch_bounds__(kThreads, 3) void gqa_split_kernel(const GqaArgs a) {
+__global__ __launch_bounds__(kThreads, (gqa_double_buffer<BF16, G>() ? 2 : 3)) void gqa_split_kernel(
+    const GqaArgs a) {
   using S = GqaShape<BF16, D>;
   constexpr int VEC = S::VEC, LPR = S::LPR, RPI = S::RPI, TPL = S::TPL;
   const float NEG_INF = -__builtin_inff();
@@ -367,23 +373,17 @@ __global__ __launch_bounds__(kThreads, 3) void gqa_split_kernel(const GqaArgs a)
                               : contig_base + (size_t)t0 * D) * S::ESZ;
       const char* kp = kb + base;
       const char* vp = vb + base;
-      if (lo == t0 && hi == t0 + kStep) {
-#pragma unroll
-        for (int u = 0; u < TPL; ++u) {
-          // (an empty asm keeps the 32-bit offset in the loop, so that each
-          // load takes the scalar base plus the lane's 32-bit offset)
-          uint32_t ro = roff[u];
-          asm volatile("" : "+v"(ro));
-          R.k[u] = load_stream(kp + ro);
-          R.v[u] = load_stream(vp + ro);
-        }
-        return;
-      }
+      const bool whole = lo == t0 && hi == t0 + kStep;
 #pragma unroll
       for (int u = 0; u < TPL; ++u) {
-        const size_t off = (size_t)(min(max(t0 + u * RPI + r, lo), hi - 1) - t0) * D * S::ESZ + lane_off;
-        R.k[u] = load_stream(kp + off);
-        R.v[u] = load_stream(vp + off);
+        // one load sequence for whole and partial blocks (the waits before
+        // the arithmetic then count loads exactly), each load the scalar
+        // base plus the lane's 32-bit offset
+        const uint32_t ro = whole ? roff[u]
+                                  : (uint32_t)((min(max(t0 + u * RPI + r, lo), hi - 1) - t0) * D * S::ESZ) +
+                                        (uint32_t)lane_off;
+        R.k[u] = load_stream(kp + ro);
+        R.v[u] = load_stream(vp + ro);
       }
     } else {
       auto off_of = [&](int t) {
@@ -610,11 +610,41 @@ __global__ __launch_bounds__(kThreads, 3) void gqa_split_kernel(const GqaArgs a)
   const bool paged_lookup = PAGED_FAST && pt;
   int blk = __builtin_amdgcn_readfirstlane(blk_begin + wave);
   int ph = paged_lookup && blk < blk_end ? page_of(blk) : 0;
-  for (; blk < blk_end; blk += kWaves) {
-    KvRegs<TPL> R;
-    issue(blk, ph, R);
-    if (paged_lookup && blk + kWaves < blk_end) ph = page_of(blk + kWaves);
-    compute(blk, R);
+  if constexpr (gqa_double_buffer<BF16, G>()) {
+    // With two waves per SIMD a wave's arithmetic would leave its SIMD with
+    // little in flight: the next block's loads go out before this block's
+    // arithmetic, into the other buffer.
+    // Every step issues its loads unconditionally (past the wave's last
+    // block it loads that block again, from L2) so that the wait before
+    // each block's arithmetic counts only the other buffer's loads.
+    KvRegs<TPL> R0, R1;
+    if (blk < blk_end) {
+      int ph1 = ph;
+      issue(blk, ph, R0);
+      if (paged_lookup && blk + kWaves < blk_end) ph1 = page_of(blk + kWaves);
+      for (;;) {
+        const int b1 = blk + kWaves < blk_end ? blk + kWaves : blk;
+        int ph2 = ph1;
+        issue(b1, ph1, R1);
+        if (paged_lookup && b1 + kWaves < blk_end) ph2 = page_of(b1 + kWaves);
+        compute(blk, R0);
+        if (b1 == blk) break;
+        const int b2 = b1 + kWaves < blk_end ? b1 + kWaves : b1;
+        ph1 = ph2;
+        issue(b2, ph2, R0);
+        if (paged_lookup && b2 + kWaves < blk_end) ph1 = page_of(b2 + kWaves);
+        compute(b1, R1);
+        if (b2 == b1) break;
+        blk = b2;
+      }
+    }
+  } else {
+    for (; blk < blk_end; blk += kWaves) {
+      KvRegs<TPL> R;
+      issue(blk, ph, R);
+      if (paged_lookup && blk + kWaves < blk_end) ph = page_of(blk + kWaves);
+      compute(blk, R);
+    }
   }
 
   if constexpr (kXpose) {  // each head's denominator, in every lane of the row
