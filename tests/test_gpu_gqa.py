@@ -114,11 +114,23 @@ def test_sink_on_empty_sequences():
     (16, 4, 128, torch.bfloat16, False),  # G = 4, contiguous
     (8, 2, 64, torch.bfloat16, True),     # G = 4 at 8 lanes per row: the transposed softmax
     (64, 8, 64, torch.bfloat16, False),   # G = 8 at 8 lanes per row, contiguous
+    (64, 8, 128, torch.bfloat16, True),   # G = 8 at 16 lanes per row
 ])
 @pytest.mark.parametrize("splits", [0, 1, 3])
 def test_gqa_ragged(Hq, Hkv, D, dtype, paged, splits):
     x = wl.make_gqa(B=4, Hq=Hq, Hkv=Hkv, D=D, seq_lens=[1, 17, 300, 1029], dtype=dtype,
                     page_size=16, paged=paged, seed=21, name=f"ragged_{Hq}_{Hkv}_{D}")
+    check_full(x, splits)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("splits", [1, 2, 5, 16])
+def test_eight_heads_double_buffer_edges(D, splits):
+    """Eight bf16 heads per KV head keep two register buffers per wave; short
+    and ragged sequences over many splits give waves none, one, two or three
+    blocks, whole and partial, so every exit of the two-buffer loop runs."""
+    x = wl.make_gqa(B=6, Hq=64, Hkv=8, D=D, seq_lens=[1, 16, 17, 64, 65, 200], dtype=torch.bfloat16,
+                    page_size=16, seed=36, name=f"g8_edges_d{D}")
     check_full(x, splits)
 
 

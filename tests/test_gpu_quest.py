@@ -90,6 +90,7 @@ def test_minmax_first_block_leaves_earlier_slots():
     (8, 8, 64, torch.bfloat16, False),
     (8, 1, 128, torch.float32, True),
     (4, 2, 64, torch.float32, False),
+    (16, 2, 128, torch.bfloat16, True),  # eight bf16 heads per KV head: two register buffers per wave
 ])
 @pytest.mark.parametrize("budget", [1, 4, 40])
 @pytest.mark.parametrize("splits", [0, 1, 3])
