@@ -21,7 +21,9 @@
 //     hidden across waves (a small register footprint keeps several
 //     workgroups resident per CU, so one wave's loads overlap another's
 //     arithmetic), and the page of the wave's next block is looked up one
-//     step ahead;
+//     step ahead.  Eight bf16 heads per KV head fill the register file, two
+//     waves per SIMD: those kernels keep two buffers per wave and issue the
+//     next block's loads before this block's arithmetic;
 //   * scores are lane-partial dot products (v_dot2_f32_bf16 for bf16: the
 //     bf16 products are exact in fp32) summed over the row's lanes with DPP;
 //   * the softmax is the online one ("All the attentions", section 1: a
