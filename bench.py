@@ -452,6 +452,25 @@ def main():
         del x3
         torch.cuda.empty_cache()
 
+        # other head layouts at config 2's K/V bytes: 64 q / 8 KV heads at D128
+        # (eight heads per KV head), and D64 over twice the tokens
+        result["workloads"]["gqa_head_layouts"] = {}
+        for hq, d, s_len in ((64, 128, 8192), (64, 64, 16384), (32, 64, 16384)):
+            name = f"gqa_{hq}q8kv_d{d}_b16_s{s_len}_paged16"
+            log(f"[bench] generating {name}")
+            xh = wl.make_gqa(B=16, Hq=hq, Hkv=8, D=d, seq_lens=[s_len] * 16, dtype=torch.bfloat16,
+                             page_size=16, seed=3, name=name)
+            bh = xh.kv_bytes()
+            rh = bench_gqa(xh, timer, steps, warmup, torch, lib)
+            result["workloads"]["gqa_head_layouts"][name] = {
+                "step_us": round(rh["wall_ms"] * 1e3, 2),
+                "GB/s": round(bh / (rh["wall_ms"] * 1e-3) / 1e9, 1),
+                "split_kernel_GB/s": round(gbs(bh, rh["kernels"]["gqa_split"]["avg_us"]), 1),
+                "kv_bytes_per_step": bh,
+                "kernels_us": {k: v["avg_us"] for k, v in rh["kernels"].items()}}
+            del xh
+            torch.cuda.empty_cache()
+
         log("[bench] generating MLA config (B32, H128, latent 576, 16384 tokens)")
         m4 = wl.config4_mla()
         r4 = bench_mla(m4, timer, steps, warmup, torch, lib)
