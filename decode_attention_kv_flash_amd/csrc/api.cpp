@@ -112,18 +112,18 @@ int64_t gqa_slots(bool bf16, int D, int G, bool paged, int page_size) {
   return (int64_t)per * cus;
 }
 
-// MLA workgroups (128 or 64 heads each, 127 KB of LDS) run one per CU: aim
-// for one full wave of 256 workgroups with splits of at least 128 tokens; a
-// split holds at most kMlaMaxSplitTokens tokens, which sets a floor on the
-// count (a request below it is raised).  0 when the count would exceed
-// kMlaMaxSplits.
-int plan_mla_splits(int32_t B, int32_t H, int64_t max_tokens, int32_t req) {
+// MLA workgroups (hpw = 128 or 64 heads each, 127 KB of LDS) run one per CU:
+// aim for one full wave of 256 workgroups with splits of at least 128
+// tokens; a split holds at most kMlaMaxSplitTokens tokens, which sets a
+// floor on the count (a request below it is raised).  0 when the count would
+// exceed kMlaMaxSplits.
+int plan_mla_splits(int32_t B, int32_t H, int hpw, int64_t max_tokens, int32_t req) {
   const int64_t floor_n = (max_tokens + dattn::kMlaMaxSplitTokens - 1) / dattn::kMlaMaxSplitTokens;
   int64_t n;
   if (req > 0) {
     n = req;
   } else {
-    const int64_t units = (int64_t)B * (H / dattn::mla_heads_per_workgroup(H));
+    const int64_t units = (int64_t)B * (H / hpw);
     const int64_t want = (256 + units - 1) / units;
     const int64_t cap = (max_tokens + 127) / 128;
     n = want < cap ? want : cap;
@@ -133,6 +133,26 @@ int plan_mla_splits(int32_t B, int32_t H, int64_t max_tokens, int32_t req) {
   if (n > kMlaMaxSplits) n = req > 0 ? kMlaMaxSplits : 0;
   if (n < floor_n) return 0;
   return (int)n;
+}
+
+// Splits and heads per workgroup of an MLA call.  A sparse call (a gathered
+// list of k rows per sequence) whose 128-head workgroups would leave CUs idle
+// takes 64-head workgroups instead: twice the workgroups, each with half the
+// query fragments and half the partials to write, the second of a pair
+// reading its rows from L2.  8 sequences x 2048 of 65536 rows, 128 heads,
+// 16 splits: 27.0 us against 29.4 us.
+struct MlaPlan {
+  int splits, heads_per_wg;
+};
+MlaPlan plan_mla(int32_t B, int32_t H, int64_t max_tokens, int32_t req, bool sparse) {
+  MlaPlan p{0, dattn::mla_heads_per_workgroup(H)};
+  p.splits = plan_mla_splits(B, H, p.heads_per_wg, max_tokens, req);
+  if (sparse && p.heads_per_wg == 128 && p.splits > 0 &&
+      (int64_t)B * (H / 128) * p.splits < dattn::device_cu_count()) {
+    const int s64 = plan_mla_splits(B, H, 64, max_tokens, req);
+    if (s64 > 0) p = MlaPlan{s64, 64};
+  }
+  return p;
 }
 
 // MLA partials: unnormalised O [rows, splits, 512], reference maxima and
@@ -390,7 +410,7 @@ int decode_attn_gqa_sink(const void* q, const void* k_cache, const void* v_cache
 size_t decode_attn_mla_workspace(int32_t B, int32_t H, int32_t d_latent, int32_t S_max,
                                  int32_t num_splits) {
   if (B < 1 || H < 64 || H % 64 != 0 || d_latent < 1 || S_max < 1 || num_splits < 0) return 0;
-  const int splits = plan_mla_splits(B, H, S_max, num_splits);
+  const int splits = plan_mla(B, H, S_max, num_splits, false).splits;
   return splits > 0 ? mla_workspace((int64_t)B * H, splits) : 0;
 }
 
@@ -425,7 +445,8 @@ int decode_attn_mla(const void* q_absorbed, const void* latent_cache, const int3
     if (max_pages < 1) return fail(DATTN_EINVAL, "decode_attn_mla: max_pages must be >= 1");
   }
   const int64_t max_tokens = page_table ? (int64_t)page_size * max_pages : S_max;
-  const int splits = plan_mla_splits(B, H, max_tokens, num_splits);
+  const MlaPlan plan = plan_mla(B, H, max_tokens, num_splits, false);
+  const int splits = plan.splits;
   if (splits < 1) return fail(DATTN_EUNSUPPORTED, "decode_attn_mla: %lld tokens need more than %d splits",
                               (long long)max_tokens, kMlaMaxSplits);
   if ((rc = check_workspace(workspace, workspace_bytes, mla_workspace((int64_t)B * H, splits))))
@@ -437,6 +458,7 @@ int decode_attn_mla(const void* q_absorbed, const void* latent_cache, const int3
   a.page_table = page_table;
   a.B = B;
   a.H = H;
+  a.heads_per_wg = plan.heads_per_wg;
   a.S_max = S_max;
   a.page_size = page_table ? page_size : S_max;
   a.log2_page = page_table ? ilog2(page_size) : 0;
@@ -448,7 +470,7 @@ int decode_attn_mla(const void* q_absorbed, const void* latent_cache, const int3
 
 size_t sparse_mla_attn_workspace(int32_t B, int32_t H, int32_t d_latent, int32_t k, int32_t num_splits) {
   if (B < 1 || H < 64 || H % 64 != 0 || d_latent < 1 || k < 1 || num_splits < 0) return 0;
-  const int splits = plan_mla_splits(B, H, k, num_splits);
+  const int splits = plan_mla(B, H, k, num_splits, true).splits;
   return splits > 0 ? mla_workspace((int64_t)B * H, splits) : 0;
 }
 
@@ -461,7 +483,8 @@ int sparse_mla_attn(const void* q, const void* latent_cache, const int32_t* topk
   if (rc) return rc;
   if (!topk_idx) return fail(DATTN_EINVAL, "sparse_mla_attn: topk_idx is NULL");
   if (k < 1) return fail(DATTN_EINVAL, "sparse_mla_attn: k must be >= 1");
-  const int splits = plan_mla_splits(B, H, k, num_splits);
+  const MlaPlan plan = plan_mla(B, H, k, num_splits, true);
+  const int splits = plan.splits;
   if (splits < 1) return fail(DATTN_EUNSUPPORTED, "sparse_mla_attn: k = %d needs more than %d splits", k,
                               kMlaMaxSplits);
   if ((rc = check_workspace(workspace, workspace_bytes, mla_workspace((int64_t)B * H, splits))))
@@ -473,6 +496,7 @@ int sparse_mla_attn(const void* q, const void* latent_cache, const int32_t* topk
   a.k_sel = k;
   a.B = B;
   a.H = H;
+  a.heads_per_wg = plan.heads_per_wg;
   a.S_max = S_max;
   a.page_size = S_max;
   a.max_pages = 1;

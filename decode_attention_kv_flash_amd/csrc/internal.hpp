@@ -111,13 +111,15 @@ struct MlaArgs {
   float* part_lse;           // [B, H, splits] reference maximum (log2 units)
   float* part_l;             // [B, H, splits] softmax denominators
   int32_t B, H, S_max, page_size, log2_page, max_pages, num_splits;
+  int32_t heads_per_wg;     // 128 (four waves) or 64 (two waves) query heads per workgroup
   float scale_log2;
 };
 
 // Tokens one MLA split may hold (its cache rows are tabled in LDS); the
 // planner picks at least ceil(tokens / kMlaMaxSplitTokens) splits.
 constexpr int kMlaMaxSplitTokens = 3840;
-// 128 query heads per workgroup when H allows it, else 64 (H % 64 == 0).
+// 128 query heads per workgroup when H allows it, else 64 (H % 64 == 0); a
+// call may take 64 when H allows 128 (MlaArgs::heads_per_wg).
 int mla_heads_per_workgroup(int H);
 hipError_t launch_mla(const MlaArgs& a, hipStream_t s);
 

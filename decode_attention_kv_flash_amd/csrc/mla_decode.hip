@@ -474,7 +474,9 @@ hipError_t launch_nw(const MlaArgs& a, hipStream_t s) {
 int mla_heads_per_workgroup(int H) { return H % 128 == 0 ? 128 : 64; }
 
 hipError_t launch_mla(const MlaArgs& a, hipStream_t s) {
-  return mla_heads_per_workgroup(a.H) == 128 ? launch_nw<4>(a, s) : launch_nw<2>(a, s);
+  if (a.heads_per_wg == 128 && a.H % 128 == 0) return launch_nw<4>(a, s);
+  if (a.heads_per_wg == 64 && a.H % 64 == 0) return launch_nw<2>(a, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace dattn
