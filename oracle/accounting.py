@@ -35,11 +35,16 @@ def attention_flops(S: int, n_heads: int, d_head: int) -> int:
 
 
 def attention_linear_crossover(params: float, n_layers: int, n_heads: int, d_head: int) -> float:
-    """Context length at which attention FLOPs per token equal the linear layers' 2 x params.
+    """Context length S at which one token's attention FLOPs over all layers,
+    n_layers x attention_flops(S, ...), equal the linear layers' 2 x params.
 
     "Long context, KV eviction and sparse attention", "The cost of long context".
+    attention_flops is linear in S, so S = 2 params / (n_layers x the FLOPs of
+    one attended token); the page's printed crossovers (~38K, ~54K) therefore
+    pin attention_flops as well.
     """
-    return 2 * params / (4 * n_layers * n_heads * d_head)
+    per_attended_token = n_layers * attention_flops(1, n_heads, d_head)
+    return 2 * params / per_attended_token
 
 
 def mla_kv_up_projection_bytes(d_latent: int, n_heads: int, d_nope: int, d_v: int,

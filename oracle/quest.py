@@ -18,8 +18,10 @@ summary, the top pages by it, attention over those only):
      chosen pages and the partial page, two passes in fp64.
 
 Everything is fp64 (exact for the integer-valued inputs the tests use, so
-the choice of pages is exact too).  Parity status: pinned (bound property,
-full budget equals full attention through the C oracle, brute force).
+the choice of pages is exact too).  Parity status: pinned (a hand-worked
+mixed-sign bound in tests/golden/quest_bound_tiny.json, tightness on pages of
+identical keys, the bound holding for every key, full budget equals full
+attention through the C oracle, ties).
 """
 from __future__ import annotations
 

@@ -69,10 +69,31 @@ def test_crossover_and_128k_cache():
         assert round(kv / 1e9, 1) == m["kv_128k_gb"]
 
 
-def test_attention_flops_split():
-    # 4 S n_h d_h: QK^T and PV each 2 S n_h d_h (one multiply-add = 2 FLOP)
-    S, nh, dh = 8192, 32, 128
-    assert acc.attention_flops(S, nh, dh) == 2 * (2 * S * nh * dh)
+def test_attention_flops_counts_a_naive_decode():
+    # brute force: run one decode step with plain loops on tiny sizes and
+    # count each multiply and each add of QK^T and PV (the page counts
+    # those two products, not the softmax)
+    S, nh, dh = 5, 3, 4
+    g = torch.Generator().manual_seed(0)
+    q, k, v = (torch.randn(*shape, generator=g).tolist()
+               for shape in ((nh, dh), (nh, S, dh), (nh, S, dh)))
+    n = 0
+    for h in range(nh):
+        s = []
+        for t in range(S):
+            acc_ = 0.0
+            for d in range(dh):
+                acc_ += q[h][d] * k[h][t][d]
+                n += 2
+            s.append(acc_)
+        m = max(s)
+        p = [math.exp(x - m) for x in s]
+        o = [0.0] * dh
+        for t in range(S):
+            for d in range(dh):
+                o[d] += p[t] * v[h][t][d]
+                n += 2
+    assert acc.attention_flops(S, nh, dh) == n
 
 
 def test_dsa_selected_cache_per_layer():
@@ -166,6 +187,15 @@ def test_sink_on_empty_sequence():
     assert lse.tolist() == [-1.5, 2.0]
 
 
+def test_very_negative_sink_equals_no_sink():
+    # e^{sink} with sink = -1e4 underflows to zero next to any score here, so
+    # the extra denominator term vanishes and the result is plain attention
+    x = wl.make_gqa(B=2, Hq=4, Hkv=2, D=16, seq_lens=[1, 37], dtype=torch.float32, paged=False, seed=19)
+    out, lse = oracle.gqa(x.q, x.k, x.v, x.seq_lens, sink_logits=[-1e4] * 4)
+    want, wlse = oracle.gqa(x.q, x.k, x.v, x.seq_lens)
+    assert torch.equal(out, want) and torch.equal(lse, wlse)
+
+
 def _sdpa_with_sink_token(q, k, v, scale, L, sink, keep=None):
     """Library attention over the cache plus one token whose key and value are
     zero vectors and whose logit is raised by the head's sink (an additive
@@ -256,6 +286,38 @@ def test_quest_bound_holds_for_every_key():
             best = s.view(-1, 16).amax(1)
             assert torch.all(best <= up[b, h, : L // 16] + 1e-12)
             assert torch.all(torch.isinf(up[b, h, L // 16:]))
+
+
+def test_quest_bound_hand_worked_example():
+    # the page's bound on a mixed-sign query, worked by hand in the fixture;
+    # a looser valid bound (sum |q| max(|kmin|, |kmax|)) or a sign slip
+    # changes both values and the page chosen at budget 1
+    from oracle import quest
+    g = gold("quest_bound_tiny.json")
+    pages = torch.tensor(g["pages"], dtype=torch.float64)        # [2, 16, 4]
+    k = pages.reshape(1, 1, 32, 4)
+    q = torch.tensor(g["q"], dtype=torch.float64).reshape(1, 1, 4)
+    kmin, kmax = quest.page_minmax(k, [32])
+    assert kmin[0, 0].tolist() == g["kmin"] and kmax[0, 0].tolist() == g["kmax"]
+    up = quest.upper_bounds(q, kmin, kmax, [32], 1)
+    assert up[0, 0].tolist() == g["upper"]
+    assert quest.choose(up, [32], 1) == [g["chosen_budget_1"]]
+
+
+def test_quest_bound_is_tight_on_identical_keys():
+    # a page whose 16 keys are one vector k has kmin = kmax = k, and the
+    # bound must then be exactly q . k, for queries and keys of any sign
+    from oracle import quest
+    g = torch.Generator().manual_seed(75)
+    D = 8
+    k = torch.randint(-4, 5, (1, 1, 3, D), generator=g).double()
+    k = k.repeat_interleave(16, dim=2)                              # 3 pages of identical keys
+    q = torch.randint(-4, 5, (1, 2, D), generator=g).double()
+    kmin, kmax = quest.page_minmax(k, [48])
+    up = quest.upper_bounds(q, kmin, kmax, [48], 2)
+    for h in range(2):
+        for p in range(3):
+            assert up[0, h, p].item() == float(k[0, 0, 16 * p] @ q[0, h])
 
 
 def test_quest_full_budget_equals_full_attention():
