@@ -28,7 +28,7 @@ EXPORTS = (
     "sparse_mla_attn", "sparse_mla_attn_workspace",
     "kv_append_gqa", "kv_append_rows",
     "quest_page_minmax", "decode_attn_quest", "decode_attn_quest_workspace",
-    "dattn_last_error", "dattn_version",
+    "dattn_last_error", "dattn_version", "dattn_debug_enable", "dattn_check_tables",
     "dattn_profile_enable", "dattn_profile_read", "dattn_profile_reset",
 )
 
@@ -82,6 +82,10 @@ def lib() -> ctypes.CDLL:
     L.dattn_last_error.restype = ctypes.c_char_p
     L.dattn_last_error.argtypes = []
     L.dattn_version.restype = I32
+    L.dattn_debug_enable.argtypes = [I32]
+    L.dattn_debug_enable.restype = ctypes.c_int
+    L.dattn_check_tables.argtypes = [P, P, I32, I32, I32, ctypes.c_int64]
+    L.dattn_check_tables.restype = ctypes.c_int
     L.dattn_profile_enable.argtypes = [I32]
     L.dattn_profile_read.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
                                      ctypes.POINTER(ctypes.c_int64)]
@@ -120,10 +124,21 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _workspace(nbytes: int, device) -> Optional[torch.Tensor]:
+def _empty(shape, dtype, device, stream) -> torch.Tensor:
+    """torch.empty on the stream the call launches on.  The caching allocator
+    ties a block to the stream it was allocated on, so a workspace freed when
+    the binding returns is not handed to other streams' work while this
+    call's kernels may still use it; outputs follow the same rule."""
+    if stream is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    with torch.cuda.stream(stream):
+        return torch.empty(shape, dtype=dtype, device=device)
+
+
+def _workspace(nbytes: int, device, stream) -> Optional[torch.Tensor]:
     if nbytes == 0:
         return None
-    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return _empty((nbytes,), torch.uint8, device, stream)
 
 
 def decode_attn_gqa(q, k_cache, v_cache, seq_lens, page_table=None, window=0, n_sink=0, *,
@@ -148,16 +163,16 @@ def decode_attn_gqa(q, k_cache, v_cache, seq_lens, page_table=None, window=0, n_
     else:
         max_pages = 1
     if out is None:
-        out = torch.empty_like(q)
+        out = _empty(q.shape, q.dtype, q.device, stream)
     if lse is None and want_lse:
-        lse = torch.empty(B, Hq, dtype=torch.float32, device=q.device)
+        lse = _empty((B, Hq), torch.float32, q.device, stream)
     nbytes = lib().decode_attn_gqa_workspace(B, Hq, Hkv, D, page_size, max_pages, int(window),
                                              int(n_sink), int(num_splits))
     if workspace is not None:
         _dev(workspace, "workspace")
         ws, nbytes = workspace, workspace.numel() * workspace.element_size()
     else:
-        ws = _workspace(nbytes, q.device)
+        ws = _workspace(nbytes, q.device, stream)
     if sink_logits is None:
         _check(lib().decode_attn_gqa(
             _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), _ptr(page_table),
@@ -225,7 +240,7 @@ def quest_page_minmax(k_cache, seq_lens, page_table=None, *, kminmax=None, first
         max_pages = page_table.shape[1]
     n_blocks = page_size * max_pages // QUEST_BLOCK
     if kminmax is None:
-        kminmax = torch.empty(B, Hkv, n_blocks, 2, D, dtype=k_cache.dtype, device=k_cache.device)
+        kminmax = _empty((B, Hkv, n_blocks, 2, D), k_cache.dtype, k_cache.device, stream)
     else:
         _dev(kminmax, "kminmax")
         if tuple(kminmax.shape) != (B, Hkv, n_blocks, 2, D) or kminmax.dtype != k_cache.dtype:
@@ -254,10 +269,10 @@ def decode_attn_quest(q, k_cache, v_cache, kminmax, seq_lens, budget, page_table
     if kminmax.dtype != k_cache.dtype or kminmax.shape[:2] != (B, Hkv):
         raise ValueError("kminmax must come from quest_page_minmax on this cache")
     if out is None:
-        out = torch.empty_like(q)
+        out = _empty(q.shape, q.dtype, q.device, stream)
     if lse is None and want_lse:
-        lse = torch.empty(B, Hq, dtype=torch.float32, device=q.device)
-    sel = torch.empty(B, Hq, int(budget), dtype=torch.int32, device=q.device) if want_selected else None
+        lse = _empty((B, Hq), torch.float32, q.device, stream)
+    sel = _empty((B, Hq, int(budget)), torch.int32, q.device, stream) if want_selected else None
     dt = _dtype_code(q)
     nbytes = lib().decode_attn_quest_workspace(B, Hq, Hkv, D, page_size, max_pages, int(budget), dt,
                                                int(num_splits))
@@ -265,7 +280,7 @@ def decode_attn_quest(q, k_cache, v_cache, kminmax, seq_lens, budget, page_table
         _dev(workspace, "workspace")
         ws, nbytes = workspace, workspace.numel() * workspace.element_size()
     else:
-        ws = _workspace(nbytes, q.device)
+        ws = _workspace(nbytes, q.device, stream)
     _check(lib().decode_attn_quest(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kminmax), _ptr(seq_lens), _ptr(page_table),
         int(budget), _ptr(out), _ptr(lse), _ptr(sel), B, Hq, Hkv, D, page_size, max_pages, dt,
@@ -289,15 +304,15 @@ def decode_attn_mla(q_absorbed, latent_cache, seq_lens, page_table=None, *, d_la
     else:
         S_max, page_size, max_pages = latent_cache.shape[1], latent_cache.shape[1], 1
     if out is None:
-        out = torch.empty(B, H, d_latent, dtype=q_absorbed.dtype, device=q_absorbed.device)
+        out = _empty((B, H, d_latent), q_absorbed.dtype, q_absorbed.device, stream)
     if lse is None and want_lse:
-        lse = torch.empty(B, H, dtype=torch.float32, device=q_absorbed.device)
+        lse = _empty((B, H), torch.float32, q_absorbed.device, stream)
     nbytes = lib().decode_attn_mla_workspace(B, H, d_latent, S_max, int(num_splits))
     if workspace is not None:
         _dev(workspace, "workspace")
         ws, nbytes = workspace, workspace.numel() * workspace.element_size()
     else:
-        ws = _workspace(nbytes, q_absorbed.device)
+        ws = _workspace(nbytes, q_absorbed.device, stream)
     _check(lib().decode_attn_mla(
         _ptr(q_absorbed), _ptr(latent_cache), _ptr(seq_lens), _ptr(page_table), _ptr(out),
         _ptr(lse), B, H, d_latent, d_rope, S_max, page_size, max_pages, _dtype_code(q_absorbed),
@@ -317,14 +332,14 @@ def dsa_indexer_topk(q_i, w, k_i_cache, seq_lens, k, *, topk_idx=None, return_sc
     if q_i.dtype != k_i_cache.dtype:
         raise ValueError("q_i and k_i_cache must have one dtype")
     if topk_idx is None:
-        topk_idx = torch.empty(B, k, dtype=torch.int32, device=q_i.device)
-    scores = torch.empty(B, S_max, dtype=torch.float32, device=q_i.device) if return_scores else None
+        topk_idx = _empty((B, k), torch.int32, q_i.device, stream)
+    scores = _empty((B, S_max), torch.float32, q_i.device, stream) if return_scores else None
     nbytes = lib().dsa_indexer_topk_workspace(B, S_max, k)
     if workspace is not None:
         _dev(workspace, "workspace")
         ws, nbytes = workspace, workspace.numel() * workspace.element_size()
     else:
-        ws = _workspace(nbytes, q_i.device)
+        ws = _workspace(nbytes, q_i.device, stream)
     _check(lib().dsa_indexer_topk(
         _ptr(q_i), _ptr(w), _ptr(k_i_cache), _ptr(seq_lens), int(k), _ptr(topk_idx), _ptr(scores),
         B, Hi, Di, S_max, _dtype_code(q_i), _ptr(ws), nbytes, _stream(stream)))
@@ -339,13 +354,13 @@ def dsa_topk(scores, seq_lens, k, *, topk_idx=None, workspace=None, stream=None)
         raise ValueError("scores must be fp32")
     B, S_max = scores.shape
     if topk_idx is None:
-        topk_idx = torch.empty(B, k, dtype=torch.int32, device=scores.device)
+        topk_idx = _empty((B, k), torch.int32, scores.device, stream)
     nbytes = lib().dsa_topk_workspace(B, S_max, k)
     if workspace is not None:
         _dev(workspace, "workspace")
         ws, nbytes = workspace, workspace.numel() * workspace.element_size()
     else:
-        ws = _workspace(nbytes, scores.device)
+        ws = _workspace(nbytes, scores.device, stream)
     _check(lib().dsa_topk(_ptr(scores), _ptr(seq_lens), int(k), _ptr(topk_idx), B, S_max,
                           _ptr(ws), nbytes, _stream(stream)))
     return topk_idx
@@ -360,20 +375,27 @@ def sparse_mla_attn(q, latent_cache, topk_idx, *, d_latent=512, scale=None, num_
     S_max = latent_cache.shape[1]
     k = topk_idx.shape[1]
     if out is None:
-        out = torch.empty(B, H, d_latent, dtype=q.dtype, device=q.device)
+        out = _empty((B, H, d_latent), q.dtype, q.device, stream)
     if lse is None and want_lse:
-        lse = torch.empty(B, H, dtype=torch.float32, device=q.device)
+        lse = _empty((B, H), torch.float32, q.device, stream)
     nbytes = lib().sparse_mla_attn_workspace(B, H, d_latent, k, int(num_splits))
     if workspace is not None:
         _dev(workspace, "workspace")
         ws, nbytes = workspace, workspace.numel() * workspace.element_size()
     else:
-        ws = _workspace(nbytes, q.device)
+        ws = _workspace(nbytes, q.device, stream)
     _check(lib().sparse_mla_attn(
         _ptr(q), _ptr(latent_cache), _ptr(topk_idx), k, _ptr(out), _ptr(lse), B, H, d_latent,
         Dq - d_latent, S_max, _dtype_code(q), float(scale or 0.0), int(num_splits), _ptr(ws),
         nbytes, _stream(stream)))
     return out, lse
+
+
+# ---- debug checking of the device-resident tables ---------------------------
+
+def debug_enable(on: bool = True):
+    """Check seq_lens / page_table on the host before each launch (synchronous)."""
+    _check(lib().dattn_debug_enable(1 if on else 0))
 
 
 # ---- per-kernel timing (HIP events recorded inside the library) -------------

@@ -9,6 +9,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -239,6 +240,85 @@ int check_workspace(void* ws, size_t have, size_t need) {
   return DATTN_OK;
 }
 
+// ------------------------------------------------------------ debug checks
+// DATTN_DEBUG=1 in the environment (or dattn_debug_enable(1)) makes the
+// entry points copy the device-resident seq_lens and page_table to the host,
+// synchronously on the call's stream, and check them against the layout
+// contract before launching; a violation returns DATTN_EINVAL naming the
+// first bad entry.  Off by default: it synchronises, so it does not suit
+// stream capture or latency-sensitive loops.
+std::atomic<int> g_debug{-1};  // -1: not read from the environment yet
+
+bool debug_on() {
+  int d = g_debug.load(std::memory_order_relaxed);
+  if (d < 0) {
+    const char* e = getenv("DATTN_DEBUG");
+    d = (e && *e && strcmp(e, "0") != 0) ? 1 : 0;
+    int expect = -1;
+    g_debug.compare_exchange_strong(expect, d);
+    d = g_debug.load(std::memory_order_relaxed);
+  }
+  return d > 0;
+}
+
+// The table contract on host copies (see dattn_check_tables in dattn.h).
+int check_tables_host(const char* fn, const int32_t* lens, const int32_t* pt, int32_t B,
+                      int32_t page_size, int32_t max_pages, int64_t num_pages) {
+  const int64_t cap = (int64_t)page_size * (pt ? max_pages : 1);
+  for (int32_t b = 0; b < B; ++b) {
+    const int64_t L = lens[b];
+    if (L < 0 || L > cap)
+      return fail(DATTN_EINVAL, "%s: seq_lens[%d] = %lld outside [0, %lld]", fn, b, (long long)L,
+                  (long long)cap);
+    if (!pt) continue;
+    const int64_t used = (L + page_size - 1) / page_size;
+    for (int64_t j = 0; j < used; ++j) {
+      const int64_t e = pt[(int64_t)b * max_pages + j];
+      if (e < 0 || (num_pages >= 0 && e >= num_pages))
+        return fail(DATTN_EINVAL, "%s: page_table[%d][%lld] = %lld names no page of the cache (%lld pages)",
+                    fn, b, (long long)j, (long long)e, (long long)num_pages);
+    }
+  }
+  return DATTN_OK;
+}
+
+// Whole pages of page_bytes from p to the end of its device allocation, or
+// -1 when the allocation cannot be queried.
+int64_t pages_in_allocation(const void* p, int64_t page_bytes) {
+  hipDeviceptr_t base = nullptr;
+  size_t size = 0;
+  if (!p || page_bytes <= 0 || hipMemGetAddressRange(&base, &size, (hipDeviceptr_t)p) != hipSuccess) {
+    (void)hipGetLastError();
+    return -1;
+  }
+  const int64_t left = (int64_t)((const char*)base + size - (const char*)p);
+  return left < 0 ? 0 : left / page_bytes;
+}
+
+// Copies the tables to the host on stream s and checks them.  caches: the
+// device buffers the table indexes, each holding pages of page_bytes.
+int debug_check(const char* fn, const int32_t* d_lens, const int32_t* d_pt, int32_t B,
+                int32_t page_size, int32_t max_pages, const void* const* caches, int n_caches,
+                int64_t page_bytes, hipStream_t s) {
+  std::vector<int32_t> lens(B), pt;
+  hipError_t e = hipMemcpyAsync(lens.data(), d_lens, sizeof(int32_t) * B, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess && d_pt) {
+    pt.resize((size_t)B * max_pages);
+    e = hipMemcpyAsync(pt.data(), d_pt, sizeof(int32_t) * pt.size(), hipMemcpyDeviceToHost, s);
+  }
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  int64_t num_pages = -1;
+  if (d_pt) {
+    for (int i = 0; i < n_caches; ++i) {
+      const int64_t n = pages_in_allocation(caches[i], page_bytes);
+      if (n >= 0 && (num_pages < 0 || n < num_pages)) num_pages = n;
+    }
+  }
+  return check_tables_host(fn, lens.data(), d_pt ? pt.data() : nullptr, B, page_size, max_pages,
+                           num_pages);
+}
+
 int validate_gqa(const void* q, const void* k, const void* v, const int32_t* seq_lens,
                  const int32_t* page_table, int32_t n_sink, const void* out, int32_t B,
                  int32_t Hq, int32_t Hkv, int32_t D, int32_t page_size, int32_t max_pages,
@@ -292,6 +372,21 @@ extern "C" {
 const char* dattn_last_error(void) { return g_err.c_str(); }
 
 int32_t dattn_version(void) { return 1; }
+
+int dattn_debug_enable(int32_t on) {
+  g_debug.store(on ? 1 : 0, std::memory_order_relaxed);
+  return ok();
+}
+
+int dattn_check_tables(const int32_t* seq_lens, const int32_t* page_table, int32_t B,
+                       int32_t page_size, int32_t max_pages, int64_t num_pages) {
+  if (!seq_lens) return fail(DATTN_EINVAL, "dattn_check_tables: seq_lens is NULL");
+  if (B < 1 || page_size < 1) return fail(DATTN_EINVAL, "dattn_check_tables: B and page_size must be >= 1");
+  if (page_table && max_pages < 1) return fail(DATTN_EINVAL, "dattn_check_tables: max_pages must be >= 1");
+  const int rc = check_tables_host("dattn_check_tables", seq_lens, page_table, B, page_size, max_pages,
+                                   num_pages);
+  return rc ? rc : ok();
+}
 
 int dattn_profile_enable(int32_t on) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
@@ -367,6 +462,13 @@ int decode_attn_gqa_sink(const void* q, const void* k_cache, const void* v_cache
       num_splits > 0 ? 0 : gqa_slots(dtype == DATTN_BF16, D, Hq / Hkv, paged, page_size));
   const size_t need = split_workspace((int64_t)B * Hq, splits, D);
   if ((rc = check_workspace(workspace, workspace_bytes, need))) return rc;
+  if (debug_on()) {
+    const void* caches[] = {k_cache, v_cache};
+    const int64_t pb = (int64_t)Hkv * page_size * D * (dtype == DATTN_BF16 ? 2 : 4);
+    if ((rc = debug_check("decode_attn_gqa", seq_lens, page_table, B, page_size, paged ? max_pages : 1,
+                          caches, 2, pb, (hipStream_t)stream)))
+      return rc;
+  }
 
   dattn::GqaArgs a{};
   a.q = q;
@@ -443,14 +545,25 @@ int decode_attn_mla(const void* q_absorbed, const void* latent_cache, const int3
   if (page_table) {
     if (!pow2(page_size)) return fail(DATTN_EUNSUPPORTED, "decode_attn_mla: paged cache needs a power-of-two page_size");
     if (max_pages < 1) return fail(DATTN_EINVAL, "decode_attn_mla: max_pages must be >= 1");
+    // decode_attn_mla_workspace plans from S_max: both must see one capacity
+    if ((int64_t)page_size * max_pages != S_max)
+      return fail(DATTN_EINVAL, "decode_attn_mla: paged S_max (%d) must equal page_size * max_pages (%lld)",
+                  S_max, (long long)page_size * max_pages);
   }
-  const int64_t max_tokens = page_table ? (int64_t)page_size * max_pages : S_max;
+  const int64_t max_tokens = S_max;
   const MlaPlan plan = plan_mla(B, H, max_tokens, num_splits, false);
   const int splits = plan.splits;
   if (splits < 1) return fail(DATTN_EUNSUPPORTED, "decode_attn_mla: %lld tokens need more than %d splits",
                               (long long)max_tokens, kMlaMaxSplits);
   if ((rc = check_workspace(workspace, workspace_bytes, mla_workspace((int64_t)B * H, splits))))
     return rc;
+  if (debug_on()) {
+    const void* caches[] = {latent_cache};
+    const int64_t pb = (int64_t)page_size * (d_latent + d_rope) * 2;
+    if ((rc = debug_check("decode_attn_mla", seq_lens, page_table, B, page_table ? page_size : S_max,
+                          page_table ? max_pages : 1, caches, 1, pb, (hipStream_t)stream)))
+      return rc;
+  }
   dattn::MlaArgs a{};
   a.q = (const uint16_t*)q_absorbed;
   a.latent = (const uint16_t*)latent_cache;
@@ -554,6 +667,9 @@ int dsa_indexer_topk(const void* q_i, const float* w, const void* k_i_cache, con
     return fail(DATTN_EINVAL, "dsa_indexer_topk: S_max must be <= %d", kTopkMaxRow);
   int rc = check_workspace(workspace, workspace_bytes, dsa_indexer_topk_workspace(B, S_max, k));
   if (rc) return rc;
+  if (debug_on() && (rc = debug_check("dsa_indexer_topk", seq_lens, nullptr, B, S_max, 1, nullptr, 0, 0,
+                                      (hipStream_t)stream)))
+    return rc;
   float* scores = scores_out ? scores_out : (float*)workspace;
   uint32_t* topk_ws = (uint32_t*)((char*)workspace + align256((size_t)B * S_max * sizeof(float)));
   hipStream_t s = (hipStream_t)stream;
@@ -708,6 +824,13 @@ int decode_attn_quest(const void* q, const void* k_cache, const void* v_cache, c
   const QuestPlan p = plan_quest(B, Hq, Hkv, D, qa.max_blocks, budget, dtype == DATTN_BF16, num_splits,
                                  selected == nullptr);
   if ((rc = check_workspace(workspace, workspace_bytes, p.total))) return rc;
+  if (debug_on()) {
+    const void* caches[] = {k_cache, v_cache};
+    const int64_t pb = (int64_t)Hkv * page_size * D * (dtype == DATTN_BF16 ? 2 : 4);
+    if ((rc = debug_check("decode_attn_quest", seq_lens, page_table, B, page_size, paged ? max_pages : 1,
+                          caches, 2, pb, (hipStream_t)stream)))
+      return rc;
+  }
   char* ws = (char*)workspace;
   hipStream_t s = (hipStream_t)stream;
   int32_t* sel = selected ? selected : (int32_t*)(ws + p.sel);

@@ -263,7 +263,9 @@ __global__ __launch_bounds__(kThreads, (gqa_double_buffer<BF16, G>() ? 2 : 3)) v
   // Token set [0, s_cnt) u [w_start, L) as 16-token blocks: sink blocks
   // first, then the window's blocks (aligned down to 16).  LISTED: the
   // listed blocks, then the partial last block.
-  const int L = a.seq_lens[b];
+  // seq_lens is a caller contract; clamping keeps an out-of-contract length
+  // inside the sequence's row of the page table (and the cache)
+  const int L = (int)min((int64_t)max(a.seq_lens[b], 0), (int64_t)a.page_size * a.max_pages);
   int s_cnt = 0, w_start = 0;
   if (!LISTED && a.window > 0 && a.window < L) {
     w_start = L - a.window;

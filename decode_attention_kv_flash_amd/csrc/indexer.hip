@@ -90,7 +90,7 @@ __global__ __launch_bounds__(kThreads) void indexer_kernel(const IndexerArgs a) 
   const int half = lane >> 5;
   const int lj = lane & 31;
   const int b = blockIdx.y;
-  const int L = a.seq_lens[b];
+  const int L = min(max(a.seq_lens[b], 0), a.S_max);  // a caller contract, clamped to the cache
   const int Hi = 32 * NMT;
 
   // A fragments (heads x dims): lane holds head 32*mt + lj

@@ -383,6 +383,31 @@ DATTN_EXPORT const char* dattn_last_error(void);
 /* ABI version of this library. */
 DATTN_EXPORT int32_t dattn_version(void);
 
+/* Debug checking of the device-resident tables.
+ *
+ * The kernel must follow the block table ("All the attentions", section 8,
+ * PagedAttention): a page table or a length outside the contract makes it
+ * read outside the cache.  The tables stay on the device and are trusted by
+ * default.  With DATTN_DEBUG=1 in the environment, or after
+ * dattn_debug_enable(1), decode_attn_gqa(_sink), decode_attn_quest,
+ * decode_attn_mla and dsa_indexer_topk first copy seq_lens (and page_table)
+ * to the host, synchronously on their stream, and check them as
+ * dattn_check_tables does (num_pages taken from the size of the cache's
+ * device allocation); a violation returns DATTN_EINVAL, names the first bad
+ * entry and launches nothing.  The copy synchronises the stream, so this
+ * mode does not suit stream capture.
+ *
+ * dattn_check_tables: the same check on HOST arrays.
+ *   seq_lens    host int32 [B]: each 0 <= L_b <= page_size * max_pages
+ *               (contiguous: page_table NULL, page_size = S_max)
+ *   page_table  host int32 [B, max_pages] or NULL: the entries of the pages
+ *               that hold tokens, j < ceil(L_b / page_size), must lie in
+ *               [0, num_pages); num_pages < 0 checks only that they are >= 0
+ * Returns DATTN_OK or DATTN_EINVAL (message in dattn_last_error). */
+DATTN_EXPORT int dattn_debug_enable(int32_t on);
+DATTN_EXPORT int dattn_check_tables(const int32_t* seq_lens, const int32_t* page_table, int32_t B,
+                                    int32_t page_size, int32_t max_pages, int64_t num_pages);
+
 /* Per-kernel timing.  While enabled, every kernel the library launches is
  * bracketed by HIP events recorded on the launch stream.  dattn_profile_read
  * waits for the recorded events and reports, for kernels whose name contains

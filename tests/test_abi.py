@@ -100,6 +100,11 @@ def test_mla_and_sparse_validation():
     rc = L.decode_attn_mla(P(256), P(256), P(256), None, P(256), None, 2, 96, 512, 64, 100, 100, 1, 1,
                            0.0, 0, None, 0, None)
     assert rc == -2
+    # paged: S_max must be the capacity page_size * max_pages, the quantity
+    # decode_attn_mla_workspace plans from
+    rc = L.decode_attn_mla(P(256), P(256), P(256), P(256), P(256), None, 2, 128, 512, 64, 100, 16, 8, 1,
+                           0.0, 0, P(256), 1 << 30, None)
+    assert rc == -1 and b"page_size * max_pages" in L.dattn_last_error()
     # sparse: k must be >= 1 and idx non-null
     rc = L.sparse_mla_attn(P(256), P(256), None, 16, P(256), None, 2, 128, 512, 64, 100, 1, 0.0, 0,
                            None, 0, None)
@@ -234,3 +239,45 @@ def test_quest_workspace_sizes():
     assert one >= 16 * 64 * 4 + 16 * 4 + 16 * 8 * 4
     assert more - one == 16 * 4 * 128 * 4 + 256    # the split partials (o, then lse aligned)
     assert L.decode_attn_quest_workspace(0, 8, 2, 128, 16, 64, 8, 1, 1) == 0
+
+
+# --------------------------------------------------------------------------
+# debug checking of the device-resident tables, on host arrays
+
+
+def _tables(lens, pt=None):
+    i32 = ctypes.c_int32
+    L = (i32 * len(lens))(*lens)
+    if pt is None:
+        return L, None
+    flat = [e for row in pt for e in row]
+    return L, (i32 * len(flat))(*flat)
+
+
+@pytest.mark.parametrize("lens,pt,page_size,max_pages,num_pages,ok,what", [
+    ([32, 17], [[3, 1], [0, 2]], 16, 2, 4, True, ""),
+    ([32, 0], [[3, 1], [-1, -1]], 16, 2, 4, True, ""),             # an empty sequence uses no page
+    ([17, 16], [[0, 5], [1, -7]], 16, 2, 6, True, ""),             # entries past the length are never read
+    ([33, 16], [[0, 1], [2, 3]], 16, 2, 4, False, "seq_lens[0] = 33"),
+    ([-1, 16], [[0, 1], [2, 3]], 16, 2, 4, False, "seq_lens[0] = -1"),
+    ([32, 17], [[3, 1], [0, 4]], 16, 2, 4, False, "page_table[1][1] = 4"),
+    ([32, 17], [[3, -2], [0, 2]], 16, 2, 4, False, "page_table[0][1] = -2"),
+    ([32, 17], [[3, -2], [0, 2]], 16, 2, -1, False, "page_table[0][1] = -2"),
+    ([32, 17], [[3, 99], [0, 2]], 16, 2, -1, True, ""),            # page count unknown: only >= 0
+    ([256, 100], None, 256, 1, -1, True, ""),                      # contiguous: L <= S_max
+    ([257, 100], None, 256, 1, -1, False, "seq_lens[0] = 257"),
+])
+def test_check_tables(lens, pt, page_size, max_pages, num_pages, ok, what):
+    L = api.lib()
+    sl, tab = _tables(lens, pt)
+    rc = L.dattn_check_tables(sl, tab, len(lens), page_size, max_pages, num_pages)
+    if ok:
+        assert rc == 0, L.dattn_last_error()
+    else:
+        assert rc == -1 and what.encode() in L.dattn_last_error(), L.dattn_last_error()
+
+
+def test_debug_toggle_without_gpu():
+    L = api.lib()
+    assert L.dattn_debug_enable(1) == 0
+    assert L.dattn_debug_enable(0) == 0

@@ -241,6 +241,21 @@ def test_sparse_mla_empty_lists_and_holes(splits):
     assert_lse_close(glse[keep], wlse[keep], 1e-5, "sparse holes")
 
 
+@pytest.mark.parametrize("k_sel", [3840, 3841])
+def test_sparse_mla_split_capacity(k_sel):
+    """One split asked for k_sel listed rows: 3840 fills a split's row table
+    exactly; 3841 is raised to two splits.  A few holes in the list, and the
+    list in descending order (order does not matter to the set)."""
+    m = wl.make_mla(B=2, H=128, seq_lens=[6000, 5000], seed=58, name="sparse_cap")
+    idx = wl.random_topk_indices(B=2, seq_lens=[6000, 5000], k=k_sel, seed=59)
+    idx[0, 7::97] = -1
+    idx[1] = idx[1].flip(0)
+    got, glse = run_sparse(m, idx, 1)
+    want, wlse = oracle.mla(m.q, m.latent, idx=idx, scale=m.scale)
+    assert_rows_close(got, want, TOL_BF16, f"sparse k={k_sel}")
+    assert_lse_close(glse, wlse, 1e-5, f"sparse k={k_sel}")
+
+
 def test_sparse_with_all_tokens_equals_dense():
     m = wl.make_mla(B=2, H=64, seq_lens=[256, 256], seed=54)
     idx = torch.arange(256, dtype=torch.int32).repeat(2, 1)

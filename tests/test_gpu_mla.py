@@ -94,11 +94,22 @@ def test_mla_score_jumps_restart_the_split():
         check(x, splits)
 
 
+# A split holds at most 3840 tokens (120 tiles of 32 in its LDS row table).
+SPLIT_CAP = 3840
+
+
 @pytest.mark.parametrize("H", [64, 128])
-@pytest.mark.parametrize("splits", [0, 1])
-def test_mla_tile_group_and_split_boundaries(H, splits):
-    """Lengths at a 32-token tile, a 96-token group and the 4032-token split
-    capacity (a request for one split is raised to two for 4033 tokens)."""
-    lens = [31, 32, 96, 97, 4032, 4033]
+@pytest.mark.parametrize("lens,splits", [
+    ([31, 32, 96, 97, SPLIT_CAP], 1),   # one split holds exactly the capacity: a full row table
+    ([31, 32, 96, 97, SPLIT_CAP], 0),
+    ([33, SPLIT_CAP + 1], 1),           # one token past it: the request for one split is raised to two
+    ([SPLIT_CAP + 1], 0),
+])
+def test_mla_tile_and_split_capacity_boundaries(H, lens, splits):
+    """Lengths at a 32-token tile and at the split capacity.  S_max is the
+    longest length, so with splits=1 the first case runs one split of
+    exactly 3840 tokens (n_tiles at its maximum) and the third is raised to
+    two splits."""
     x = wl.make_mla(B=len(lens), H=H, seq_lens=lens, seed=46, name=f"mla_bounds_h{H}")
+    assert x.S_max == max(lens)
     check(x, splits)
