@@ -21,7 +21,7 @@ DATTN_F32, DATTN_BF16, DATTN_FP8_E4M3 = 0, 1, 2
 STATUS = {0: "OK", -1: "EINVAL", -2: "EUNSUPPORTED", -3: "EWORKSPACE", -4: "EHIP"}
 
 EXPORTS = (
-    "decode_attn_gqa", "decode_attn_gqa_sink", "decode_attn_gqa_workspace",
+    "decode_attn_gqa", "decode_attn_gqa_sink", "decode_attn_gqa_workspace", "decode_attn_gqa_noalloc",
     "decode_attn_mla", "decode_attn_mla_workspace",
     "dsa_indexer_topk", "dsa_indexer_topk_workspace",
     "dsa_topk", "dsa_topk_workspace",
@@ -56,6 +56,8 @@ def lib() -> ctypes.CDLL:
     L.decode_attn_gqa_sink.argtypes = [P, P, P, P, P, I32, I32, P, P, P, I32, I32, I32, I32, I32,
                                        I32, I32, F, I32, P, SZ, P]
     L.decode_attn_gqa_workspace.argtypes = [I32] * 9
+    L.decode_attn_gqa_noalloc.argtypes = [P, P, P, P, P, I32, I32, P, P, P, I32, I32, I32, I32, I32,
+                                          I32, I32, F, I32, P]
     L.kv_append_gqa.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, I32, P]
     L.kv_append_rows.argtypes = [P, P, P, P, I32, I32, I32, I32, I32, P]
     L.quest_page_minmax.argtypes = [P, P, P, P, I32, I32, I32, I32, I32, I32, I32, P]
@@ -74,7 +76,7 @@ def lib() -> ctypes.CDLL:
     for name in ("decode_attn_gqa_workspace", "decode_attn_mla_workspace", "decode_attn_quest_workspace",
                  "dsa_indexer_topk_workspace", "dsa_topk_workspace", "sparse_mla_attn_workspace"):
         getattr(L, name).restype = SZ
-    for name in ("decode_attn_gqa", "decode_attn_gqa_sink", "decode_attn_mla", "dsa_indexer_topk", "dsa_topk",
+    for name in ("decode_attn_gqa", "decode_attn_gqa_sink", "decode_attn_gqa_noalloc", "decode_attn_mla", "dsa_indexer_topk", "dsa_topk",
                  "kv_append_gqa", "kv_append_rows", "quest_page_minmax", "decode_attn_quest",
                  "sparse_mla_attn", "dattn_profile_enable", "dattn_profile_read",
                  "dattn_profile_reset"):
@@ -184,6 +186,34 @@ def decode_attn_gqa(q, k_cache, v_cache, seq_lens, page_table=None, window=0, n_
             int(window), int(n_sink), _ptr(sink_logits.contiguous()), _ptr(out), _ptr(lse), B, Hq,
             Hkv, D, page_size, max_pages, _dtype_code(q), float(scale or 0.0), int(num_splits),
             _ptr(ws), nbytes, _stream(stream)))
+    return out, lse
+
+
+def decode_attn_gqa_noalloc(q, k_cache, v_cache, seq_lens, page_table=None, window=0, n_sink=0, *,
+                            out, lse=None, scale=None, num_splits=0, stream=None, sink_logits=None):
+    """decode_attn_gqa whose split partials live in the library's own device
+    array: the caller passes every output (out, and lse or None) and nothing
+    is allocated.  Calls that overlap on one GPU race (one shared array)."""
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (seq_lens, "seq_lens"), (out, "out")):
+        _dev(t, n)
+    if lse is not None:
+        _dev(lse, "lse")
+    if sink_logits is not None:
+        _dev(sink_logits, "sink_logits")
+        if sink_logits.dtype != torch.float32 or sink_logits.shape != (q.shape[1],):
+            raise ValueError("sink_logits must be fp32 [Hq]")
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q's shape and dtype")
+    B, Hq, D = q.shape
+    Hkv, page_size = k_cache.shape[1], k_cache.shape[2]
+    max_pages = 1
+    if page_table is not None:
+        _dev(page_table, "page_table")
+        max_pages = page_table.shape[1]
+    _check(lib().decode_attn_gqa_noalloc(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), _ptr(page_table), int(window), int(n_sink),
+        _ptr(sink_logits), _ptr(out), _ptr(lse), B, Hq, Hkv, D, page_size, max_pages, _dtype_code(q),
+        float(scale or 0.0), int(num_splits), _stream(stream)))
     return out, lse
 
 

@@ -365,6 +365,102 @@ int validate_mla_common(const char* fn, const void* q, const void* latent, const
   return DATTN_OK;
 }
 
+// ---------------------------------------------------- allocation-free scratch
+// Device memory of decode_attn_gqa_noalloc: the split partials live in this
+// file-scope array instead of a caller workspace.  Each GPU the library runs
+// on holds its own copy until the process ends.  In host code the name is
+// only a stand-in: kernels get the address hipGetSymbolAddress returns for
+// the current device, looked up once per device.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+int scratch_address(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "decode_attn_gqa_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(DATTN_EUNSUPPORTED, "decode_attn_gqa_noalloc: device %d", dev);
+  std::lock_guard<std::mutex> lk(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return hip_fail(e, "decode_attn_gqa_noalloc: hipGetSymbolAddress");
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return DATTN_OK;
+}
+
+// Steps a1-a5 (and the sink logit of N2) for decode_attn_gqa(_sink) and, with
+// from_scratch, for decode_attn_gqa_noalloc: workspace is then the scratch
+// array (kScratchBytes); an automatic split count is lowered until its
+// partials fit, a requested one that does not fit is refused.
+int run_gqa(const char* fn, const void* q, const void* k_cache, const void* v_cache, const int32_t* seq_lens,
+            const int32_t* page_table, int32_t window, int32_t n_sink, const float* sink_logits, void* out,
+            float* lse, int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t page_size, int32_t max_pages,
+            int32_t dtype, float scale, int32_t num_splits, void* workspace, size_t workspace_bytes,
+            hipStream_t s, bool from_scratch) {
+  int rc = validate_gqa(q, k_cache, v_cache, seq_lens, page_table, n_sink, out, B, Hq, Hkv, D,
+                        page_size, max_pages, dtype, scale, num_splits);
+  if (rc) return rc;
+  const bool paged = page_table != nullptr;
+  int splits = plan_gqa_splits(
+      B, Hkv, gqa_max_tokens(page_size, paged ? max_pages : 1, window, n_sink), num_splits,
+      num_splits > 0 ? 0 : gqa_slots(dtype == DATTN_BF16, D, Hq / Hkv, paged, page_size));
+  size_t need = split_workspace((int64_t)B * Hq, splits, D);
+  if (from_scratch && need > workspace_bytes) {
+    if (num_splits > 0)
+      return fail(DATTN_EWORKSPACE, "%s: %d splits need %zu bytes of partials, above the %zu-byte scratch", fn,
+                  splits, need, workspace_bytes);
+    while (splits > 1 && split_workspace((int64_t)B * Hq, splits, D) > workspace_bytes) --splits;
+    need = split_workspace((int64_t)B * Hq, splits, D);
+  }
+  if ((rc = check_workspace(workspace, workspace_bytes, need))) return rc;
+  if (debug_on()) {
+    const void* caches[] = {k_cache, v_cache};
+    const int64_t pb = (int64_t)Hkv * page_size * D * (dtype == DATTN_BF16 ? 2 : 4);
+    if ((rc = debug_check(fn, seq_lens, page_table, B, page_size, paged ? max_pages : 1, caches, 2, pb, s)))
+      return rc;
+  }
+
+  dattn::GqaArgs a{};
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.seq_lens = seq_lens;
+  a.page_table = page_table;
+  a.window = window;
+  a.n_sink = n_sink;
+  a.out = out;
+  a.lse = lse;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.D = D;
+  a.G = Hq / Hkv;
+  a.page_size = page_size;
+  a.log2_page = paged ? ilog2(page_size) : 0;
+  a.max_pages = paged ? max_pages : 1;
+  a.num_splits = splits;
+  a.bf16 = dtype == DATTN_BF16;
+  const float sc = scale > 0.f ? scale : 1.0f / std::sqrt((float)D);
+  a.scale_log2 = sc * 1.4426950408889634f;
+  a.sink = sink_logits;
+  if (splits > 1) {
+    a.part_o = (float*)workspace;
+    a.part_lse = (float*)((char*)workspace + align256((size_t)B * Hq * splits * D * sizeof(float)));
+  }
+  if ((rc = launch("gqa_split", s, [&] { return dattn::launch_gqa(a, s); }))) return rc;
+  if (splits > 1) {
+    dattn::CombineArgs c{a.part_o, a.part_lse, nullptr, out, lse, B * Hq, splits, D, a.bf16,
+                         sink_logits, Hq};
+    if ((rc = launch("lse_combine", s, [&] { return dattn::launch_combine(c, s); }))) return rc;
+  }
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -453,58 +549,22 @@ int decode_attn_gqa_sink(const void* q, const void* k_cache, const void* v_cache
                          int32_t Hq, int32_t Hkv, int32_t D, int32_t page_size, int32_t max_pages,
                          int32_t dtype, float scale, int32_t num_splits, void* workspace,
                          size_t workspace_bytes, void* stream) {
-  int rc = validate_gqa(q, k_cache, v_cache, seq_lens, page_table, n_sink, out, B, Hq, Hkv, D,
-                        page_size, max_pages, dtype, scale, num_splits);
-  if (rc) return rc;
-  const bool paged = page_table != nullptr;
-  const int splits = plan_gqa_splits(
-      B, Hkv, gqa_max_tokens(page_size, paged ? max_pages : 1, window, n_sink), num_splits,
-      num_splits > 0 ? 0 : gqa_slots(dtype == DATTN_BF16, D, Hq / Hkv, paged, page_size));
-  const size_t need = split_workspace((int64_t)B * Hq, splits, D);
-  if ((rc = check_workspace(workspace, workspace_bytes, need))) return rc;
-  if (debug_on()) {
-    const void* caches[] = {k_cache, v_cache};
-    const int64_t pb = (int64_t)Hkv * page_size * D * (dtype == DATTN_BF16 ? 2 : 4);
-    if ((rc = debug_check("decode_attn_gqa", seq_lens, page_table, B, page_size, paged ? max_pages : 1,
-                          caches, 2, pb, (hipStream_t)stream)))
-      return rc;
-  }
+  return run_gqa("decode_attn_gqa", q, k_cache, v_cache, seq_lens, page_table, window, n_sink, sink_logits,
+                 out, lse, B, Hq, Hkv, D, page_size, max_pages, dtype, scale, num_splits, workspace,
+                 workspace_bytes, (hipStream_t)stream, false);
+}
 
-  dattn::GqaArgs a{};
-  a.q = q;
-  a.k = k_cache;
-  a.v = v_cache;
-  a.seq_lens = seq_lens;
-  a.page_table = page_table;
-  a.window = window;
-  a.n_sink = n_sink;
-  a.out = out;
-  a.lse = lse;
-  a.B = B;
-  a.Hq = Hq;
-  a.Hkv = Hkv;
-  a.D = D;
-  a.G = Hq / Hkv;
-  a.page_size = page_size;
-  a.log2_page = paged ? ilog2(page_size) : 0;
-  a.max_pages = paged ? max_pages : 1;
-  a.num_splits = splits;
-  a.bf16 = dtype == DATTN_BF16;
-  const float sc = scale > 0.f ? scale : 1.0f / std::sqrt((float)D);
-  a.scale_log2 = sc * 1.4426950408889634f;
-  a.sink = sink_logits;
-  if (splits > 1) {
-    a.part_o = (float*)workspace;
-    a.part_lse = (float*)((char*)workspace + align256((size_t)B * Hq * splits * D * sizeof(float)));
-  }
-  hipStream_t s = (hipStream_t)stream;
-  if ((rc = launch("gqa_split", s, [&] { return dattn::launch_gqa(a, s); }))) return rc;
-  if (splits > 1) {
-    dattn::CombineArgs c{a.part_o, a.part_lse, nullptr, out, lse, B * Hq, splits, D, a.bf16,
-                         sink_logits, Hq};
-    if ((rc = launch("lse_combine", s, [&] { return dattn::launch_combine(c, s); }))) return rc;
-  }
-  return ok();
+int decode_attn_gqa_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* seq_lens, const int32_t* page_table, int32_t window,
+                            int32_t n_sink, const float* sink_logits, void* out, float* lse, int32_t B,
+                            int32_t Hq, int32_t Hkv, int32_t D, int32_t page_size, int32_t max_pages,
+                            int32_t dtype, float scale, int32_t num_splits, void* stream) {
+  void* ws = nullptr;
+  const int rc = scratch_address(&ws);
+  if (rc) return rc;
+  return run_gqa("decode_attn_gqa_noalloc", q, k_cache, v_cache, seq_lens, page_table, window, n_sink,
+                 sink_logits, out, lse, B, Hq, Hkv, D, page_size, max_pages, dtype, scale, num_splits, ws,
+                 kScratchBytes, (hipStream_t)stream, true);
 }
 
 // ------------------------------------------------------------------- MLA

@@ -137,6 +137,31 @@ DATTN_EXPORT size_t decode_attn_gqa_workspace(int32_t B, int32_t Hq, int32_t Hkv
                                  int32_t page_size, int32_t max_pages, int32_t window,
                                  int32_t n_sink, int32_t num_splits);
 
+/* decode_attn_gqa_sink for callers that cannot allocate device memory: code
+ * under graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * It takes no workspace: the split partials go to a file-scope device array
+ * of the library, 16 MiB per GPU (each GPU the library runs on holds its own
+ * copy until the process ends; its address is looked up once per device with
+ * hipGetSymbolAddress).  The call allocates nothing.  The caller still passes
+ * every input and output, with the meanings, layouts and errors of
+ * decode_attn_gqa_sink (sink_logits may be NULL).
+ *   num_splits  0 = automatic, lowered when needed until the partials,
+ *               B * Hq * splits * (D + 1) fp32 values (each of the two parts
+ *               rounded up to 256 bytes), fit the 16 MiB; a requested count
+ *               whose partials do not fit returns DATTN_EWORKSPACE.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (different streams, or different threads without ordering) race and
+ * give wrong results.  Calls ordered on one stream are safe; the array keeps
+ * the last call's partials, and no call needs it cleared.
+ */
+DATTN_EXPORT int decode_attn_gqa_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* seq_lens, const int32_t* page_table,
+                    int32_t window, int32_t n_sink, const float* sink_logits,
+                    void* out, float* lse,
+                    int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                    int32_t page_size, int32_t max_pages, int32_t dtype, float scale,
+                    int32_t num_splits, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Cache append: the new token's entries, written before attending.
  *
