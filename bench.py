@@ -8,17 +8,32 @@ Llama-3-8B-shaped GQA layer must read (B16, 32/8 heads, D128, 8192 tokens,
 paged 16, bf16) divided by the wall time of one decode_attn_gqa call (split
 kernel + log-sum-exp combine), K calls timed back to back with inputs resident
 in HBM.  The other workloads (window + sinks, MLA, DSA, Quest page selection,
-cache append) are reported under
-"workloads".  A step is one call of the hot path on one batch; buffers rotate
-over copies whose total exceeds 1 GiB so no step reads another's data from
-the 256 MB Infinity Cache.
+cache append) are reported under "workloads".  A step is one call of the hot
+path on one batch.  Inputs rotate over copies so that the bytes a step reads
+recur only after about 1 GiB of other reads: no step is served from the
+256 MB Infinity Cache by a previous one.
+
+Timing, per workload:
+  * W warmup calls, then a clock ramp: calls keep running until `--ramp-ms`
+    of wall time has passed (the GPU's clocks take tens of ms of sustained
+    work to rise after the inputs were built on the CPU); reported as
+    "ramp";
+  * the step pass: K calls back to back between two synchronisations (the
+    headline `ms_per_step` and `value`);
+  * the kernel pass: the same K calls with the library's per-kernel timing,
+    HIP events bound to the kernel dispatches on the launch stream
+    (hipExtLaunchKernel), which exclude the launch gaps between kernels;
+  * per-call statistics: each call bracketed by HIP events, median and
+    p10/p90, once after an untimed 1 GiB scrub write before every call
+    ("call_us", cold) and once with no scrub on one buffer ("warm_call_us",
+    labelled warm).
 
 `roofline` covers the dominant kernel (gqa_split): algorithmic bytes per
-launch over its average duration, measured with HIP events the library
-records around each launch on the same stream, in a second pass of the same
-K steps (the first pass, without events, gives the step time).  `cpu_baseline` is the CPU
-oracle (plain fp64 C, OpenMP over rows) timed on this host on the same
-workload.
+launch over its average duration from the kernel pass.  `read_ceiling` is
+the best rate of a plain streaming-read probe over the same bytes.
+`cpu_baseline` is the CPU oracle (plain fp64 C, OpenMP over rows) timed on
+this host on the same workload; the same leg, the only one that uses the
+oracle, also reports each configuration's error against it on sampled rows.
 """
 import argparse
 import ctypes
@@ -45,8 +60,17 @@ def ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def copies_for(nbytes):
-    return max(1, min(8, math.ceil(ROTATE_BYTES / max(1, nbytes))))
+def copies_for(touched_bytes):
+    """Copies to rotate over so that the bytes one step touches recur only
+    after ~1 GiB of other reads (at most 8)."""
+    return max(1, min(8, math.ceil(ROTATE_BYTES / max(1, touched_bytes))))
+
+
+def pct(xs):
+    import numpy as np
+    a = np.asarray(xs, dtype=np.float64)
+    return {"median": round(float(np.median(a)), 3), "p10": round(float(np.percentile(a, 10)), 3),
+            "p90": round(float(np.percentile(a, 90)), 3)}
 
 
 def sha256_of(path):
@@ -69,18 +93,47 @@ def counter_traffic(kernel, source):
 
 
 class Timer:
-    def __init__(self, api, torch):
-        self.api, self.torch = api, torch
+    def __init__(self, api, torch, ramp_ms):
+        self.api, self.torch, self.ramp_ms = api, torch, ramp_ms
+        # written before each cold per-call sample: evicts the 256 MB
+        # Infinity Cache and the L2s
+        self.scrub = torch.empty(ROTATE_BYTES, dtype=torch.uint8, device="cuda:0")
+
+    def ramp(self, step, start):
+        torch = self.torch
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        n = 0
+        while (time.perf_counter() - t0) * 1e3 < self.ramp_ms:
+            for _ in range(16):
+                step(start + n)
+                n += 1
+            torch.cuda.synchronize()
+        return {"calls": n, "ms": round((time.perf_counter() - t0) * 1e3, 1)}
+
+    def per_call(self, step, steps, scrub):
+        torch = self.torch
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for i, (a, b) in enumerate(ev):
+            if scrub:
+                self.scrub.fill_(i & 255)
+            a.record()
+            step(i if scrub else 0)
+            b.record()
+        torch.cuda.synchronize()
+        return pct([1e3 * a.elapsed_time(b) for a, b in ev])
 
     def run(self, step, steps, warmup, kernels):
-        """K timed steps, twice: first plain (the step time), then with the
-        library's per-kernel HIP events enabled (kernel durations)."""
+        """Warmup, clock ramp, then the step pass (wall time), the kernel pass
+        (dispatch-bound per-kernel events) and the per-call passes."""
         torch, api = self.torch, self.api
         for i in range(warmup):
             step(i)
-        torch.cuda.synchronize()
+        ramp = self.ramp(step, warmup)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
         t0 = time.perf_counter()
         e0.record()
         for i in range(steps):
@@ -99,8 +152,15 @@ class Timer:
             tot, cnt = api.profile_read(k)
             per_kernel[k] = {"avg_us": 1e3 * tot / cnt if cnt else None, "launches": cnt}
         api.profile_reset()
+        cold = self.per_call(step, steps, scrub=True)
+        warm = self.per_call(step, steps, scrub=False)
         return {"wall_ms": 1e3 * (t1 - t0) / steps, "event_ms": e0.elapsed_time(e1) / steps,
-                "kernels": per_kernel}
+                "kernels": per_kernel, "call_us": cold, "warm_call_us": warm, "ramp": ramp}
+
+
+def stats(r):
+    """The timing fields every workload record carries."""
+    return {"call_us": r["call_us"], "warm_call_us": r["warm_call_us"], "ramp": r["ramp"]}
 
 
 def check(lib, rc):
@@ -114,8 +174,7 @@ def bench_gqa(x, timer, steps, warmup, torch, lib, sink_logits=None):
     dev = torch.device("cuda:0")
     q, sl = x.q.to(dev), x.seq_lens.to(dev)
     pt = x.page_table.to(dev) if x.page_table is not None else None
-    kv_bytes_alloc = 2 * x.k_cache.numel() * x.k_cache.element_size()
-    R = copies_for(kv_bytes_alloc)
+    R = copies_for(x.kv_bytes())
     kc = [x.k_cache.to(dev) for _ in range(R)]
     vc = [x.v_cache.to(dev) for _ in range(R)]
     out = torch.empty_like(q)
@@ -143,13 +202,14 @@ def bench_gqa(x, timer, steps, warmup, torch, lib, sink_logits=None):
 
     rec = timer.run(step, steps, warmup, ["gqa_split", "lse_combine"])
     rec["copies"] = R
+    rec["out"], rec["lse"] = out, lse
     return rec
 
 
 def bench_mla(m, timer, steps, warmup, torch, lib):
     dev = torch.device("cuda:0")
     q, sl = m.q.to(dev), m.seq_lens.to(dev)
-    R = copies_for(m.latent.numel() * 2)
+    R = copies_for(m.kv_bytes())
     lat = [m.latent.to(dev) for _ in range(R)]
     out = torch.empty(m.B, m.H, 512, dtype=torch.bfloat16, device=dev)
     lse = torch.empty(m.B, m.H, dtype=torch.float32, device=dev)
@@ -165,6 +225,7 @@ def bench_mla(m, timer, steps, warmup, torch, lib):
 
     rec = timer.run(step, steps, warmup, ["mla_split", "lse_combine"])
     rec["copies"] = R
+    rec["out"], rec["lse"] = out, lse
     return rec
 
 
@@ -174,10 +235,14 @@ def bench_dsa(d, timer, steps, warmup, torch, lib):
     m = d.mla
     B, Hi, Di = d.q_i.shape
     S = d.k_i.shape[1]
-    R = copies_for(d.k_i.numel() * 2)
+    # each step reads every key of the indexer cache and the selected latent
+    # rows; both rotate over R copies (the latent's selected rows are 18.9 MB
+    # a step, so a copy is read again only after R - 1 indexer passes)
+    R = copies_for(d.indexer_bytes())
     qi, w, sl = d.q_i.to(dev), d.w.to(dev), d.seq_lens.to(dev)
     ki = [d.k_i.to(dev) for _ in range(R)]
-    q, lat = m.q.to(dev), m.latent.to(dev)
+    q = m.q.to(dev)
+    lat = [m.latent.to(dev) for _ in range(R)]
     idx = torch.empty(B, d.topk, dtype=torch.int32, device=dev)
     scores = torch.empty(B, S, dtype=torch.float32, device=dev)
     out = torch.empty(B, m.H, 512, dtype=torch.bfloat16, device=dev)
@@ -189,16 +254,17 @@ def bench_dsa(d, timer, steps, warmup, torch, lib):
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     a1 = [(ptr(qi), ptr(w), ptr(ki[r]), ptr(sl), d.topk, ptr(idx), ptr(scores), B, Hi, Di, S, 1,
            ptr(iws), ibytes, stream) for r in range(R)]
-    a2 = (ptr(q), ptr(lat), ptr(idx), d.topk, ptr(out), ptr(lse), B, m.H, 512, 64, m.S_max, 1,
-          ctypes.c_float(m.scale), 0, ptr(ws), nbytes, stream)
+    a2 = [(ptr(q), ptr(lat[r]), ptr(idx), d.topk, ptr(out), ptr(lse), B, m.H, 512, 64, m.S_max, 1,
+           ctypes.c_float(m.scale), 0, ptr(ws), nbytes, stream) for r in range(R)]
 
     def step(i):
         check(lib, lib.dsa_indexer_topk(*a1[i % R]))
-        check(lib, lib.sparse_mla_attn(*a2))
+        check(lib, lib.sparse_mla_attn(*a2[i % R]))
 
     rec = timer.run(step, steps, warmup, ["indexer_scores", "topk_select", "sparse_mla_split",
                                           "lse_combine"])
     rec["copies"] = R
+    rec["out"], rec["lse"], rec["idx"] = out, lse, idx.clone()
     # the indexer with its inputs in fp8 e4m3 (exact for these integers): half the key bytes
     qi8 = qi.to(torch.float8_e4m3fn)
     ki8 = [t.to(torch.float8_e4m3fn) for t in ki]
@@ -216,7 +282,9 @@ def bench_quest(x, timer, steps, warmup, torch, lib, budget):
     over the chosen blocks, combine), and the block-summary build."""
     dev = torch.device("cuda:0")
     q, sl, pt = x.q.to(dev), x.seq_lens.to(dev), x.page_table.to(dev)
-    R = copies_for(2 * x.k_cache.numel() * x.k_cache.element_size())
+    # a step reads the block summaries (1/16 of K) and the chosen blocks' K/V
+    # (about 60% of the layer for these inputs)
+    R = copies_for(x.kv_bytes() // 2)
     kc = [x.k_cache.to(dev) for _ in range(R)]
     vc = [x.v_cache.to(dev) for _ in range(R)]
     max_pages = x.page_table.shape[1]
@@ -323,15 +391,44 @@ def tflops(flops, us):
     return None if not us else flops / (us * 1e-6) / 1e12
 
 
+def rows_sample(n_rows, k, seed):
+    """Deterministic sample of k flat row ids, the first and last included."""
+    import torch
+    g = torch.Generator().manual_seed(seed)
+    pick = torch.randperm(n_rows, generator=g)[: max(0, k - 2)].tolist()
+    return sorted(set([0, n_rows - 1] + pick))
+
+
+def err_record(got, want, tol):
+    """Max per-row ||x - y||_inf / ||y||_inf and the normwise ||x - y||_2 / ||y||_2."""
+    import oracle
+    import torch
+    got = torch.as_tensor(got, dtype=torch.float64)
+    want = torch.as_tensor(want, dtype=torch.float64)
+    nw = float((got - want).norm() / want.norm()) if want.norm() > 0 else float((got - want).norm())
+    return {"max_row_rel_err": float(f"{oracle.rel_err_rows(got, want):.3e}"),
+            "normwise_rel_err": float(f"{nw:.3e}"), "rows": int(got.shape[0]), "tol": tol}
+
+
+def gqa_error(x, rec, n_rows=48, seed=0):
+    """The cpu_baseline leg: a GQA workload's output on sampled rows against the oracle."""
+    import oracle
+    rows = rows_sample(x.B * x.Hq, n_rows, seed)
+    want, _ = oracle.gqa(x.q, x.k, x.v, x.seq_lens, window=x.window, n_sink=x.n_sink, scale=x.scale,
+                         rows=rows)
+    got = rec["out"].float().cpu().reshape(-1, x.D)[rows]
+    return err_record(got, want, 1e-5 if x.q.dtype.itemsize == 4 else 2e-2)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    # the GPU's clocks take ~20 ms of sustained work to ramp up after idling
-    # (input generation runs on the CPU); 300 calls cover that
-    ap.add_argument("--warmup", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--ramp-ms", type=float, default=200.0,
+                    help="wall time of calls before each timed region (clock ramp)")
     ap.add_argument("--quick", action="store_true", help="headline workload only")
-    ap.add_argument("--only", choices=["gqa", "swa", "mla", "dsa", "append", "quest"],
+    ap.add_argument("--only", choices=["gqa", "swa", "mla", "dsa", "append", "quest", "read"],
                     help="time one workload and print its record (for profiling runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="time a plain 1 GiB device copy (reference for HBM byte counters)")
@@ -349,14 +446,16 @@ def main():
     from decode_attention_kv_flash_amd import workloads as wl
     lib = api.lib()
     torch.cuda.set_device(0)
-    timer = Timer(api, torch)
     steps, warmup = args.steps, args.warmup
     if args.calibrate_copy:
         calibrate_copy(torch, steps)
         return
+    timer = Timer(api, torch, args.ramp_ms)
     if args.only:
         only(args.only, timer, steps, warmup, torch, lib, wl)
         return
+    cpu = not args.no_cpu_baseline
+    errors = {}
 
     # ---- headline: Llama-3-8B-shaped GQA layer --------------------------------
     log("[bench] generating gqa config (B16, 32/8 heads, D128, 8192 tokens, paged 16, bf16)")
@@ -366,8 +465,12 @@ def main():
     r2 = bench_gqa(x2, timer, steps, warmup, torch, lib)
     split_us = r2["kernels"]["gqa_split"]["avg_us"]
     log(f"[bench] gqa: {r2['wall_ms']*1e3:.1f} us/step wall, split kernel {split_us:.1f} us")
+    if cpu:
+        errors["config2_" + x2.name] = gqa_error(x2, r2, seed=2)
     value = bytes2 / (r2["wall_ms"] * 1e-3) / 1e9
     achieved = gbs(bytes2, split_us)
+    log("[bench] streaming-read ceiling")
+    ceiling = read_ceiling(timer, torch, lib, bytes2, steps)
     result = {
         "metric": "decode-attention KV GB/s read (% of MI355X HBM peak); MLA/DSA TFLOP/s",
         "value": round(value, 1),
@@ -387,6 +490,7 @@ def main():
             "context": int(x2.seq_lens[0]), "page_size": x2.page_size,
             "kv_bytes_per_step": bytes2, "cache_copies_rotated": r2["copies"],
             "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+            "pct_of_read_ceiling": round(100 * value / ceiling["GB/s"], 2),
         },
         "roofline": {
             "kernel": "gqa_split",
@@ -398,13 +502,18 @@ def main():
             "traffic": counter_traffic("gqa_split", "gqa_decode.hip"),
             "algorithmic_bytes_per_launch": bytes2,
             "avg_launch_us": round(split_us, 2),
+            "frac_of_read_ceiling": round(achieved / ceiling["GB/s"], 4),
         },
+        "read_ceiling": ceiling,
+        "clock_ramp_ms": args.ramp_ms,
         "workloads": {
             "gqa_llama3_8b": {"step_us": round(r2["wall_ms"] * 1e3, 2), "GB/s": round(value, 1),
                               "TFLOP/s": round(flops2 / (r2["wall_ms"] * 1e-3) / 1e12, 3),
-                              "kernels_us": {k: v["avg_us"] for k, v in r2["kernels"].items()}},
+                              "kernels_us": {k: v["avg_us"] for k, v in r2["kernels"].items()},
+                              **stats(r2)},
         },
     }
+    del r2
     if not args.quick:
         budget = 128  # blocks of 16: 2048 tokens per query head
         log(f"[bench] quest on the gqa config, budget {budget} blocks")
@@ -415,7 +524,7 @@ def main():
         mm_us = rq["minmax_full"]["kernels"]["quest_minmax"]["avg_us"]
         result["workloads"]["quest_llama3_8b_budget2048"] = {
             "step_us": round(rq["wall_ms"] * 1e3, 2),
-            "dense_step_us": round(r2["wall_ms"] * 1e3, 2),
+            "dense_step_us": result["workloads"]["gqa_llama3_8b"]["step_us"],
             "bytes_per_step": summ + bnd + unib,
             "GB/s": round((summ + bnd + unib) / (rq["wall_ms"] * 1e-3) / 1e9, 1),
             "kv_bytes_per_head_sum": selb,
@@ -424,22 +533,29 @@ def main():
             "attention_GB/s": round(gbs(unib, kq["gqa_split"]["avg_us"]), 1),
             "topk_us": kq["topk_select"]["avg_us"],
             "kernels_us": {k: v["avg_us"] for k, v in kq.items()},
+            "copies": rq["copies"],
             "minmax_all_blocks_us": round(mm_us, 2),
             "minmax_all_blocks_GB/s": round(gbs(kbytes, mm_us), 1),
-            "minmax_one_block_us": round(rq["minmax_one_block"]["kernels"]["quest_minmax"]["avg_us"], 2)}
+            "minmax_one_block_us": round(rq["minmax_one_block"]["kernels"]["quest_minmax"]["avg_us"], 2),
+            **stats(rq)}
+        del rq
     del x2
+    torch.cuda.empty_cache()
 
     if not args.quick:
         log("[bench] generating window+sinks config (B32, lens U[4096,32768], W4096 + 4 sinks)")
         x3 = wl.config3_swa_sinks()
         b3 = x3.kv_bytes()
         r3 = bench_gqa(x3, timer, steps, warmup, torch, lib)
+        if cpu:
+            errors["config3_" + x3.name] = gqa_error(x3, r3, seed=3)
         result["workloads"]["swa4096_sinks4"] = {
             "step_us": round(r3["wall_ms"] * 1e3, 2),
             "GB/s": round(b3 / (r3["wall_ms"] * 1e-3) / 1e9, 1),
             "split_kernel_GB/s": round(gbs(b3, r3["kernels"]["gqa_split"]["avg_us"]), 1),
-            "kv_bytes_per_step": b3,
-            "kernels_us": {k: v["avg_us"] for k, v in r3["kernels"].items()}}
+            "kv_bytes_per_step": b3, "copies": r3["copies"],
+            "kernels_us": {k: v["avg_us"] for k, v in r3["kernels"].items()}, **stats(r3)}
+        del r3
         # the same workload with an explicit sink logit per head
         sk = torch.linspace(-2.0, 2.0, x3.Hq, dtype=torch.float32)
         r3s = bench_gqa(x3, timer, steps, warmup, torch, lib, sink_logits=sk)
@@ -448,8 +564,8 @@ def main():
             "GB/s": round(b3 / (r3s["wall_ms"] * 1e-3) / 1e9, 1),
             "split_kernel_GB/s": round(gbs(b3, r3s["kernels"]["gqa_split"]["avg_us"]), 1),
             "kv_bytes_per_step": b3,
-            "kernels_us": {k: v["avg_us"] for k, v in r3s["kernels"].items()}}
-        del x3
+            "kernels_us": {k: v["avg_us"] for k, v in r3s["kernels"].items()}, **stats(r3s)}
+        del x3, r3s
         torch.cuda.empty_cache()
 
         # other head layouts at config 2's K/V bytes: 64 q / 8 KV heads at D128
@@ -467,8 +583,8 @@ def main():
                 "GB/s": round(bh / (rh["wall_ms"] * 1e-3) / 1e9, 1),
                 "split_kernel_GB/s": round(gbs(bh, rh["kernels"]["gqa_split"]["avg_us"]), 1),
                 "kv_bytes_per_step": bh,
-                "kernels_us": {k: v["avg_us"] for k, v in rh["kernels"].items()}}
-            del xh
+                "kernels_us": {k: v["avg_us"] for k, v in rh["kernels"].items()}, **stats(rh)}
+            del xh, rh
             torch.cuda.empty_cache()
 
         log("[bench] generating MLA config (B32, H128, latent 576, 16384 tokens)")
@@ -476,6 +592,11 @@ def main():
         r4 = bench_mla(m4, timer, steps, warmup, torch, lib)
         b4, f4 = m4.kv_bytes(), m4.flops()
         us4 = r4["kernels"]["mla_split"]["avg_us"]
+        if cpu:
+            import oracle
+            rows = rows_sample(m4.B * m4.H, 48, 4)
+            want, _ = oracle.mla(m4.q, m4.latent, m4.seq_lens, scale=m4.scale, rows=rows)
+            errors["config4_" + m4.name] = err_record(r4["out"].float().cpu().reshape(-1, 512)[rows], want, 2e-2)
         result["workloads"]["mla_dsv3"] = {
             "step_us": round(r4["wall_ms"] * 1e3, 2),
             "TFLOP/s": round(f4 / (r4["wall_ms"] * 1e-3) / 1e12, 1),
@@ -483,8 +604,9 @@ def main():
             "split_kernel_TFLOP/s": round(tflops(f4, us4), 1),
             "mfma_frac_of_bf16_peak": round(tflops(f4, us4) / BF16_PEAK_TFLOPS, 4),
             "split_kernel_hbm_frac": round(gbs(b4, us4) / HBM_PEAK_GBS, 4),
-            "kernels_us": {k: v["avg_us"] for k, v in r4["kernels"].items()}}
-        del m4
+            "copies": r4["copies"],
+            "kernels_us": {k: v["avg_us"] for k, v in r4["kernels"].items()}, **stats(r4)}
+        del m4, r4
         torch.cuda.empty_cache()
 
         log("[bench] generating DSA config (B8, 65536 tokens, indexer 64x128, top-2048)")
@@ -495,6 +617,15 @@ def main():
         sel = d5.B * d5.topk
         fs = sel * 2 * d5.mla.H * (576 + 512)
         bs = sel * 576 * 2
+        if cpu:
+            import oracle
+            want_idx = oracle.topk(oracle.indexer(d5.q_i, d5.w, d5.k_i, d5.seq_lens), d5.seq_lens, d5.topk)
+            m = d5.mla
+            rows = rows_sample(m.B * m.H, 48, 5)
+            want, _ = oracle.mla(m.q, m.latent, idx=want_idx, scale=m.scale, rows=rows)
+            e5 = err_record(r5["out"].float().cpu().reshape(-1, 512)[rows], want, 2e-2)
+            e5["index_sets_bit_exact"] = bool(torch.equal(r5["idx"].cpu(), want_idx))
+            errors["config5_" + d5.name] = e5
         result["workloads"]["dsa_top2048"] = {
             "step_us": round(r5["wall_ms"] * 1e3, 2),
             "indexer_GB/s": round(gbs(bi, ku["indexer_scores"]["avg_us"]), 1),
@@ -502,22 +633,66 @@ def main():
             "topk_us": ku["topk_select"]["avg_us"],
             "sparse_mla_TFLOP/s": round(tflops(fs, ku["sparse_mla_split"]["avg_us"]), 2),
             "sparse_mla_GB/s": round(gbs(bs, ku["sparse_mla_split"]["avg_us"]), 1),
-            "kernels_us": {k: v["avg_us"] for k, v in ku.items()},
+            "copies": r5["copies"],
+            "kernels_us": {k: v["avg_us"] for k, v in ku.items()}, **stats(r5),
             "indexer_fp8": {
                 "indexer_us": r5["fp8"]["kernels"]["indexer_scores"]["avg_us"],
                 "indexer_GB/s": round(gbs(bi // 2, r5["fp8"]["kernels"]["indexer_scores"]["avg_us"]), 1),
                 "key_bytes_per_step": bi // 2,
-                "indexer_topk_step_us": round(r5["fp8"]["wall_ms"] * 1e3, 2)}}
-        del d5
+                "indexer_topk_step_us": round(r5["fp8"]["wall_ms"] * 1e3, 2), **stats(r5["fp8"])}}
+        del d5, r5
         torch.cuda.empty_cache()
 
         log("[bench] cache append (GQA K/V, MLA latent, indexer keys)")
         result["workloads"]["kv_append"] = bench_append(timer, steps, warmup, torch, lib)
         torch.cuda.empty_cache()
 
-    if not args.no_cpu_baseline:
+    if cpu:
+        x1 = wl.config1_tiny_gqa()
+        r1 = bench_gqa(x1, timer, min(steps, 20), 2, torch, lib)
+        errors["config1_" + x1.name] = gqa_error(x1, r1, n_rows=x1.B * x1.Hq)
         result["cpu_baseline"] = cpu_baseline()
+        result["cpu_baseline"]["max_error_vs_oracle"] = errors
     print(json.dumps(result), flush=True)
+
+
+def read_ceiling(timer, torch, lib, nbytes, steps):
+    """Best rate of the library's plain streaming-read probe over nbytes per
+    launch, two buffers alternated (2 x nbytes > the Infinity Cache), over
+    launch shapes: workgroups x loads in flight per thread."""
+    nbytes = nbytes // 16 * 16
+    bufs = [torch.zeros(nbytes, dtype=torch.uint8, device="cuda:0") for _ in range(2)]
+    sink = torch.zeros(1 << 16, dtype=torch.int32, device="cuda:0")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def launcher(grid, depth):
+        return lambda i: check(lib, lib.dattn_stream_read_probe(ptr(bufs[i % 2]), nbytes, ptr(sink), grid,
+                                                                 depth, stream))
+    timer.ramp(launcher(1024, 8), 0)
+    best, tried = None, []
+    for grid in (512, 1024, 2048, 4096):
+        for depth in (4, 8, 16):
+            step = launcher(grid, depth)
+            for i in range(4):
+                step(i)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for i in range(steps):
+                step(i)
+            e1.record()
+            torch.cuda.synchronize()
+            us = 1e3 * e0.elapsed_time(e1) / steps
+            rate = nbytes / (us * 1e-6) / 1e9
+            tried.append([grid, depth, round(rate, 1)])
+            if best is None or rate > best["GB/s"]:
+                best = {"GB/s": round(rate, 1), "us": round(us, 2), "grid": grid, "loads_in_flight": depth}
+    best.update({"bytes_per_launch": nbytes, "launches": steps,
+                 "pct_of_hbm_peak": round(100 * best["GB/s"] / HBM_PEAK_GBS, 2),
+                 "sweep_grid_depth_GBs": tried,
+                 "probe": "dattn_stream_read_probe: 256-thread workgroups over contiguous ranges, "
+                          "16-byte nontemporal loads"})
+    del bufs
+    return best
 
 
 def calibrate_copy(torch, steps):
@@ -558,12 +733,27 @@ def only(name, timer, steps, warmup, torch, lib, wl):
         summ, bnd, selb, unib = quest_bytes(x, 128, r.pop("selected"))
         r["bytes_per_step"] = summ + bnd + unib
         r["kv_bytes_per_head_sum"], r["kv_bytes_union_per_kv_head"] = selb, unib
+    elif name == "read":
+        r = read_ceiling(timer, torch, lib, wl.config2_llama3_8b_gqa().kv_bytes(), steps)
     else:
         d = wl.config5_dsa()
         r = bench_dsa(d, timer, steps, warmup, torch, lib)
         r["indexer_bytes_per_step"] = d.indexer_bytes()
+    for k in ("out", "lse", "idx"):
+        r.pop(k, None)
     r["workload"] = name
     print(json.dumps(r), flush=True)
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(target_s=15.0, max_passes=500):
@@ -582,6 +772,7 @@ def cpu_baseline(target_s=15.0, max_passes=500):
         reps += 1
     value = nbytes * reps / total / 1e9
     return {"value": round(value, 3), "unit": "GB/s", "cores": oracle.threads(), "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"full gqa workload ({x.B * x.Hq} rows x {int(x.seq_lens[0])} tokens, "
                       f"{nbytes} KV bytes) x {reps} passes, {total:.1f} s"}
 

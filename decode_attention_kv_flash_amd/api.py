@@ -29,7 +29,7 @@ EXPORTS = (
     "kv_append_gqa", "kv_append_rows",
     "quest_page_minmax", "decode_attn_quest", "decode_attn_quest_workspace",
     "dattn_last_error", "dattn_version", "dattn_debug_enable", "dattn_check_tables",
-    "dattn_profile_enable", "dattn_profile_read", "dattn_profile_reset",
+    "dattn_profile_enable", "dattn_profile_read", "dattn_profile_reset", "dattn_stream_read_probe",
 )
 
 _lib = None
@@ -84,6 +84,8 @@ def lib() -> ctypes.CDLL:
     L.dattn_last_error.restype = ctypes.c_char_p
     L.dattn_last_error.argtypes = []
     L.dattn_version.restype = I32
+    L.dattn_stream_read_probe.argtypes = [P, SZ, P, I32, I32, P]
+    L.dattn_stream_read_probe.restype = ctypes.c_int
     L.dattn_debug_enable.argtypes = [I32]
     L.dattn_debug_enable.restype = ctypes.c_int
     L.dattn_check_tables.argtypes = [P, P, I32, I32, I32, ctypes.c_int64]

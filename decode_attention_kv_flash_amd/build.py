@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.environ.get("DATTN_BUILD_DIR", os.path.join(PKG, "_build"))
 LIB = os.environ.get("DATTN_LIB_OUT", os.path.join(PKG, "libdattn.so"))
-SOURCES = ["api.cpp", "gqa_decode.hip", "mla_decode.hip", "indexer.hip", "topk.hip", "kv_append.hip", "quest.hip"]
+SOURCES = ["api.cpp", "gqa_decode.hip", "mla_decode.hip", "indexer.hip", "topk.hip", "kv_append.hip", "quest.hip", "probe.hip"]
 ARCH = os.environ.get("DATTN_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

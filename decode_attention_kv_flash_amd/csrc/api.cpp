@@ -57,6 +57,7 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 struct ProfRec {
   const char* name;
   hipEvent_t start, stop;
+  bool launched;  // a kernel carried the events (else they were never recorded)
 };
 std::mutex g_prof_mu;
 bool g_prof_on = false;
@@ -197,22 +198,55 @@ int device_cu_count() {
   return cus;
 }
 
+namespace {
+// The record the launches on this thread bind to (between prof_begin and
+// prof_end), and whether one of them took its start event yet.
+thread_local ProfRec* tl_open = nullptr;
+thread_local size_t tl_open_index = 0;
+thread_local bool tl_started = false;
+}  // namespace
+
 void prof_begin(const char* name, hipStream_t s) {
+  (void)s;
   std::lock_guard<std::mutex> lk(g_prof_mu);
+  tl_open = nullptr;
   if (!g_prof_on) return;
-  hipEvent_t e = pool_get();
-  if (!e) return;
-  hipEventRecord(e, s);
-  g_recs.push_back({name, e, nullptr});
+  hipEvent_t a = pool_get(), b = pool_get();
+  if (!a || !b) {
+    if (a) g_pool.push_back(a);
+    if (b) g_pool.push_back(b);
+    return;
+  }
+  g_recs.push_back({name, a, b, false});
+  tl_open_index = g_recs.size() - 1;
+  tl_open = &g_recs.back();
+  tl_started = false;
+}
+
+ProfEvents prof_events_for_launch() {
+  ProfEvents ev;
+  if (!tl_open) return ev;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (tl_open_index >= g_recs.size()) return ev;  // records dropped meanwhile
+  ProfRec& r = g_recs[tl_open_index];
+  if (!tl_started) ev.start = r.start;
+  ev.stop = r.stop;
+  tl_started = true;
+  r.launched = true;
+  return ev;
 }
 
 void prof_end(hipStream_t s) {
+  (void)s;
+  if (!tl_open) return;
   std::lock_guard<std::mutex> lk(g_prof_mu);
-  if (!g_prof_on || g_recs.empty() || g_recs.back().stop) return;
-  hipEvent_t e = pool_get();
-  if (!e) return;
-  hipEventRecord(e, s);
-  g_recs.back().stop = e;
+  // a group that launched nothing leaves no record
+  if (tl_open_index + 1 == g_recs.size() && !g_recs.back().launched) {  // (else dropped meanwhile)
+    g_pool.push_back(g_recs.back().start);
+    g_pool.push_back(g_recs.back().stop);
+    g_recs.pop_back();
+  }
+  tl_open = nullptr;
 }
 
 }  // namespace dattn
@@ -469,6 +503,19 @@ const char* dattn_last_error(void) { return g_err.c_str(); }
 
 int32_t dattn_version(void) { return 1; }
 
+int dattn_stream_read_probe(const void* src, size_t bytes, uint32_t* sink, int32_t grid, int32_t depth,
+                            void* stream) {
+  if (!src || !sink) return fail(DATTN_EINVAL, "dattn_stream_read_probe: NULL pointer argument");
+  if (!aligned16(src) || bytes % 16 != 0)
+    return fail(DATTN_EINVAL, "dattn_stream_read_probe: src must be 16-byte aligned and bytes a multiple of 16");
+  if (grid < 1 || grid > (1 << 20)) return fail(DATTN_EINVAL, "dattn_stream_read_probe: grid %d", grid);
+  if (depth != 4 && depth != 8 && depth != 16)
+    return fail(DATTN_EINVAL, "dattn_stream_read_probe: depth %d not in {4, 8, 16}", depth);
+  hipStream_t s = (hipStream_t)stream;
+  const int rc = launch("stream_read", s, [&] { return dattn::launch_stream_read(src, bytes, sink, grid, depth, s); });
+  return rc ? rc : ok();
+}
+
 int dattn_debug_enable(int32_t on) {
   g_debug.store(on ? 1 : 0, std::memory_order_relaxed);
   return ok();
@@ -506,7 +553,7 @@ int dattn_profile_read(const char* name, double* total_ms, int64_t* count) {
   double tot = 0.0;
   int64_t n = 0;
   for (auto& r : g_recs) {
-    if (!r.stop || (name && !strstr(r.name, name))) continue;
+    if (!r.launched || (name && !strstr(r.name, name))) continue;
     hipError_t e = hipEventSynchronize(r.stop);
     if (e != hipSuccess) return hip_fail(e, "dattn_profile_read");
     float ms = 0.f;

@@ -731,10 +731,10 @@ template <bool BF16, int D, bool FAST>
 hipError_t launch_df(const GqaArgs& a, hipStream_t s) {
   dim3 grid(a.num_splits, a.Hkv, a.B), block(kThreads);
   switch (a.G) {
-    case 1: gqa_split_kernel<BF16, D, 1, FAST><<<grid, block, 0, s>>>(a); break;
-    case 2: gqa_split_kernel<BF16, D, 2, FAST><<<grid, block, 0, s>>>(a); break;
-    case 4: gqa_split_kernel<BF16, D, 4, FAST><<<grid, block, 0, s>>>(a); break;
-    case 8: gqa_split_kernel<BF16, D, 8, FAST><<<grid, block, 0, s>>>(a); break;
+    case 1: launch_kernel(gqa_split_kernel<BF16, D, 1, FAST>, grid, block, s, a); break;
+    case 2: launch_kernel(gqa_split_kernel<BF16, D, 2, FAST>, grid, block, s, a); break;
+    case 4: launch_kernel(gqa_split_kernel<BF16, D, 4, FAST>, grid, block, s, a); break;
+    case 8: launch_kernel(gqa_split_kernel<BF16, D, 8, FAST>, grid, block, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -747,15 +747,15 @@ hipError_t launch_d(const GqaArgs& a, hipStream_t s) {
     if (!fast) return hipErrorInvalidValue;
     if (!a.list_count) {
       dim3 grid(a.num_splits, a.Hq, a.B), block(kThreads);
-      gqa_split_kernel<BF16, D, 1, true, kSetPerHead><<<grid, block, 0, s>>>(a);
+      launch_kernel(gqa_split_kernel<BF16, D, 1, true, kSetPerHead>, grid, block, s, a);
       return hipGetLastError();
     }
     dim3 grid(a.num_splits, a.Hkv, a.B), block(kThreads);
     switch (a.G) {
-      case 1: gqa_split_kernel<BF16, D, 1, true, kSetUnion><<<grid, block, 0, s>>>(a); break;
-      case 2: gqa_split_kernel<BF16, D, 2, true, kSetUnion><<<grid, block, 0, s>>>(a); break;
-      case 4: gqa_split_kernel<BF16, D, 4, true, kSetUnion><<<grid, block, 0, s>>>(a); break;
-      case 8: gqa_split_kernel<BF16, D, 8, true, kSetUnion><<<grid, block, 0, s>>>(a); break;
+      case 1: launch_kernel(gqa_split_kernel<BF16, D, 1, true, kSetUnion>, grid, block, s, a); break;
+      case 2: launch_kernel(gqa_split_kernel<BF16, D, 2, true, kSetUnion>, grid, block, s, a); break;
+      case 4: launch_kernel(gqa_split_kernel<BF16, D, 4, true, kSetUnion>, grid, block, s, a); break;
+      case 8: launch_kernel(gqa_split_kernel<BF16, D, 8, true, kSetUnion>, grid, block, s, a); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -922,8 +922,8 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   if (a.D % 4 != 0) return hipErrorInvalidValue;
   const size_t total = (size_t)a.rows * (a.D / 4);
   const unsigned blocks = (unsigned)((total + kCombineThreads - 1) / kCombineThreads);
-  if (a.bf16) lse_combine_kernel<true><<<blocks, kCombineThreads, 0, s>>>(a);
-  else lse_combine_kernel<false><<<blocks, kCombineThreads, 0, s>>>(a);
+  if (a.bf16) launch_kernel(lse_combine_kernel<true>, blocks, kCombineThreads, s, a);
+  else launch_kernel(lse_combine_kernel<false>, blocks, kCombineThreads, s, a);
   return hipGetLastError();
 }
 

@@ -231,7 +231,7 @@ hipError_t launch_nmt(IndexerArgs& a, hipStream_t s) {
   // the select's first level comes along only when the ranges are its chunks
   if (per != kTopkChunk || a.S_max <= kTopkChunk) a.hist0 = nullptr;
   dim3 grid((unsigned)((a.S_max + per - 1) / per), a.B), block(kThreads);
-  indexer_kernel<NMT, FP8><<<grid, block, 0, s>>>(a);
+  launch_kernel(indexer_kernel<NMT, FP8>, grid, block, s, a);
   return hipGetLastError();
 }
 

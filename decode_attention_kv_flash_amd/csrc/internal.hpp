@@ -1,15 +1,31 @@
 // Host-side launch interfaces between the C ABI (api.cpp) and the kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace dattn {
 
-// Kernel launch bracketing for per-kernel timing (api.cpp).
+// Kernel launch bracketing for per-kernel timing (api.cpp).  Between
+// prof_begin and prof_end, the kernels launched on this thread carry the
+// record's events: the first launch its start event, every launch its stop
+// event, so the record spans the first kernel's start to the last one's end
+// as the dispatches themselves report them (launch overhead excluded).
 void prof_begin(const char* name, hipStream_t s);
 void prof_end(hipStream_t s);
+struct ProfEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+ProfEvents prof_events_for_launch();  // both null when timing is off
+
+// Every kernel of the library is launched through here.
+template <typename F, typename... Args>
+void launch_kernel(F kernel, dim3 grid, dim3 block, hipStream_t s, Args... args) {
+  const ProfEvents ev = prof_events_for_launch();
+  hipExtLaunchKernelGGL(kernel, grid, block, 0, s, ev.start, ev.stop, 0, args...);
+}
 
 // Compute units of the current device, queried once per device (256 when the
 // device cannot be queried); the decode calls make no other device queries.
@@ -174,5 +190,11 @@ struct KvAppendArgs {
 };
 
 hipError_t launch_kv_append(const KvAppendArgs& a, hipStream_t s);
+
+// Streaming-read probe (diagnostics): reads `bytes` (a multiple of 16) from
+// src with `grid` workgroups, `depth` (4, 8 or 16) loads in flight per
+// thread; sink holds `grid` words.
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int grid, int depth,
+                              hipStream_t s);
 
 }  // namespace dattn

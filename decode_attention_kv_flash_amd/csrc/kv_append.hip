@@ -68,7 +68,7 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(const KvAppendArgs 
 }  // namespace
 
 hipError_t launch_kv_append(const KvAppendArgs& a, hipStream_t s) {
-  kv_append_kernel<<<a.B, kThreads, 0, s>>>(a);
+  launch_kernel(kv_append_kernel, a.B, kThreads, s, a);
   return hipGetLastError();
 }
 

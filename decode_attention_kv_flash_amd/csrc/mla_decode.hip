@@ -458,7 +458,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_split_kernel(const MlaArgs a) 
 template <bool SPARSE, bool PAGED, int NW>
 hipError_t launch_variant(const MlaArgs& a, hipStream_t s) {
   dim3 grid(a.num_splits, a.H / (NW * kHeadsPerWave), a.B), block(64 * NW);
-  mla_split_kernel<SPARSE, PAGED, NW><<<grid, block, 0, s>>>(a);
+  launch_kernel(mla_split_kernel<SPARSE, PAGED, NW>, grid, block, s, a);
   return hipGetLastError();
 }
 

@@ -262,7 +262,7 @@ hipError_t minmax_d(const QuestArgs& a, hipStream_t s) {
   const int wgs = (a.max_blocks + kWaves - 1) / kWaves - a.first_block / kWaves;
   if (wgs <= 0) return hipSuccess;
   dim3 grid(wgs, a.Hkv, a.B);
-  quest_minmax_kernel<BF16, D><<<grid, kThreads, 0, s>>>(a);
+  launch_kernel(quest_minmax_kernel<BF16, D>, grid, kThreads, s, a);
   return hipGetLastError();
 }
 
@@ -270,7 +270,7 @@ template <bool BF16, int D>
 hipError_t bounds_d(const QuestArgs& a, hipStream_t s) {
   const int per_wg = kWaves * kTiles * 16;
   dim3 grid((a.max_blocks + per_wg - 1) / per_wg, a.Hkv * ((a.G + 15) / 16), a.B);
-  quest_bounds_kernel<BF16, D><<<grid, kThreads, 0, s>>>(a);
+  launch_kernel(quest_bounds_kernel<BF16, D>, grid, kThreads, s, a);
   return hipGetLastError();
 }
 
@@ -283,7 +283,7 @@ hipError_t launch_quest_minmax(const QuestArgs& a, hipStream_t s) {
 
 hipError_t launch_quest_union(const QuestUnionArgs& a, hipStream_t s) {
   if (a.G > 8 || a.max_blocks > kQuestUnionMaxBlocks) return hipErrorInvalidValue;
-  quest_union_kernel<<<dim3(a.Hkv, a.B), kThreads, 0, s>>>(a);
+  launch_kernel(quest_union_kernel, dim3(a.Hkv, a.B), kThreads, s, a);
   return hipGetLastError();
 }
 

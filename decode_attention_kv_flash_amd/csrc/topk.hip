@@ -352,14 +352,14 @@ hipError_t launch_topk(const TopkArgs& a0, hipStream_t s) {
   a.row_words = (int64_t)topk_row_words(a.n_chunks);
   const dim3 grid(a.n_chunks, a.B);
   if (a.n_chunks == 1) {
-    topk_single_kernel<<<grid, kTT, 0, s>>>(a);
+    launch_kernel(topk_single_kernel, grid, kTT, s, a);
     return hipGetLastError();
   }
-  if (!a.hist0_done) topk_digit_kernel<0><<<grid, kTT, 0, s>>>(a);
-  topk_digit_kernel<1><<<grid, kTT, 0, s>>>(a);
-  topk_digit_kernel<2><<<grid, kTT, 0, s>>>(a);
-  topk_digit_kernel<3><<<grid, kTT, 0, s>>>(a);
-  topk_write_kernel<<<grid, kTT, 0, s>>>(a);
+  if (!a.hist0_done) launch_kernel(topk_digit_kernel<0>, grid, kTT, s, a);
+  launch_kernel(topk_digit_kernel<1>, grid, kTT, s, a);
+  launch_kernel(topk_digit_kernel<2>, grid, kTT, s, a);
+  launch_kernel(topk_digit_kernel<3>, grid, kTT, s, a);
+  launch_kernel(topk_write_kernel, grid, kTT, s, a);
   return hipGetLastError();
 }
 

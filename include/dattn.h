@@ -433,15 +433,28 @@ DATTN_EXPORT int dattn_debug_enable(int32_t on);
 DATTN_EXPORT int dattn_check_tables(const int32_t* seq_lens, const int32_t* page_table, int32_t B,
                                     int32_t page_size, int32_t max_pages, int64_t num_pages);
 
-/* Per-kernel timing.  While enabled, every kernel the library launches is
- * bracketed by HIP events recorded on the launch stream.  dattn_profile_read
- * waits for the recorded events and reports, for kernels whose name contains
- * `name`, the summed duration in milliseconds and the launch count.
- * dattn_profile_reset drops all records.  Timing adds two event records per
- * launch and is meant for benchmarks, not production. */
+/* Per-kernel timing.  While enabled, every call's kernels carry HIP events
+ * on the launch stream, bound to the dispatches themselves
+ * (hipExtLaunchKernel): one record per launch step (a step of several kernels,
+ * such as the top-k levels, spans the first kernel's start to the last one's
+ * end), so launch overhead between kernels is not counted.  dattn_profile_read
+ * waits for the events and reports, for records whose name contains `name`,
+ * the summed duration in milliseconds and the record count.
+ * dattn_profile_reset drops all records.  Meant for benchmarks, not
+ * production. */
 DATTN_EXPORT int dattn_profile_enable(int32_t on);
 DATTN_EXPORT int dattn_profile_read(const char* name, double* total_ms, int64_t* count);
 DATTN_EXPORT int dattn_profile_reset(void);
+
+/* Streaming-read probe: reads `bytes` (a multiple of 16) from the device
+ * buffer src (16-byte aligned) with `grid` workgroups of 256 threads, each
+ * workgroup one contiguous range, each thread keeping `depth` (4, 8 or 16)
+ * 16-byte nontemporal loads in flight; sink (device, `grid` words) is almost
+ * never written.  The best rate over launch shapes is the ceiling that the
+ * HBM-bound kernels are compared with besides the specification's peak.
+ * Diagnostics only. */
+DATTN_EXPORT int dattn_stream_read_probe(const void* src, size_t bytes, uint32_t* sink, int32_t grid,
+                                         int32_t depth, void* stream);
 
 #ifdef __cplusplus
 }
