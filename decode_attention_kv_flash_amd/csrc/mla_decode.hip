@@ -9,32 +9,40 @@
 // heads, token split) and reads each latent row of its split once; each wave
 // owns 32 heads, one wave per SIMD.
 //
-// Data movement: the split's cache rows (paged, contiguous or gathered by a
-// top-k list) are resolved once into a row table in LDS.  Tiles of 32 rows
-// (36 KB) then go from HBM straight into LDS by direct-to-LDS loads
-// (global_load_lds_dwordx4: no registers in between) into four tile
-// buffers, issued two tiles ahead of use.  Row r of a tile keeps its 16-byte
-// chunk c at slot c ^ f(r) within its group of eight chunks; both read
-// patterns below are then free of LDS bank conflicts.
+// Data movement.  Tiles of 16 rows (18 KB) go from HBM straight into LDS by
+// direct-to-LDS loads (global_load_lds_dwordx4: no registers in between),
+// into eight tile buffers: while one tile is P.V'd and the next scored, six
+// more are in flight (108 KB per CU), enough to keep the HBM stream full.  A
+// contiguous cache needs no lookup: a tile is 18 KB of consecutive rows, one
+// uniform base address plus a fixed offset per lane.  A paged cache and a
+// gathered list resolve their rows once into a row table in LDS.  Row r of a
+// tile keeps its 16-byte chunk c at slot c ^ f(r) within its group of eight
+// chunks, which makes both LDS read patterns below free of bank conflicts.
 //
-// Per tile and wave:
-//   * S^T[token, head] = C[token, :] . Q^T over 576 dims: 36 32x32x16 bf16
-//     MFMAs, A = latent chunks from LDS, B = the wave's 32 query rows held in
-//     registers for the whole split;
+// Per tile (16 tokens), in one instruction stream per wave:
+//   * S^T[token, head] = C[token, :] . Q^T over 576 dims for the wave's own 32
+//     heads: 18 k-steps of two 16x16x32 bf16 MFMAs (two groups of 16 heads),
+//     A = latent chunks from LDS (one read serves both), B = the wave's query
+//     rows, held in registers for the whole split;
 //   * online softmax in log2 units per head ("All the attentions", section 1:
 //     running maximum and sum); the reference maximum is set by the head's
 //     first scores and moves only when a score passes it by more than 2^64
 //     (exponentials stay finite in fp32 and keep their relative precision);
 //     when that happens the workgroup restarts the split with the larger
-//     reference, so the 256-value accumulator is never rescaled;
-//   * O[head, 0:512] += P . C[:, 0:512]: the S^T accumulator layout is
-//     exactly the A operand P needs (heads x tokens, the k order permuted the
-//     same way on both operands), and the B operand (tokens x dims) comes
-//     from the row-major tile by the gfx950 transpose read ds_read_b64_tr_b16.
-// One wave per SIMD cannot hide LDS latency behind other waves, so the loop
-// is software-pipelined: iteration t alternates the score MFMAs of tile t + 1
-// with the P.V MFMAs of tile t (independent chains), each LDS read issued
-// five MFMAs before its use, then runs the softmax of tile t + 1.
+//     reference, so the accumulators are never rescaled.  P goes to LDS in
+//     the A layout of the 32x32x16 MFMA (a head's 8 consecutive tokens per
+//     lane), which one v_permlane16_swap per register pair makes from the
+//     score layout;
+//   * O[head, dims] += P . C[:, dims]: the wave owns 512 / W of the output
+//     dims for all the workgroup's heads (W waves), 16 32x32x16 MFMAs; the B
+//     operand (tokens x dims) comes from the row-major tile by the gfx950
+//     transpose read ds_read_b64_tr_b16, so each wave reads only its own
+//     dims of the value, and every head's P from the other waves through LDS.
+// A single wave per SIMD issues at most one instruction every four cycles,
+// so the stream is built to fit the matrix cores' time: the score MFMAs of
+// tile t + 1, the P.V MFMAs of tile t - 1, the softmax of tile t and the
+// copies of tile t + 6 are interleaved, each LDS operand read a few MFMA
+// steps ahead of its use.
 //
 // O lives in accumulation registers (AGPRs) for the whole split.  All MFMAs
 // are issued by inline assembly that pins each operand to its register file
@@ -56,39 +64,81 @@ constexpr int kDc = 512;            // c_KV width (the value)
 constexpr int kDq = 576;            // latent row: c_KV + k_pe
 constexpr int kRowBytes = kDq * 2;
 constexpr int kChunks = kDq / 8;    // 16-byte chunks per row
-constexpr int kTile = 32;           // tokens per tile
+constexpr int kTile = 16;           // tokens per tile
 constexpr int kHeadsPerWave = 32;
-constexpr int kTileChunks = kTile * kChunks;              // 2304
-constexpr int kTileBytes = kTileChunks * 16;              // 36864
-constexpr int kBuffers = 4;
-constexpr int kDmaPerTile = kTileChunks / 64;             // 36 wave-wide 1 KB copies
-constexpr int kKSteps = kDq / 16;                         // 36 MFMA k-steps for the scores
+constexpr int kTileChunks = kTile * kChunks;              // 1152
+constexpr int kTileBytes = kTileChunks * 16;              // 18432
+constexpr int kKSteps = kDq / 32;                         // 18 score k-steps of 32 dims
 constexpr int kNTiles = kDc / 32;                         // 16 output tiles of 32 dims
-constexpr int kPvSteps = 2 * kNTiles;                     // 2 k-steps of 16 tokens x 16 tiles
 constexpr int kRing = 3;                                  // LDS fragments in flight per operand
 constexpr float kTau = 64.0f;                             // reference-maximum slack (log2)
 constexpr uint32_t kPad = 0x80000000u;                    // row-table flag: no token here
 constexpr int kMaxTiles = kMlaMaxSplitTokens / kTile;
-// tiles t + 1 (scores) and up to t + 3 (prefetch) of the last iteration
-constexpr int kRowTable = (kMaxTiles + 3) * kTile;
+constexpr int kRowTable = (kMaxTiles + 1) * kTile;  // plus one tile of padding
 static_assert(kMlaMaxSplitTokens % kTile == 0, "splits hold whole tiles");
-static_assert(kBuffers * kTileBytes + kRowTable * 4 + 16 <= 160 * 1024, "fits the LDS");
+// tile buffers: eight for a contiguous cache, seven beside a row table; tile
+// t + kBuffers - 2 is copied into the buffer of tile t - 2 while tiles t - 1
+// (P.V), t (softmax) and t + 1 (scores) are in use
+template <bool TABLE> constexpr int kBuffersOf = TABLE ? 7 : 8;
+constexpr int kPBytes = 4 * 1024;  // P of one tile for up to 128 heads, bf16
+static_assert(8 * kTileBytes + 2 * kPBytes + 64 <= 160 * 1024, "fits the LDS");
+static_assert(7 * kTileBytes + 2 * kPBytes + kRowTable * 4 + ((kMaxTiles + 32) / 32) * 4 + 64 <= 160 * 1024,
+              "fits the LDS");
 
-// Chunk permutation of row r (low three bits of the chunk index only).  LDS
-// has 64 four-byte banks; a 16-byte read serves 16 lanes per pass and an
-// 8-byte read 32.  Rows are 1152 B apart, i.e. alternate between two
-// 128-byte halves of the bank space, so rows of equal parity among 16
-// consecutive ones must take distinct slots (score reads: 16 rows, one
-// chunk), and rows r, r + 2 (r % 4 < 2) must take slots in different halves
-// of an 8-chunk group (transpose reads: 4 rows, 4 chunks).  m -> (m & 1) << 2
-// | m >> 1 over m = (r / 2) % 8 does both.
+// Chunk permutation of row r (low three bits of the chunk index only): the
+// 16-byte chunk c of tile row r sits at slot c ^ f(r) of its group of eight.
+// Both read patterns must be free of LDS bank conflicts: the score reads
+// (lane l: row l % 16, chunk 4 ks + l / 16, 16 bytes) and the transpose
+// reads (lane l: rows 8 (l / 32) + (l % 16) / 4 and + 4, chunks 4 n + 0..3,
+// 8 bytes).  f was chosen by measurement: among all 4096 XOR-linear maps of
+// r's four bits to three, the rocprofv3 counter SQ_LDS_BANK_CONFLICT on
+// gfx950 reads zero for both patterns only when bit 1 of r flips bit 2 of the
+// slot (the map here also lets bit 2 of r flip bit 1); the swizzle of the
+// earlier 32-row tile left the score reads 2-way conflicted.
 __device__ __forceinline__ int swz(int r) {
-  const int m = (r >> 1) & 7;
-  return ((m & 1) << 2) | (m >> 1);
+  return (((r >> 1) & 1) << 2) | (((r >> 2) & 1) << 1);
 }
 
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
 typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8;
+
+// One wave-wide 16-byte-per-lane copy into LDS at lds_dst + 16 * lane, from
+// sbase + voff (sbase uniform, in SGPRs) or from a per-lane address.  M0
+// carries the LDS address; it is declared clobbered (the compiler keeps
+// nothing in it across the copy) rather than saved and restored.
+__device__ __forceinline__ void copy_to_lds_sv(uint32_t voff, const void* sbase, uint32_t lds_dst) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1 nt"
+      :
+      : "v"(voff), "s"(sbase), "s"(lds_dst)
+      : "memory", "m0");
+}
+
+__device__ __forceinline__ void copy_to_lds_v(const void* src, uint32_t lds_dst) {
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off nt"
+      :
+      : "v"((uint64_t)(uintptr_t)src), "s"(lds_dst)
+      : "memory", "m0");
+}
+
+// Maxima of values the compiler cannot prove canonical (MFMA results): as
+// plain v_max instructions, without the canonicalising v_max x, x it would
+// put before each operand.
+__device__ __forceinline__ float max2(float x, float y) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(x), "v"(y));
+  return r;
+}
+__device__ __forceinline__ float max3(float x, float y, float z) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(y), "v"(z));
+  return r;
+}
 
 // The O accumulators are written by MFMAs the compiler does not see; before
 // ordinary code reads or writes them, let the last of those MFMAs retire
@@ -100,18 +150,47 @@ __device__ __forceinline__ void settle(f32x16_t (&acc)[kNTiles]) {
   for (int n = 0; n < kNTiles; ++n) asm volatile("" : "+a"(acc[n]));
 }
 
-template <bool SPARSE, bool PAGED, int NW>
+// Barrier with the newest k tiles' copies (of kc copies each) still in flight.
+template <int kc>
+__device__ __forceinline__ void barrier_tiles_in_flight(int k) {
+  switch (k) {
+    case 0: barrier_in_flight<0>(); break;
+    case 1: barrier_in_flight<kc>(); break;
+    case 2: barrier_in_flight<2 * kc>(); break;
+    case 3: barrier_in_flight<3 * kc>(); break;
+    case 4: barrier_in_flight<4 * kc>(); break;
+    case 5: barrier_in_flight<5 * kc>(); break;
+    default: barrier_in_flight<6 * kc>(); break;
+  }
+}
+
+// TABLE: rows through the LDS row table (a paged cache, or SPARSE lists);
+// otherwise a contiguous cache, whose tiles are consecutive rows.
+template <bool SPARSE, bool TABLE, int NW>
 __global__ __launch_bounds__(64 * NW, 1) void mla_split_kernel(const MlaArgs a) {
   constexpr int kThreads = 64 * NW;
-  constexpr int kDmaPerWave = kDmaPerTile / NW;
-  static_assert(kDmaPerTile % NW == 0, "copies split evenly over the waves");
+  constexpr int kBuffers = kBuffersOf<TABLE>;
+  constexpr int kAhead = kBuffers - 2;                   // tiles requested ahead
+  constexpr int kPerWave = kTileChunks / NW;             // 16-byte slots one wave copies per tile
+  constexpr int kCopies = (kPerWave + 63) / 64;          // copy instructions per wave and tile
+  constexpr int kLastLanes = kPerWave - 64 * (kCopies - 1);  // lanes of the last one
+  constexpr int kCopyStride = kKSteps / kCopies;          // k-steps between two copies
+  constexpr int kHG = NW;                                // 32-head groups of the workgroup
+  constexpr int kNT = kNTiles / NW;                      // 32-dim output tiles of one wave
+  constexpr int kPStart = kKSteps - kHG * kNT;           // first k-step with a P.V MFMA
+  static_assert(kTileChunks % NW == 0 && kLastLanes > 0 && kLastLanes <= 64, "copy split");
+  static_assert(kCopyStride >= 1 && kPStart >= 1, "fits the k-steps");
+  static_assert(!SPARSE || TABLE, "gathered rows go through the row table");
   const float NEG_INF = -__builtin_inff();
 
   __shared__ __attribute__((aligned(16))) char tiles[kBuffers * kTileBytes];
-  __shared__ __attribute__((aligned(16))) uint32_t rows[kRowTable];
+  // P of two consecutive tiles for all heads, each in the 32x32x16 A layout:
+  // head group hg at [hg][lane] (16 bytes)
+  __shared__ __attribute__((aligned(16))) char pbuf[2][kPBytes];
+  __shared__ __attribute__((aligned(16))) uint32_t rows[TABLE ? kRowTable : 4];
   __shared__ int first_valid;
   // bit t: tile t holds a position without a token (its scores need the mask)
-  __shared__ uint32_t tile_pad[(kMaxTiles + 3 + 31) / 32];
+  __shared__ uint32_t tile_pad[TABLE ? (kMaxTiles + 32) / 32 : 1];
   // restart votes: iteration u votes in slot u % 3, every wave reads it after
   // the iteration's barrier, and iteration u + 2 clears it, so a fast wave
   // never touches a vote a slow wave has yet to read
@@ -119,142 +198,152 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_split_kernel(const MlaArgs a) 
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int half = lane >> 5;   // 32-lane half
-  const int lj = lane & 31;
+  const int l16 = lane & 15, g4 = lane >> 4, half = lane >> 5;
   const int split = blockIdx.x;
   const int b = blockIdx.z;
-  const int h0 = blockIdx.y * (NW * kHeadsPerWave) + wave * kHeadsPerWave;
+  const int hw = blockIdx.y * (NW * kHeadsPerWave);   // the workgroup's first head
+  const int h0 = hw + wave * kHeadsPerWave;           // this wave's score heads
+  const int d0 = wave * (kDc / NW);                   // this wave's output dims
 
   int N;
   if constexpr (SPARSE) {
     N = a.k_sel;
   } else {
-    const int cap = PAGED ? a.page_size * a.max_pages : a.S_max;
+    const int cap = a.page_table ? a.page_size * a.max_pages : a.S_max;
     N = max(0, min(a.seq_lens[b], cap));
   }
   const int per = ((N + a.num_splits - 1) / a.num_splits + kTile - 1) / kTile * kTile;
   const int f_begin = min(N, split * per);
   const int f_end = min(N, f_begin + per);
-  int n_tiles = min((f_end - f_begin + kTile - 1) / kTile, kMaxTiles);
+  const int n_tok = f_end - f_begin;
+  int n_tiles = min((n_tok + kTile - 1) / kTile, kMaxTiles);
 
-  // Q^T fragments (B operand): lane holds head h0 + lj, dims 16 ks + 8 half + [0, 8)
-  bf16x8_t qf[kKSteps];
+  // Q^T fragments (B operand of the 16x16x32 scores): for head group hh the
+  // lane holds head h0 + 16 hh + l16, dims 32 ks + 8 g4 + [0, 8)
+  bf16x8_t qf[kKSteps][2];
   {
-    const uint16_t* qrow = a.q + ((size_t)b * a.H + h0 + lj) * kDq + 8 * half;
 #pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = *(const bf16x8_t*)(qrow + 16 * ks);
+    for (int hh = 0; hh < 2; ++hh) {
+      const uint16_t* qrow = a.q + ((size_t)b * a.H + h0 + 16 * hh + l16) * kDq + 8 * g4;
+#pragma unroll
+      for (int ks = 0; ks < kKSteps; ++ks) qf[ks][hh] = *(const bf16x8_t*)(qrow + 32 * ks);
+    }
   }
 
-  // ---- row table: cache row of every position of the split and of the
-  // three tiles past it.  Flag kPad marks a position without a token; its
-  // entry still names a row of finite data (a real row of the same split),
-  // so that P = 0 times it stays 0.
-  if (threadIdx.x < (kMaxTiles + 3 + 31) / 32) tile_pad[threadIdx.x] = 0u;
   if (threadIdx.x == 0) {
     first_valid = 0x7fffffff;
     restart_vote[0] = restart_vote[1] = restart_vote[2] = 0;
   }
-  __syncthreads();
-  const int n_rows = n_tiles > 0 ? (n_tiles + 3) * kTile : 0;
-  for (int i = threadIdx.x; i < n_rows; i += kThreads) {
-    const int f = f_begin + i;
-    uint32_t e;
-    if constexpr (SPARSE) {
-      const int t = f < f_end ? a.idx[(size_t)b * a.k_sel + f] : -1;
-      const bool ok = t >= 0 && t < a.S_max;
-      e = ok ? (uint32_t)b * (uint32_t)a.S_max + (uint32_t)t : kPad;
-      if (ok) atomicMin(&first_valid, i);
-    } else {
-      const bool ok = f < f_end;
-      const int t = ok ? f : f_end - 1;
-      uint32_t row;
-      if constexpr (PAGED) {
-        const int phys = a.page_table[(size_t)b * a.max_pages + (t >> a.log2_page)];
-        row = (uint32_t)phys * (uint32_t)a.page_size + (uint32_t)(t & (a.page_size - 1));
+  // ---- row table: cache row of every position of the split and of one
+  // all-padding tile past it.  Flag kPad marks a position without a token;
+  // its entry still names a row of finite data (a real row of the same
+  // split), so that P = 0 times it stays 0.
+  if constexpr (TABLE) {
+    if (threadIdx.x < (kMaxTiles + 32) / 32) tile_pad[threadIdx.x] = 0u;
+    __syncthreads();
+    const int n_rows = (n_tiles + 1) * kTile;
+    for (int i = threadIdx.x; i < n_rows; i += kThreads) {
+      const int f = f_begin + i;
+      uint32_t e;
+      if constexpr (SPARSE) {
+        const int t = f < f_end ? a.idx[(size_t)b * a.k_sel + f] : -1;
+        const bool ok = t >= 0 && t < a.S_max;
+        e = ok ? (uint32_t)b * (uint32_t)a.S_max + (uint32_t)t : kPad;
+        if (ok) atomicMin(&first_valid, i);
       } else {
-        row = (uint32_t)b * (uint32_t)a.S_max + (uint32_t)t;
+        const bool ok = f < f_end;
+        const int t = ok ? f : f_end - 1;
+        const int phys = a.page_table[(size_t)b * a.max_pages + (t >> a.log2_page)];
+        const uint32_t row = (uint32_t)phys * (uint32_t)a.page_size + (uint32_t)(t & (a.page_size - 1));
+        e = row | (ok ? 0u : kPad);
       }
-      e = row | (ok ? 0u : kPad);
+      rows[i] = e;
+      if (e & kPad) atomicOr(&tile_pad[(i / kTile) >> 5], 1u << ((i / kTile) & 31));
     }
-    rows[i] = e;
-    if (e & kPad) atomicOr(&tile_pad[(i / kTile) >> 5], 1u << ((i / kTile) & 31));
-  }
-  __syncthreads();
-  if constexpr (SPARSE) {
-    const int fv = first_valid;
-    if (fv == 0x7fffffff) {
-      n_tiles = 0;  // nothing to attend in this split
-    } else {
-      const uint32_t fb = rows[fv] | kPad;
-      for (int i = threadIdx.x; i < n_rows; i += kThreads)
-        if (rows[i] == kPad) rows[i] = fb;
-      __syncthreads();
+    __syncthreads();
+    if constexpr (SPARSE) {
+      const int fv = first_valid;
+      if (fv == 0x7fffffff) {
+        n_tiles = 0;  // nothing to attend in this split
+      } else {
+        const uint32_t fb = rows[fv] | kPad;
+        for (int i = threadIdx.x; i < n_rows; i += kThreads)
+          if (rows[i] == kPad) rows[i] = fb;
+        __syncthreads();
+      }
     }
+  } else {
+    __syncthreads();
   }
 
   const uint32_t tiles_base = lds_address(tiles);
+  // buffer of tile tix >= -1
   auto buffer = [&](int tix) -> uint32_t {
-    return tiles_base + (uint32_t)(tix & (kBuffers - 1)) * kTileBytes;
+    return tiles_base + (uint32_t)((tix + kBuffers) % kBuffers) * kTileBytes;
   };
+  const uint32_t pbuf_base = lds_address(pbuf);
 
-  // ---- tile copy: wave copy i (of 36) fills slots 64 i + lane; slot q is
-  // row q / 72, stored chunk q % 72, i.e. chunk (q % 72) ^ f(row)
-  // This lane's slot in each copy: tile row r and stored chunk c' (a wave's
-  // copies cover tile rows 32 w / NW .. + 32 / NW - 1).  With 4 waves the
-  // nine slots are kept packed, ten bits each (row within the wave's eight,
-  // chunk); with 2 waves they are recomputed per tile (no registers spare).
-  auto slot_of = [&](uint32_t q) -> uint32_t {  // row | chunk << 8
-    const uint32_t r = q / kChunks;
-    return r | (((q - r * kChunks) ^ swz(r)) << 8);
-  };
-  uint32_t slot_pk[3] = {0u, 0u, 0u};
-  if constexpr (NW == 4) {
+  // ---- tile copy: this wave's copy j fills slots kPerWave * wave + 64 j +
+  // lane; slot q of a tile is row q / 72, stored chunk q % 72, i.e. logical
+  // chunk (q % 72) ^ f(row).  The lane's (row, chunk) of each copy is fixed.
+  uint32_t rc[kCopies];  // row | logical chunk << 8
 #pragma unroll
-    for (int j = 0; j < kDmaPerWave; ++j) {
-      const uint32_t rc = slot_of(64 * (wave * kDmaPerWave + j) + lane);
-      slot_pk[j / 3] |= (((rc & 0xff) - 8 * wave) | ((rc >> 8) << 3)) << (10 * (j % 3));
-    }
+  for (int j = 0; j < kCopies; ++j) {
+    const uint32_t q = (uint32_t)(kPerWave * wave + 64 * j + lane);
+    const uint32_t r = q / kChunks, cs = q - r * kChunks;
+    const uint32_t c = (cs & ~7u) | ((cs & 7u) ^ (uint32_t)swz((int)r));
+    rc[j] = r | (c << 8);
   }
-  auto issue = [&](int tix) {
-    const uint32_t dst = buffer(tix) + 1024u * (uint32_t)(wave * kDmaPerWave);
-    const uint32_t* rt = rows + tix * kTile;
-    constexpr int kBatch = 9;  // row lookups in flight together
-    static_assert(kDmaPerWave % kBatch == 0, "whole batches");
-    uint32_t pk[3] = {slot_pk[0], slot_pk[1], slot_pk[2]};
-    asm volatile("" : "+v"(pk[0]), "+v"(pk[1]), "+v"(pk[2]));  // unpack here, not once per kernel
+  const char* latent = (const char*)a.latent;
+  // Per tile: the copies' sources.  TABLE: each lane's row from the table
+  // (read ahead of the copies, so that no LDS wait lands among the operand
+  // reads); otherwise a uniform base and each lane's offset, rows past the
+  // split end re-reading its last row (finite data; their P is 0).
+  struct CopySrc {
+    uint32_t v[kCopies];
+    const char* base;
+  };
+  auto copy_src = [&](int tix) -> CopySrc {
+    CopySrc c;
+    if constexpr (TABLE) {
+      const uint32_t* rt = rows + tix * kTile;
 #pragma unroll
-    for (int j0 = 0; j0 < kDmaPerWave; j0 += kBatch) {
-      uint32_t rc[kBatch], row[kBatch];  // rc: row | chunk << 8 of this lane's slot
+      for (int j = 0; j < kCopies; ++j) c.v[j] = rt[rc[j] & 0xff] & ~kPad;
+      c.base = latent;
+    } else {
+      c.base = latent + ((size_t)b * a.S_max + f_begin + tix * kTile) * kRowBytes;
+      const uint32_t last = (uint32_t)(min(kTile, n_tok - tix * kTile) - 1);
 #pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        if constexpr (NW == 4) {
-          const uint32_t x = pk[j / 3] >> (10 * (j % 3));
-          rc[j] = (8 * wave + (x & 7)) | (((x >> 3) & 127) << 8);
-        } else {
-          uint32_t q = 64 * (wave * kDmaPerWave + j0 + j) + lane;
-          asm volatile("" : "+v"(q));  // recomputed per tile: registers are the scarce resource
-          rc[j] = slot_of(q);
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < kBatch; ++j) row[j] = rt[rc[j] & 0xff] & ~kPad;
-#pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        const uint64_t chunk = (uint64_t)row[j] * kChunks + (rc[j] >> 8);
-        copy_to_lds((const char*)a.latent + 16 * chunk, dst + 1024u * (j0 + j));
-      }
+      for (int j = 0; j < kCopies; ++j) c.v[j] = min(rc[j] & 0xff, last) * kRowBytes + (rc[j] >> 8) * 16;
     }
+    return c;
+  };
+  // copy j of tile tix: one wave-wide instruction (the last may use part of the wave)
+  auto copy = [&](int tix, int j, const CopySrc& c) {
+    const uint32_t dst = buffer(tix) + 16u * (uint32_t)(kPerWave * wave) + 1024u * j;
+    if (j == kCopies - 1 && lane >= kLastLanes) return;
+    if constexpr (TABLE) copy_to_lds_v(c.base + ((size_t)c.v[j] * kChunks + (rc[j] >> 8)) * 16, dst);
+    else copy_to_lds_sv(c.v[j], c.base, dst);
+  };
+  auto issue = [&](int tix) {
+    const CopySrc c = copy_src(tix);
+#pragma unroll
+    for (int j = 0; j < kCopies; ++j) copy(tix, j, c);
   };
 
-  // ---- per-lane parts of the two LDS read patterns
-  const int sw_lj = swz(lj);
-  const int li = lane & 15, g = lane >> 4;
-  const int r1 = 4 * half + (li >> 2);                 // token of k elements 0..3 (+16 kk, +8)
-  const int c0 = 2 * (g & 1) + ((li >> 1) & 1);        // chunk of dims 32 n + 16 (g&1) + 4 (li&3)
-  const int sw_r1 = swz(r1), sw_r9 = swz(r1 + 8);      // rows + 16 share them
+  // ---- per-lane parts of the LDS read patterns
+  // scores (A of the 16x16x32): row l16, chunk 4 ks + g4
+  const int sw_s = swz(l16);
+  // P.V (B of the 32x32x16 via the transpose read): rows 8 half + (l16 >> 2)
+  // (+ 4 for the second read), chunk d0 / 8 + 4 nt + 2 (g4 & 1) + ((l16 >> 1)
+  // & 1), byte 8 (l16 & 1) within it
+  const int rv = 8 * half + (l16 >> 2);
+  const int cv = 2 * (g4 & 1) + ((l16 >> 1) & 1);
+  const int sw_v0 = swz(rv), sw_v1 = swz(rv + 4);
 
-  // O accumulators: defined (zeroed) by MFMAs with zero operands, so that
-  // they are born in AGPRs and never pass through VGPRs
+  // O accumulators acc[hg * kNT + nt]: heads hw + 32 hg + .., dims d0 + 32 nt
+  // + ..  Defined (zeroed) by MFMAs with zero operands, so that they are born
+  // in AGPRs and never pass through VGPRs.
   f32x16_t acc[kNTiles];
   auto zero_acc = [&]() {
     const bf16x8_t z = {};
@@ -263,168 +352,243 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_split_kernel(const MlaArgs a) 
       asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=a"(acc[n]) : "v"(z));
   };
   zero_acc();
-  // m_run: the head's reference maximum (log2 units); m_seen: largest score so far
-  float m_run = NEG_INF, m_seen = NEG_INF, l_run = 0.f;
-  bf16x8_t pa[2];  // P of the tile whose P.V comes next, bf16, one per 16-token k-step
+  // per head group hh (head h0 + 16 hh + l16): m_run the reference maximum
+  // (log2 units), m_seen the largest score so far, l_run this lane's share
+  // of the softmax denominator
+  float m_run[2] = {NEG_INF, NEG_INF}, m_seen[2] = {NEG_INF, NEG_INF}, l_run[2] = {0.f, 0.f};
+  // S^T of the tile whose softmax comes next: for group hh the lane holds
+  // head 16 hh + l16, tokens 4 g4 + [0, 4)
+  f32x4_t sc[2];
 
-  // Scores of the tile in buffer sbuf (S^T, 32 tokens x 32 heads: lane holds
-  // head lj, tokens 8(v/4) + 4 half + v%4), alternated with the P.V MFMAs of
-  // the tile in buffer pbuf when WITH_PV.
-  auto scores = [&](auto with_pv, uint32_t sbuf, uint32_t pbuf) -> f32x16_t {
-    constexpr bool WITH_PV = decltype(with_pv)::value;
-    // Per-lane LDS addresses, made opaque here so that the compiler keeps
-    // eight per tile instead of an address per read.
-    // A operand of the scores: row lj, chunk c = 2 ks + half, stored at slot
-    // 8 (c / 8) + ((c % 8) ^ f(lj)): so[ks % 4] + 128 (ks / 4).
-    // B operand of P.V: rows r1 + 16 kk and r1 + 8 + 16 kk, chunk c = 4 n +
-    // c0, stored at 8 (c / 8) + ((c % 8) ^ f(row)): vo[n % 2] and
-    // vo[2 + n % 2], + 128 (n / 2) + 16 kk rows.
-    uint32_t so[4], vo[4];
+  // The tile pipeline.  Iteration t (0 <= t <= n_tiles) runs, interleaved
+  // on one instruction stream:
+  //   S: the score MFMAs of tile t + 1 (buffer t + 1),
+  //   X: the softmax of tile t (its scores from iteration t - 1) -> its P to
+  //      pbuf[t % 2],
+  //   P: the P.V MFMAs of tile t - 1 (buffer t - 1, P from pbuf[(t - 1) % 2]),
+  //   C: the copies of tile t + kAhead into the buffer tile t - 2 freed.
+  // The first and last iterations run the same stream on stand-ins: tile -1
+  // has P = 0 (a zeroed P buffer; its tile buffer holds finite data), and
+  // tile n_tiles is all padding (its scores are dropped, its softmax changes
+  // nothing).
+  auto stream = [&](auto with_copies, int t, int slot) {
+    constexpr bool copies = decltype(with_copies)::value;
+    const uint32_t sbuf = buffer(t + 1), vbuf = buffer(t - 1);
+    const uint32_t pin = pbuf_base + (uint32_t)((t + 1) & 1) * kPBytes;  // P of tile t - 1
+    const uint32_t pout = pbuf_base + (uint32_t)(t & 1) * kPBytes + 16u * (uint32_t)(wave * 64 + lane);
+    uint32_t so[2], vo[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      so[j] = sbuf + lj * kRowBytes + 16 * (((2 * j) | half) ^ sw_lj);
-      asm volatile("" : "+v"(so[j]));
+    for (int j = 0; j < 2; ++j) {
+      so[j] = sbuf + l16 * kRowBytes + 16 * ((4 * j + g4) ^ sw_s);
+      const int cb = d0 / 8;  // 8 (d0 / 64) + 0: the wave's dims start on an 8-chunk group
+      vo[j] = vbuf + rv * kRowBytes + 16 * (cb + ((4 * j + cv) ^ sw_v0)) + 8 * (l16 & 1);
+      vo[2 + j] = vbuf + (rv + 4) * kRowBytes + 16 * (cb + ((4 * j + cv) ^ sw_v1)) + 8 * (l16 & 1);
+      asm volatile("" : "+v"(so[j]), "+v"(vo[j]), "+v"(vo[2 + j]));
     }
-    if constexpr (WITH_PV) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        vo[j] = pbuf + r1 * kRowBytes + 16 * ((4 * j + c0) ^ sw_r1) + 8 * (li & 1);
-        vo[2 + j] = pbuf + (r1 + 8) * kRowBytes + 16 * ((4 * j + c0) ^ sw_r9) + 8 * (li & 1);
-        asm volatile("" : "+v"(vo[j]), "+v"(vo[2 + j]));
-      }
-    }
-    auto aread = [&](int ks) -> bf16x8_t {
-      return *(const lds_bf16x8*)(uintptr_t)(so[ks & 3] + 128 * (ks >> 2));
+    auto aread = [&](int k) -> bf16x8_t {  // chunk 4 k + g4 = 8 (k / 2) + (4 (k % 2) + g4)
+      return *(const lds_bf16x8*)(uintptr_t)(so[k & 1] + 128 * (k >> 1));
     };
-    auto vread = [&](int p) -> bf16x8_t {  // p = 16 kk + n
-      const int kk = p >> 4, n = p & 15;
-      const uint32_t imm = 128 * (n >> 1) + 16 * kk * kRowBytes;
-      const bf16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(uintptr_t)(vo[n & 1] + imm));
-      const bf16x4_t v2 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(uintptr_t)(vo[2 + (n & 1)] + imm));
+    auto vread = [&](int nt) -> bf16x8_t {  // chunk d0 / 8 + 4 nt + cv
+      const uint32_t imm = 128 * (nt >> 1);
+      const bf16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(uintptr_t)(vo[nt & 1] + imm));
+      const bf16x4_t v2 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(uintptr_t)(vo[2 + (nt & 1)] + imm));
       return __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7);
     };
-    bf16x8_t ar[kRing], vr[kRing];
+
+    // X's inputs: padding of tile t; the copies' sources of tile t + kAhead
+    bool pad[4] = {false, false, false, false};
+    bool padded;
+    if constexpr (TABLE) {
+      padded = (tile_pad[t >> 5] >> (t & 31)) & 1u;
+      const uint4 e = *(const uint4*)(rows + t * kTile + 4 * g4);
+      pad[0] = e.x & kPad; pad[1] = e.y & kPad; pad[2] = e.z & kPad; pad[3] = e.w & kPad;
+    } else {
+      padded = t * kTile + kTile > n_tok;
 #pragma unroll
-    for (int j = 0; j < kRing; ++j) {
-      ar[j] = aread(j);
-      if constexpr (WITH_PV) vr[j] = vread(j);
+      for (int i = 0; i < 4; ++i) pad[i] = t * kTile + 4 * g4 + i >= n_tok;
     }
-    f32x16_t s;
-    asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(ar[0]), "v"(qf[0]));
+    CopySrc csrc;
+    if constexpr (copies) csrc = copy_src(t + kAhead);
+
+    // P of tile t - 1 for every head group, and the first value fragments
+    bf16x8_t pa[kHG];
+#pragma unroll
+    for (int hg = 0; hg < kHG; ++hg) pa[hg] = *(const lds_bf16x8*)(uintptr_t)(pin + 16u * (hg * 64 + lane));
+    bf16x8_t ar[kRing], vr[2];
+#pragma unroll
+    for (int j = 0; j < kRing; ++j) ar[j] = aread(j);
+    vr[0] = vread(0);
+    vr[1] = vread(1);
+
+    f32x4_t sn[2];
+    float m4[2], mx[2], nmu[2], pe[2][4];
+    uint32_t pk[2][2];
 #pragma unroll
     for (int i = 0; i < kKSteps; ++i) {
-      if (i > 0)
-        asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
-                     : "+v"(s) : "v"(ar[i % kRing]), "v"(qf[i]));
+      // S: scores of tile t + 1, k-step i, both head groups
+      if (i == 0) {
+        asm volatile("s_nop 2\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(sn[0]) : "v"(ar[0]), "v"(qf[0][0]));
+        asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(sn[1]) : "v"(ar[0]), "v"(qf[0][1]));
+      } else {
+        asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(sn[0]) : "v"(ar[i % kRing]), "v"(qf[i][0]));
+        asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(sn[1]) : "v"(ar[i % kRing]), "v"(qf[i][1]));
+      }
       if (i + kRing < kKSteps) ar[i % kRing] = aread(i + kRing);
-      if constexpr (WITH_PV) {
-        if (i < kPvSteps) {
-          asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
-                       : "+a"(acc[i & (kNTiles - 1)]) : "v"(pa[i >> 4]), "v"(vr[i % kRing]));
-          if (i + kRing < kPvSteps) vr[i % kRing] = vread(i + kRing);
+      // P: P.V of tile t - 1, one (output tile, head group) per k-step from kPStart
+      if (i >= kPStart) {
+        const int u = i - kPStart, nt = u / kHG, hg = u % kHG;
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                     : "+a"(acc[hg * kNT + nt]) : "v"(pa[hg]), "v"(vr[nt & 1]));
+        if (hg == kHG - 1 && nt + 2 < kNT) vr[nt & 1] = vread(nt + 2);
+      }
+      // X: softmax of tile t, one piece per k-step
+      if (i == 0) {
+        if (padded) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (pad[q]) sc[0][q] = sc[1][q] = NEG_INF;
         }
+      } else if (i == 1) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) m4[hh] = max3(sc[hh][0], sc[hh][1], max2(sc[hh][2], sc[hh][3]));
+      } else if (i == 2) {
+        // the head's 16 tokens are on the four lanes l16 + 16 g
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const auto w = __builtin_amdgcn_permlane16_swap(__float_as_uint(m4[hh]), __float_as_uint(m4[hh]), false, false);
+          m4[hh] = max2(__uint_as_float(w[0]), __uint_as_float(w[1]));
+        }
+      } else if (i == 3) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const auto w = __builtin_amdgcn_permlane32_swap(__float_as_uint(m4[hh]), __float_as_uint(m4[hh]), false, false);
+          mx[hh] = max2(__uint_as_float(w[0]), __uint_as_float(w[1])) * a.scale_log2;
+        }
+      } else if (i == 4) {
+        // a head's first scores set its reference (its O is still zero); a
+        // later score past the reference by more than kTau asks for a restart
+        bool jump = false;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          m_seen[hh] = max2(m_seen[hh], mx[hh]);
+          jump |= mx[hh] > m_run[hh] + kTau && m_run[hh] != NEG_INF;
+          m_run[hh] = m_run[hh] == NEG_INF ? mx[hh] : m_run[hh];
+          nmu[hh] = m_run[hh] == NEG_INF ? 0.f : -m_run[hh];
+        }
+        if (jump) restart_vote[slot] = 1;
+      } else if (i >= 5 && i < 9) {
+        const int hh = (i - 5) >> 1, q0 = 2 * ((i - 5) & 1);
+        pe[hh][q0] = fast_exp2(__builtin_fmaf(sc[hh][q0], a.scale_log2, nmu[hh]));
+        pe[hh][q0 + 1] = fast_exp2(__builtin_fmaf(sc[hh][q0 + 1], a.scale_log2, nmu[hh]));
+      } else if (i == 9) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          l_run[hh] += (pe[hh][0] + pe[hh][1]) + (pe[hh][2] + pe[hh][3]);
+          pk[hh][0] = pack_bf16x2(pe[hh][0], pe[hh][1]);
+          pk[hh][1] = pack_bf16x2(pe[hh][2], pe[hh][3]);
+        }
+      } else if (i == 10) {
+        // to the A layout of P.V: lane l takes head l % 32 and tokens
+        // 8 (l / 32) + [0, 8) -- rows 0 and 1 (2 and 3) of 16 lanes trade
+        // the group they do not keep -- and out to LDS for every wave
+        const auto x0 = __builtin_amdgcn_permlane16_swap(pk[0][0], pk[1][0], false, false);
+        const auto x1 = __builtin_amdgcn_permlane16_swap(pk[0][1], pk[1][1], false, false);
+        uint4 v;
+        v.x = x0[0];  // tokens 8 half + 0, 1
+        v.y = x1[0];  // + 2, 3
+        v.z = x0[1];  // + 4, 5
+        v.w = x1[1];  // + 6, 7
+        *(lds_bf16x8*)(uintptr_t)pout = __builtin_bit_cast(bf16x8_t, v);
+      }
+      // C: copies of tile t + kAhead spread over the k-steps
+      if constexpr (copies) {
+        if (i % kCopyStride == 0 && i / kCopyStride < kCopies) copy(t + kAhead, i / kCopyStride, csrc);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    // the scores are read by ordinary code next: let the last MFMA retire
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s));
-    return s;
+    // ordinary code reads the scores next: let the last MFMA retire first
+    asm volatile("s_nop 7\n\ts_nop 7" : "+v"(sn[0]), "+v"(sn[1]));
+    sc[0] = sn[0];
+    sc[1] = sn[1];
   };
 
-  // Online softmax of tile tix from its scores s; leaves its P in pa and
-  // votes for a restart in restart_vote[slot] when a maximum jumps.
-  auto softmax = [&](f32x16_t s, int tix, int slot) {
-    // maximum over the raw scores (the scale is positive), masking only in
-    // tiles that hold positions without a token
-    float mx = NEG_INF;
-    if ((tile_pad[tix >> 5] >> (tix & 31)) & 1u) {
-      const uint32_t* rt = rows + tix * kTile + 4 * half;
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const uint4 e = *(const uint4*)(rt + 8 * q4);
-        const uint32_t ev[4] = {e.x, e.y, e.z, e.w};
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int v = 4 * q4 + u;
-          if (ev[u] & kPad) s[v] = NEG_INF;
-          mx = fmaxf(mx, s[v]);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[v]);
-    }
-    // lanes lj and lj + 32 hold the two halves of head lj's tokens
-    {
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * a.scale_log2;
-    }
-    m_seen = fmaxf(m_seen, mx);
-    // a head's first scores set its reference (its O is still zero); a later
-    // score past the reference by more than kTau asks for a restart
-    if (m_run != NEG_INF && mx > m_run + kTau) restart_vote[slot] = 1;
-    if (m_run == NEG_INF) m_run = mx;
-    const float nmu = m_run == NEG_INF ? 0.f : -m_run;
-    float psum = 0.f;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      s[v] = fast_exp2(__builtin_fmaf(s[v], a.scale_log2, nmu));
-      psum += s[v];
-    }
-    l_run += psum;
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      uint4 p;
-      p.x = pack_bf16x2(s[8 * kk + 0], s[8 * kk + 1]);
-      p.y = pack_bf16x2(s[8 * kk + 2], s[8 * kk + 3]);
-      p.z = pack_bf16x2(s[8 * kk + 4], s[8 * kk + 5]);
-      p.w = pack_bf16x2(s[8 * kk + 6], s[8 * kk + 7]);
-      pa[kk] = __builtin_bit_cast(bf16x8_t, p);
-    }
+  // stand-ins for tile -1: zero P, finite values in its tile buffer
+  auto zero_standins = [&]() {
+    uint4* z = (uint4*)(tiles + (kBuffers - 1) * kTileBytes);
+    for (int i = threadIdx.x; i < kTileBytes / 16; i += kThreads) z[i] = make_uint4(0u, 0u, 0u, 0u);
+    uint4* zp = (uint4*)pbuf[1];
+    for (int i = threadIdx.x; i < kPBytes / 16; i += kThreads) zp[i] = make_uint4(0u, 0u, 0u, 0u);
   };
 
-  // Prologue: tiles 0..2 requested, tile 0 scored and its softmax taken,
-  // tile 1 complete in LDS.  (A prologue never votes: its reference is unset
-  // or already the largest score seen.)
-  // Tiles past the split are never copied (their positions are all masked,
-  // so whatever their buffers hold never reaches a result).
+  // Prologue: tiles 0..kAhead - 1 requested, tile 0 scored, tile 1 complete.
   auto prime = [&]() {
-    issue(0);
-    if (n_tiles > 1) issue(1);
-    if (n_tiles > 2) issue(2);
-    if (n_tiles > 2) barrier_in_flight<2 * kDmaPerWave>();  // tile 0 complete
-    else if (n_tiles > 1) barrier_in_flight<kDmaPerWave>();
-    else barrier_in_flight<0>();
-    softmax(scores(std::false_type{}, buffer(0), 0u), 0, 0);
-    if (n_tiles > 2) barrier_in_flight<kDmaPerWave>();  // tile 1 complete
-    else barrier_in_flight<0>();
+    zero_standins();
+    const int first = min(n_tiles, kAhead);
+    for (int t = 0; t < first; ++t) issue(t);
+    barrier_tiles_in_flight<kCopies>(first - 1);  // tile 0 complete
+    {
+      const uint32_t sbuf = buffer(0);
+      uint32_t so[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        so[j] = sbuf + l16 * kRowBytes + 16 * ((4 * j + g4) ^ sw_s);
+        asm volatile("" : "+v"(so[j]));
+      }
+      auto aread = [&](int k) -> bf16x8_t {
+        return *(const lds_bf16x8*)(uintptr_t)(so[k & 1] + 128 * (k >> 1));
+      };
+      bf16x8_t ar[kRing];
+#pragma unroll
+      for (int j = 0; j < kRing; ++j) ar[j] = aread(j);
+#pragma unroll
+      for (int i = 0; i < kKSteps; ++i) {
+        if (i == 0) {
+          asm volatile("s_nop 2\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(sc[0]) : "v"(ar[0]), "v"(qf[0][0]));
+          asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(sc[1]) : "v"(ar[0]), "v"(qf[0][1]));
+        } else {
+          asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(sc[0]) : "v"(ar[i % kRing]), "v"(qf[i][0]));
+          asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(sc[1]) : "v"(ar[i % kRing]), "v"(qf[i][1]));
+        }
+        if (i + kRing < kKSteps) ar[i % kRing] = aread(i + kRing);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    asm volatile("s_nop 7\n\ts_nop 7" : "+v"(sc[0]), "+v"(sc[1]));
+    barrier_tiles_in_flight<kCopies>(max(first - 2, 0));  // tile 1 complete, stand-ins zeroed
   };
 
-  // Iteration t: request tile t + 3 if the split has it (into the buffer
-  // tile t - 1 freed), P.V of tile t alternated with the scores of tile t + 1
-  // (for the last t a padding tile, all flagged: its softmax changes
-  // nothing), then the softmax of tile t + 1.  Once no tile is requested the
-  // barrier waits for every copy, so none is in flight when the workgroup
-  // ends.  A restart leaves the tile loop and runs the prologue again.
+  // Iteration t of the pipeline above, then a barrier after which tile t + 2
+  // is complete in LDS and tile t's P in pbuf for every wave (only the copies
+  // of later tiles may be in flight), and the buffer of tile t - 1 is free.
+  // A restart leaves the loop and runs the prologue again.
   while (n_tiles > 0) {
     prime();
     int slot = 0;
     bool again = false;
-    for (int t = 0; t < n_tiles; ++t) {
+    // while tiles remain to be requested (copies in every iteration), then the tail
+    const int n_copying = max(n_tiles - kAhead, 0);
+    int t = 0;
+    for (; t < n_copying; ++t) {
       if (threadIdx.x == 0) restart_vote[slot == 2 ? 0 : slot + 1] = 0;  // iteration t - 2's
-      const bool more = t + 3 < n_tiles;
-      if (more) issue(t + 3);
-      const f32x16_t s = scores(std::true_type{}, buffer(t + 1), buffer(t));
-      softmax(s, t + 1, slot);
-      // tile t + 2 complete in LDS for every wave (only tile t + 3 may still
-      // be in flight); buffer of tile t free for reuse
-      if (more) barrier_in_flight<kDmaPerWave>();
-      else barrier_in_flight<0>();
+      stream(std::true_type{}, t, slot);
+      barrier_in_flight<(kAhead - 2) * kCopies>();  // tiles t + 3 .. t + kAhead in flight
       if (restart_vote[slot]) {
         again = true;
         break;
       }
       slot = slot == 2 ? 0 : slot + 1;
+    }
+    if (!again) {
+      for (; t <= n_tiles; ++t) {
+        if (threadIdx.x == 0) restart_vote[slot == 2 ? 0 : slot + 1] = 0;
+        stream(std::false_type{}, t, slot);
+        barrier_tiles_in_flight<kCopies>(min(max(n_tiles - 1 - (t + 2), 0), kAhead - 2));
+        if (restart_vote[slot]) {
+          again = true;
+          break;
+        }
+        slot = slot == 2 ? 0 : slot + 1;
+      }
     }
     if (!again) break;
     // some head's maximum jumped: redo the split with every head's reference
@@ -434,37 +598,411 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_split_kernel(const MlaArgs a) 
     if (threadIdx.x == 0) restart_vote[0] = restart_vote[1] = restart_vote[2] = 0;
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::);  // in-flight MFMAs retire first
     zero_acc();
-    m_run = m_seen;
-    l_run = 0.f;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      m_run[hh] = m_seen[hh];
+      l_run[hh] = 0.f;
+    }
   }
   settle(acc);
 
   // unnormalised partials: O (relative to m_run), m_run and l per head; the
   // combine merges the splits and divides
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const size_t row0 = (size_t)b * a.H + h0;
+  float l_tot[2];
 #pragma unroll
-  for (int n = 0; n < kNTiles; ++n)
+  for (int hh = 0; hh < 2; ++hh) {
+    const auto w16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(l_run[hh]), __float_as_uint(l_run[hh]),
+                                                      false, false);
+    const float x = __uint_as_float(w16[0]) + __uint_as_float(w16[1]);
+    const auto w32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    l_tot[hh] = __uint_as_float(w32[0]) + __uint_as_float(w32[1]);
+  }
+  const size_t roww = (size_t)b * a.H + hw;
+  const int lj = lane & 31;
 #pragma unroll
-    for (int v = 0; v < 16; ++v)
-      a.part_o[((row0 + 8 * (v / 4) + 4 * half + (v % 4)) * a.num_splits + split) * kDc + 32 * n + lj] =
-          acc[n][v];
-  if (half == 0) {
-    a.part_lse[(row0 + lj) * a.num_splits + split] = l_tot > 0.f ? m_run : NEG_INF;
-    a.part_l[(row0 + lj) * a.num_splits + split] = l_tot;
+  for (int hg = 0; hg < kHG; ++hg)
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        a.part_o[((roww + 32 * hg + 8 * (v / 4) + 4 * half + (v % 4)) * a.num_splits + split) * kDc + d0 +
+                 32 * nt + lj] = acc[hg * kNT + nt][v];
+  if (g4 == 0) {
+    const size_t row0 = (size_t)b * a.H + h0;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const size_t r = (row0 + 16 * hh + l16) * a.num_splits + split;
+      a.part_lse[r] = l_tot[hh] > 0.f ? m_run[hh] : NEG_INF;
+      a.part_l[r] = l_tot[hh];
+    }
   }
 }
 
-template <bool SPARSE, bool PAGED, int NW>
+// ---------------------------------------------------------------------------
+// The contiguous-cache kernel (dense MLA over [B, S_max, 576], 128 heads per
+// workgroup): tiles of 32 rows and 32x32x16 MFMAs throughout.  A 32x32x16
+// MFMA keeps the matrix core busy for 32 cycles, in which the wave can issue
+// about four other instructions; with 16x16x32 scores there is half that
+// room per instruction.  So here every k-step of the scores is one MFMA for
+// the wave's 32 heads, and the softmax, the operand reads and the copies fit
+// between the MFMAs.
+//
+// Per tile t the stream is: S(t + 1) interleaved with the first P.V MFMAs of
+// tile t, then the rest of P.V(t) interleaved with the softmax of tile t + 1
+// (its scores are complete by then), which sends P(t + 1) to the other waves
+// through LDS.  The S^T accumulator layout of the 32x32x16 MFMA (lane: head
+// lane % 32, tokens 8 (v / 4) + 4 (lane / 32) + v % 4) is the A layout P.V
+// needs for each 16-token k-step, with the token order permuted the same way
+// on the value's side, so P needs no shuffle.
+//
+// LDS: four 36 KB tile buffers (tiles t (P.V), t + 1 (scores), t + 2 and
+// t + 3 in flight) and two 8 KB buffers of P: 160 KB, all of it.  The
+// restart vote therefore rides on P itself: probabilities are never negative,
+// so a wave that sees a maximum jump sets the sign bit of the first value of
+// its P fragment (head group w, lane 0); every wave reads that value back
+// with the fragment and leaves the tile loop on it.
+constexpr int kT2 = 32;                       // tokens per tile
+constexpr int kT2Bytes = kT2 * kRowBytes;     // 36864
+constexpr int kT2Buffers = 4;
+constexpr int kT2Copies = kT2 * kChunks / 64 / 4;  // 9 wave copies per wave and tile
+constexpr int kP2Bytes = 2 * 4 * 64 * 16;     // P of one tile: 2 k-steps x 4 head groups x 64 lanes x 16 B
+static_assert(kT2Buffers * kT2Bytes + 2 * kP2Bytes <= 160 * 1024, "fits the LDS");
+
+// Chunk permutation for the 32-row tiles, measured conflict-free (rocprofv3
+// SQ_LDS_BANK_CONFLICT = 0 on gfx950) for both read patterns of this kernel:
+// score reads (lane l: row l % 32, chunk 2 k + l / 32, 16 bytes) and
+// transpose reads (rows 16 ks + 4 (l / 32) + (l % 16) / 4 and + 8).
+__device__ __forceinline__ int swz32(int r) {
+  const int m = (r >> 1) & 7;
+  return ((m & 1) << 2) | (m >> 1);
+}
+
+__global__ __launch_bounds__(256, 1) void mla_contig_kernel(const MlaArgs a) {
+  constexpr int kKS = kDq / 16;          // 36 score k-steps of 16 dims
+  constexpr int kNT = kDc / 4 / 32;      // 4 output tiles of 32 dims per wave
+  constexpr int kP1 = 8;                 // P.V MFMAs in the score phase (of 32)
+  const float NEG_INF = -__builtin_inff();
+  __shared__ __attribute__((aligned(16))) char tiles[kT2Buffers * kT2Bytes];
+  __shared__ __attribute__((aligned(16))) char pbuf[2][kP2Bytes];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int half = lane >> 5, lj = lane & 31, li = lane & 15, g = lane >> 4;
+  const int split = blockIdx.x;
+  const int b = blockIdx.z;
+  const int hw = blockIdx.y * 128;       // the workgroup's first head
+  const int h0 = hw + wave * 32;         // this wave's score heads
+  const int d0 = wave * 128;             // this wave's output dims
+
+  const int N = max(0, min(a.seq_lens[b], a.S_max));
+  const int per = ((N + a.num_splits - 1) / a.num_splits + kT2 - 1) / kT2 * kT2;
+  const int f_begin = min(N, split * per);
+  const int n_tok = min(N, f_begin + per) - f_begin;
+  const int n_tiles = (n_tok + kT2 - 1) / kT2;
+
+  // Q^T fragments (B of the scores): lane holds head h0 + lj, dims 16 k + 8 half + [0, 8)
+  bf16x8_t qf[kKS];
+  {
+    const uint16_t* qrow = a.q + ((size_t)b * a.H + h0 + lj) * kDq + 8 * half;
+#pragma unroll
+    for (int k = 0; k < kKS; ++k) qf[k] = *(const bf16x8_t*)(qrow + 16 * k);
+  }
+
+  const uint32_t tiles_base = lds_address(tiles);
+  const uint32_t pbuf_base = lds_address(pbuf);
+  auto buffer = [&](int tix) -> uint32_t { return tiles_base + (uint32_t)(tix & 3) * kT2Bytes; };
+
+  // ---- copies: wave copy j fills slots 576 wave + 64 j + lane of a tile;
+  // slot q is row q / 72, stored chunk q % 72, logical chunk (q % 72) ^ f(row).
+  // Byte offset within the tile of this lane's source for each copy, for
+  // whole tiles; the last tile clamps rows past the split end to its last.
+  uint32_t coff2[(kT2Copies + 1) / 2];  // two 16-bit offsets per register
+#pragma unroll
+  for (int j = 0; j < kT2Copies; ++j) {
+    const uint32_t q = (uint32_t)(576 * wave + 64 * j + lane);
+    const uint32_t r = q / kChunks, cs = q - r * kChunks;
+    const uint32_t c = (cs & ~7u) | ((cs & 7u) ^ (uint32_t)swz32((int)r));
+    const uint32_t off = r * kRowBytes + c * 16;  // < 2^16
+    if (j % 2 == 0) coff2[j / 2] = off;
+    else coff2[j / 2] |= off << 16;
+  }
+  auto coff = [&](int j) -> uint32_t { return j % 2 == 0 ? coff2[j / 2] & 0xffffu : coff2[j / 2] >> 16; };
+  const char* latent = (const char*)a.latent + ((size_t)b * a.S_max + f_begin) * kRowBytes;
+  auto tile_src = [&](int tix) -> const char* { return latent + (size_t)tix * kT2Bytes; };
+  // source offset of copy j for tile tix (rows past the split end re-read its
+  // last row: finite data whose P is 0)
+  auto copy_off = [&](int tix, int j) -> uint32_t {
+    const int rows_here = n_tok - tix * kT2;
+    const uint32_t o = coff(j);
+    if (rows_here >= kT2) return o;
+    const uint32_t r = o / kRowBytes;
+    return min(r, (uint32_t)(rows_here - 1)) * kRowBytes + (o - r * kRowBytes);
+  };
+  auto copy = [&](int tix, int j) {
+    copy_to_lds_sv(copy_off(tix, j), tile_src(tix), buffer(tix) + 16u * (uint32_t)(576 * wave) + 1024u * j);
+  };
+  auto issue = [&](int tix) {
+#pragma unroll
+    for (int j = 0; j < kT2Copies; ++j) copy(tix, j);
+  };
+
+  // ---- per-lane parts of the LDS reads
+  const int sw_a = swz32(lj);                 // scores: row lj, chunk 2 k + half
+  const int rv = 4 * half + (li >> 2);         // values: rows 16 ks + rv and + 8
+  const int cv = 2 * (g & 1) + ((li >> 1) & 1);  // chunk 16 wave + 4 nt + cv, byte 8 (li & 1)
+  const int sw_v0 = swz32(rv), sw_v1 = swz32(rv + 8);  // the same for every ks (rows + 16)
+
+  f32x16_t acc[16];  // [hg * kNT + nt]: heads hw + 32 hg + .., dims d0 + 32 nt + ..
+  auto zero_acc = [&]() {
+    const bf16x8_t z = {};
+#pragma unroll
+    for (int n = 0; n < 16; ++n)
+      asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=a"(acc[n]) : "v"(z));
+  };
+  zero_acc();
+  // head h0 + lj: reference maximum (log2 units), largest score seen, this
+  // lane's share of the denominator
+  float m_run = NEG_INF, m_seen = NEG_INF, l_run = 0.f;
+
+  // Softmax of one tile's scores s (tile tix) in pieces; piece k of 8.  Writes
+  // the tile's P (and this wave's vote) to pbuf[tix & 1].
+  float mxs, nmu;
+  bool jump = false;
+  auto xpiece = [&](f32x16_t& s, int tix, int k) {
+    if (k == 0) {
+      if (tix * kT2 + kT2 > n_tok) {  // positions past the split end
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          if (tix * kT2 + 8 * (v / 4) + 4 * half + (v % 4) >= n_tok) s[v] = NEG_INF;
+      }
+      const float m8a = max3(s[0], s[1], max3(s[2], s[3], s[4]));
+      const float m8b = max3(s[5], s[6], max3(s[7], s[8], s[9]));
+      const float m8c = max3(s[10], s[11], max3(s[12], s[13], max2(s[14], s[15])));
+      mxs = max3(m8a, m8b, m8c);
+    } else if (k == 1) {
+      // lanes lj and lj + 32 hold the two halves of head lj's tokens
+      const auto w = __builtin_amdgcn_permlane32_swap(__float_as_uint(mxs), __float_as_uint(mxs), false, false);
+      const float mx = max2(__uint_as_float(w[0]), __uint_as_float(w[1])) * a.scale_log2;
+      m_seen = max2(m_seen, mx);
+      // a head's first scores set its reference (its O is still zero); a
+      // later score past it by more than kTau asks for a restart
+      jump = mx > m_run + kTau && m_run != NEG_INF;
+      m_run = m_run == NEG_INF ? mx : m_run;
+      nmu = m_run == NEG_INF ? 0.f : -m_run;
+    } else if (k >= 2 && k < 6) {
+      const int v0 = 4 * (k - 2);
+#pragma unroll
+      for (int v = v0; v < v0 + 4; ++v) s[v] = fast_exp2(__builtin_fmaf(s[v], a.scale_log2, nmu));
+      l_run += (s[v0] + s[v0 + 1]) + (s[v0 + 2] + s[v0 + 3]);
+    } else if (k == 6 || k == 7) {
+      // P of k-step ks = k - 6: tokens 16 ks + 8 (v / 4) + 4 half + v % 4 for
+      // v = 8 ks .. 8 ks + 7, in the 32x32x16 A layout
+      const int ks = k - 6;
+      uint4 pv;
+      pv.x = pack_bf16x2(s[8 * ks + 0], s[8 * ks + 1]);
+      pv.y = pack_bf16x2(s[8 * ks + 2], s[8 * ks + 3]);
+      pv.z = pack_bf16x2(s[8 * ks + 4], s[8 * ks + 5]);
+      pv.w = pack_bf16x2(s[8 * ks + 6], s[8 * ks + 7]);
+      if (ks == 0) {
+        // the vote: lane 0's first value carries the wave's sign bit
+        const bool any = __ballot(jump) != 0;
+        if (lane == 0) pv.x = (pv.x & 0xffff7fffu) | (any ? 0x8000u : 0u);
+      }
+      const uint32_t dst = pbuf_base + (uint32_t)(tix & 1) * kP2Bytes + 16u * (uint32_t)((ks * 4 + wave) * 64 + lane);
+      *(lds_bf16x8*)(uintptr_t)dst = __builtin_bit_cast(bf16x8_t, pv);
+    }
+  };
+
+  // Scores of the tile in buffer sbuf (36 MFMAs), optionally interleaved with
+  // P.V MFMAs, copies and softmax pieces via the hook called at each k-step.
+  auto a_addr = [&](uint32_t sbuf, int j) -> uint32_t {  // chunk 2 k + half = 8 (k / 4) + (2 (k % 4) + half)
+    return sbuf + lj * kRowBytes + 16 * ((2 * j + half) ^ sw_a);
+  };
+
+  // P.V MFMA u (0..31): k-step u / 16, output tile (u / 4) % 4, head group u % 4
+  auto pv_mfma = [&](int u, const bf16x8_t (&pa)[4], const bf16x8_t (&vr)[2]) {
+    const int nt = (u >> 2) & 3, hg = u & 3;
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                 : "+a"(acc[hg * kNT + nt]) : "v"(pa[hg]), "v"(vr[nt & 1]));
+  };
+
+  // The stream of iteration t: S(t + 1) || P.V(t) || softmax(t + 1) || copies of t + 3.
+  auto stream = [&](auto with_copies, int t, f32x16_t& s, bool& vote) {
+    constexpr bool copies = decltype(with_copies)::value;
+    const uint32_t sbuf = buffer(t + 1), vbuf = buffer(t);
+    const uint32_t pin = pbuf_base + (uint32_t)(t & 1) * kP2Bytes;
+    uint32_t so[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      so[j] = a_addr(sbuf, j);
+      asm volatile("" : "+v"(so[j]));
+    }
+    uint32_t vo[4];  // rows rv (+ 8), chunk groups 0 and 1 of the wave's 128 dims
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      vo[j] = vbuf + rv * kRowBytes + 16 * (16 * wave + ((4 * j + cv) ^ sw_v0)) + 8 * (li & 1);
+      vo[2 + j] = vbuf + (rv + 8) * kRowBytes + 16 * (16 * wave + ((4 * j + cv) ^ sw_v1)) + 8 * (li & 1);
+      asm volatile("" : "+v"(vo[j]), "+v"(vo[2 + j]));
+    }
+    auto aread = [&](int k) -> bf16x8_t {
+      return *(const lds_bf16x8*)(uintptr_t)(so[k & 3] + 128 * (k >> 2));
+    };
+    // value fragment of k-step ks, output tile nt: chunk 16 wave + 4 nt + cv
+    // = 8 (2 wave + nt / 2) + (4 (nt % 2) + cv), rows + 16 ks
+    auto vread = [&](int ks, int nt) -> bf16x8_t {
+      const uint32_t imm = 128 * (nt >> 1) + 16 * kRowBytes * ks;
+      const bf16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(uintptr_t)(vo[nt & 1] + imm));
+      const bf16x4_t v2 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(uintptr_t)(vo[2 + (nt & 1)] + imm));
+      return __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    auto pread = [&](int ks, int hg) -> bf16x8_t {
+      return *(const lds_bf16x8*)(uintptr_t)(pin + 16u * (uint32_t)((ks * 4 + hg) * 64 + lane));
+    };
+    bf16x8_t pa[4], vr[2];  // P fragments of one k-step (head groups), value fragments
+    // value fragments: (ks, nt) for MFMAs 16 ks + 4 nt .. + 3, two in flight
+    auto vload = [&](int u) {  // load the fragment MFMA u first needs
+      const int ks = u >> 4, nt = (u >> 2) & 3;
+      vr[nt & 1] = vread(ks, nt);
+    };
+
+#pragma unroll
+    for (int hg = 0; hg < 4; ++hg) pa[hg] = pread(0, hg);
+    // the vote in tile t's P: any wave's sign bit on lane 0's first value
+    const uint32_t vote_bits = __builtin_bit_cast(uint4, pa[0]).x | __builtin_bit_cast(uint4, pa[1]).x |
+                               __builtin_bit_cast(uint4, pa[2]).x | __builtin_bit_cast(uint4, pa[3]).x;
+    vload(0);
+    vload(4);
+    bf16x8_t ar[kRing];
+#pragma unroll
+    for (int j = 0; j < kRing; ++j) ar[j] = aread(j);
+
+    // phase 1: the 36 score MFMAs, with P.V MFMAs 0 .. kP1 - 1 (at k = 3, 7,
+    // .., 31) and the copies (at k = 1, 5, .., 33)
+#pragma unroll
+    for (int k = 0; k < kKS; ++k) {
+      if (k == 0) asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(ar[0]), "v"(qf[0]));
+      else asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(ar[k % kRing]), "v"(qf[k]));
+      if (k + kRing < kKS) ar[k % kRing] = aread(k + kRing);
+      // (the P fragments arrived before the first score operand)
+      if (k == 0) vote = (__builtin_amdgcn_readfirstlane(vote_bits) & 0x8000u) != 0;
+      if (k % 4 == 3 && k / 4 < kP1) {
+        const int u = k / 4;
+        pv_mfma(u, pa, vr);
+        if ((u & 3) == 3 && u + 5 < 32) vload(u + 5);
+      }
+      if constexpr (copies) {
+        if (k % 4 == 1) copy(t + 3, k / 4);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // phase 2: the remaining P.V MFMAs with the softmax of tile t + 1 between
+    // them (its first read of the scores comes two MFMAs after the last score
+    // MFMA, past the 18 wait states a 32x32 MFMA result needs)
+#pragma unroll
+    for (int u = kP1; u < 32; ++u) {
+      const int w = u - kP1;
+      pv_mfma(u, pa, vr);
+      if ((u & 3) == 3 && u + 5 < 32) vload(u + 5);
+      // k-step 1's P fragment of a head group once k-step 0's last use is past
+      if (u >= 12 && u < 16) pa[u - 12] = pread(1, u - 12);
+      if (w >= 2 && (w - 2) % 3 == 0 && (w - 2) / 3 < 8) xpiece(s, t + 1, (w - 2) / 3);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Prologue: tiles 0..2 requested; tile 0 scored, its softmax taken and its
+  // P in pbuf[0]; tile 1 complete.
+  auto prime = [&](f32x16_t& s) {
+    const int first = min(n_tiles, 3);
+    for (int t = 0; t < first; ++t) issue(t);
+    if (first == 3) barrier_in_flight<2 * kT2Copies>();
+    else if (first == 2) barrier_in_flight<kT2Copies>();
+    else barrier_in_flight<0>();
+    uint32_t so[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      so[j] = a_addr(buffer(0), j);
+      asm volatile("" : "+v"(so[j]));
+    }
+    bf16x8_t ar[kRing];
+#pragma unroll
+    for (int j = 0; j < kRing; ++j) ar[j] = *(const lds_bf16x8*)(uintptr_t)(so[j & 3] + 128 * (j >> 2));
+#pragma unroll
+    for (int k = 0; k < kKS; ++k) {
+      if (k == 0) asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(ar[0]), "v"(qf[0]));
+      else asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(ar[k % kRing]), "v"(qf[k]));
+      if (k + kRing < kKS) ar[k % kRing] = *(const lds_bf16x8*)(uintptr_t)(so[(k + kRing) & 3] + 128 * ((k + kRing) >> 2));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s));
+#pragma unroll
+    for (int k = 0; k < 8; ++k) xpiece(s, 0, k);
+    if (first >= 3) barrier_in_flight<kT2Copies>();  // tile 1 complete; P(0) visible
+    else barrier_in_flight<0>();
+  };
+
+  // A pass runs every tile of the split; a vote seen on the way (a maximum
+  // jump) makes the whole pass run again with the raised references.  The
+  // tile loops have no early exit, so the accumulators follow one path.
+  f32x16_t s;
+  bool vote = false;
+  while (n_tiles > 0) {
+    prime(s);
+    bool again = false;
+    // iterations with a tile to request, then the tail
+    const int n_copying = max(n_tiles - 3, 0);
+    int t = 0;
+    for (; t < n_copying; ++t) {
+      stream(std::true_type{}, t, s, vote);
+      barrier_in_flight<kT2Copies>();  // tile t + 2 complete, tile t + 3 in flight
+      again |= vote;
+    }
+    for (; t < n_tiles; ++t) {
+      stream(std::false_type{}, t, s, vote);
+      barrier_in_flight<0>();
+      again |= vote;
+    }
+    if (!again) break;
+    // some head's maximum jumped: redo the split with every head's reference
+    // at the largest score it has seen (each restart raises a reference by
+    // more than kTau; a jump needs an ordered comparison, so NaN scores never
+    // vote and restarts are few)
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::);  // in-flight MFMAs retire first
+    zero_acc();
+    m_run = m_seen;
+    l_run = 0.f;
+  }
+  settle(acc);
+
+  // unnormalised partials: O (relative to m_run), m_run and l per head
+  const size_t roww = (size_t)b * a.H + hw;
+#pragma unroll
+  for (int hg = 0; hg < 4; ++hg)
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        a.part_o[((roww + 32 * hg + 8 * (v / 4) + 4 * half + (v % 4)) * a.num_splits + split) * kDc + d0 +
+                 32 * nt + lj] = acc[hg * kNT + nt][v];
+  const auto w = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
+  const float l_tot = __uint_as_float(w[0]) + __uint_as_float(w[1]);
+  if (half == 0) {
+    const size_t r = ((size_t)b * a.H + h0 + lj) * a.num_splits + split;
+    a.part_lse[r] = l_tot > 0.f ? m_run : NEG_INF;
+    a.part_l[r] = l_tot;
+  }
+}
+
+template <bool SPARSE, bool TABLE, int NW>
 hipError_t launch_variant(const MlaArgs& a, hipStream_t s) {
   dim3 grid(a.num_splits, a.H / (NW * kHeadsPerWave), a.B), block(64 * NW);
-  launch_kernel(mla_split_kernel<SPARSE, PAGED, NW>, grid, block, s, a);
+  launch_kernel(mla_split_kernel<SPARSE, TABLE, NW>, grid, block, s, a);
   return hipGetLastError();
 }
 
 template <int NW>
 hipError_t launch_nw(const MlaArgs& a, hipStream_t s) {
-  if (a.idx) return launch_variant<true, false, NW>(a, s);
+  if (a.idx) return launch_variant<true, true, NW>(a, s);
   if (a.page_table) return launch_variant<false, true, NW>(a, s);
   return launch_variant<false, false, NW>(a, s);
 }
@@ -474,6 +1012,11 @@ hipError_t launch_nw(const MlaArgs& a, hipStream_t s) {
 int mla_heads_per_workgroup(int H) { return H % 128 == 0 ? 128 : 64; }
 
 hipError_t launch_mla(const MlaArgs& a, hipStream_t s) {
+  if (!a.idx && !a.page_table && a.heads_per_wg == 128 && a.H % 128 == 0) {
+    dim3 grid(a.num_splits, a.H / 128, a.B);
+    launch_kernel(mla_contig_kernel, grid, dim3(256), s, a);
+    return hipGetLastError();
+  }
   if (a.heads_per_wg == 128 && a.H % 128 == 0) return launch_nw<4>(a, s);
   if (a.heads_per_wg == 64 && a.H % 64 == 0) return launch_nw<2>(a, s);
   return hipErrorInvalidValue;
