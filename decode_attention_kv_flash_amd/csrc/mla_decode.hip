@@ -731,19 +731,20 @@ __global__ __launch_bounds__(256, 1) void mla_contig_kernel(const MlaArgs a) {
   auto tile_src = [&](int tix) -> const char* { return latent + (size_t)tix * kT2Bytes; };
   // source offset of copy j for tile tix (rows past the split end re-read its
   // last row: finite data whose P is 0)
-  auto copy_off = [&](int tix, int j) -> uint32_t {
-    const int rows_here = n_tok - tix * kT2;
+  auto copy_off = [&](int tix, int j, bool whole) -> uint32_t {
     const uint32_t o = coff(j);
-    if (rows_here >= kT2) return o;
+    if (whole) return o;
+    const int rows_here = n_tok - tix * kT2;
     const uint32_t r = o / kRowBytes;
-    return min(r, (uint32_t)(rows_here - 1)) * kRowBytes + (o - r * kRowBytes);
+    return min(r, (uint32_t)(max(rows_here, 1) - 1)) * kRowBytes + (o - r * kRowBytes);
   };
-  auto copy = [&](int tix, int j) {
-    copy_to_lds_sv(copy_off(tix, j), tile_src(tix), buffer(tix) + 16u * (uint32_t)(576 * wave) + 1024u * j);
+  // whole: the tile holds kT2 tokens of the split (no clamping)
+  auto copy = [&](int tix, int j, bool whole) {
+    copy_to_lds_sv(copy_off(tix, j, whole), tile_src(tix), buffer(tix) + 16u * (uint32_t)(576 * wave) + 1024u * j);
   };
   auto issue = [&](int tix) {
 #pragma unroll
-    for (int j = 0; j < kT2Copies; ++j) copy(tix, j);
+    for (int j = 0; j < kT2Copies; ++j) copy(tix, j, false);
   };
 
   // ---- per-lane parts of the LDS reads
@@ -770,7 +771,7 @@ __global__ __launch_bounds__(256, 1) void mla_contig_kernel(const MlaArgs a) {
   bool jump = false;
   auto xpiece = [&](f32x16_t& s, int tix, int k) {
     if (k == 0) {
-      if (tix * kT2 + kT2 > n_tok) {  // positions past the split end
+      if (__builtin_amdgcn_readfirstlane(tix * kT2 + kT2 > n_tok)) {  // positions past the split end
 #pragma unroll
         for (int v = 0; v < 16; ++v)
           if (tix * kT2 + 8 * (v / 4) + 4 * half + (v % 4) >= n_tok) s[v] = NEG_INF;
@@ -826,9 +827,11 @@ __global__ __launch_bounds__(256, 1) void mla_contig_kernel(const MlaArgs a) {
                  : "+a"(acc[hg * kNT + nt]) : "v"(pa[hg]), "v"(vr[nt & 1]));
   };
 
-  // The stream of iteration t: S(t + 1) || P.V(t) || softmax(t + 1) || copies of t + 3.
-  auto stream = [&](auto with_copies, int t, f32x16_t& s, bool& vote) {
-    constexpr bool copies = decltype(with_copies)::value;
+  // The stream of iteration t: S(t + 1) || P.V(t) || softmax(t + 1) || copies of
+  // t + 3: none (kCopy = 0), of a whole tile (1) or of the split's last,
+  // partial tile (2).
+  auto stream = [&](auto copy_kind, int t, f32x16_t& s, bool& vote) {
+    constexpr int kCopy = decltype(copy_kind)::value;
     const uint32_t sbuf = buffer(t + 1), vbuf = buffer(t);
     const uint32_t pin = pbuf_base + (uint32_t)(t & 1) * kP2Bytes;
     uint32_t so[4];
@@ -890,8 +893,8 @@ __global__ __launch_bounds__(256, 1) void mla_contig_kernel(const MlaArgs a) {
         pv_mfma(u, pa, vr);
         if ((u & 3) == 3 && u + 5 < 32) vload(u + 5);
       }
-      if constexpr (copies) {
-        if (k % 4 == 1) copy(t + 3, k / 4);
+      if constexpr (kCopy > 0) {
+        if (k % 4 == 1) copy(t + 3, k / 4, kCopy == 1);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -949,16 +952,23 @@ __global__ __launch_bounds__(256, 1) void mla_contig_kernel(const MlaArgs a) {
   while (n_tiles > 0) {
     prime(s);
     bool again = false;
-    // iterations with a tile to request, then the tail
+    // iterations that request a whole tile, the one that requests the
+    // split's partial last tile, then the tail
     const int n_copying = max(n_tiles - 3, 0);
+    const int n_whole = min(n_copying, max(n_tok / kT2 - 3, 0));
     int t = 0;
-    for (; t < n_copying; ++t) {
-      stream(std::true_type{}, t, s, vote);
+    for (; t < n_whole; ++t) {
+      stream(std::integral_constant<int, 1>{}, t, s, vote);
       barrier_in_flight<kT2Copies>();  // tile t + 2 complete, tile t + 3 in flight
       again |= vote;
     }
+    for (; t < n_copying; ++t) {
+      stream(std::integral_constant<int, 2>{}, t, s, vote);
+      barrier_in_flight<kT2Copies>();
+      again |= vote;
+    }
     for (; t < n_tiles; ++t) {
-      stream(std::false_type{}, t, s, vote);
+      stream(std::integral_constant<int, 0>{}, t, s, vote);
       barrier_in_flight<0>();
       again |= vote;
     }
