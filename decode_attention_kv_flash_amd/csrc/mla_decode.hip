@@ -660,7 +660,13 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_split_kernel(const MlaArgs a) 
 // restart vote therefore rides on P itself: probabilities are never negative,
 // so a wave that sees a maximum jump sets the sign bit of the first value of
 // its P fragment (head group w, lane 0); every wave reads that value back
-// with the fragment and leaves the tile loop on it.
+// with the fragment, finishes the pass over the split's tiles and runs it
+// again with the raised references.
+//
+// Within an iteration the first LDS reads after the barrier are the first
+// score operands (the P and value fragments follow), and the splits of one
+// (sequence, head block) are placed on one XCD so that its L2 serves their
+// shared query rows.
 constexpr int kT2 = 32;                       // tokens per tile
 constexpr int kT2Bytes = kT2 * kRowBytes;     // 36864
 constexpr int kT2Buffers = 4;
@@ -680,7 +686,7 @@ __device__ __forceinline__ int swz32(int r) {
 __global__ __launch_bounds__(256, 1) void mla_contig_kernel(const MlaArgs a) {
   constexpr int kKS = kDq / 16;          // 36 score k-steps of 16 dims
   constexpr int kNT = kDc / 4 / 32;      // 4 output tiles of 32 dims per wave
-  constexpr int kP1 = 8;                 // P.V MFMAs in the score phase (of 32)
+  constexpr int kP1 = 4;                 // P.V MFMAs in the score phase (of 32)
   const float NEG_INF = -__builtin_inff();
   __shared__ __attribute__((aligned(16))) char tiles[kT2Buffers * kT2Bytes];
   __shared__ __attribute__((aligned(16))) char pbuf[2][kP2Bytes];
@@ -688,9 +694,15 @@ __global__ __launch_bounds__(256, 1) void mla_contig_kernel(const MlaArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int half = lane >> 5, lj = lane & 31, li = lane & 15, g = lane >> 4;
-  const int split = blockIdx.x;
-  const int b = blockIdx.z;
-  const int hw = blockIdx.y * 128;       // the workgroup's first head
+  // workgroups reach the 8 XCDs round-robin by linear id; renumber them so
+  // that the splits of one (batch, head block) share an XCD, and its L2
+  // serves their common query rows
+  int lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  const int n_wg = gridDim.x * gridDim.y * gridDim.z;
+  if (n_wg % 8 == 0) lin = (lin % 8) * (n_wg / 8) + lin / 8;
+  const int split = lin % gridDim.x;
+  const int b = lin / (gridDim.x * gridDim.y);
+  const int hw = (lin / gridDim.x) % gridDim.y * 128;  // the workgroup's first head
   const int h0 = hw + wave * 32;         // this wave's score heads
   const int d0 = wave * 128;             // this wave's output dims
 
@@ -868,26 +880,31 @@ __global__ __launch_bounds__(256, 1) void mla_contig_kernel(const MlaArgs a) {
       vr[nt & 1] = vread(ks, nt);
     };
 
-#pragma unroll
-    for (int hg = 0; hg < 4; ++hg) pa[hg] = pread(0, hg);
-    // the vote in tile t's P: any wave's sign bit on lane 0's first value
-    const uint32_t vote_bits = __builtin_bit_cast(uint4, pa[0]).x | __builtin_bit_cast(uint4, pa[1]).x |
-                               __builtin_bit_cast(uint4, pa[2]).x | __builtin_bit_cast(uint4, pa[3]).x;
-    vload(0);
-    vload(4);
+    // the first score operands first: every wave's first MFMA waits on them
     bf16x8_t ar[kRing];
 #pragma unroll
     for (int j = 0; j < kRing; ++j) ar[j] = aread(j);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int hg = 0; hg < 4; ++hg) pa[hg] = pread(0, hg);
+    vload(0);
+    vload(4);
+    __builtin_amdgcn_sched_barrier(0);
 
     // phase 1: the 36 score MFMAs, with P.V MFMAs 0 .. kP1 - 1 (at k = 3, 7,
-    // .., 31) and the copies (at k = 1, 5, .., 33)
+    // 11, 15) and the copies (at k = 1, 5, .., 33)
 #pragma unroll
     for (int k = 0; k < kKS; ++k) {
       if (k == 0) asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(ar[0]), "v"(qf[0]));
       else asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(ar[k % kRing]), "v"(qf[k]));
       if (k + kRing < kKS) ar[k % kRing] = aread(k + kRing);
-      // (the P fragments arrived before the first score operand)
-      if (k == 0) vote = (__builtin_amdgcn_readfirstlane(vote_bits) & 0x8000u) != 0;
+      // the vote in tile t's P: any wave's sign bit on lane 0's first value
+      // (read once the P fragments are in, for the first P.V MFMA)
+      if (k == 4) {
+        const uint32_t vote_bits = __builtin_bit_cast(uint4, pa[0]).x | __builtin_bit_cast(uint4, pa[1]).x |
+                                   __builtin_bit_cast(uint4, pa[2]).x | __builtin_bit_cast(uint4, pa[3]).x;
+        vote = (__builtin_amdgcn_readfirstlane(vote_bits) & 0x8000u) != 0;
+      }
       if (k % 4 == 3 && k / 4 < kP1) {
         const int u = k / 4;
         pv_mfma(u, pa, vr);
