@@ -78,18 +78,245 @@ def sha256_of(path):
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def counter_traffic(kernel, source):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"{kernel}_traffic.json")
+# Kernels with committed rocprofv3 counter records (profiles/<name>_counters.json):
+# name -> (bench --only workload, kernel-name pattern, source file, what one
+# launch does).  The records are written by `bench.py --counter-summary DIR`
+# from the counter passes listed in COUNTER_PASSES, each run as
+#   rocprofv3 --pmc <counters> -d DIR/<workload>_<pass> -o run --output-format csv --
+#       python3 bench.py --only <workload> --steps 20 --warmup 5 --ramp-ms 50
+# and from the same FETCH_SIZE / WRITE_SIZE passes over `bench.py
+# --calibrate-copy --steps 5` (DIR/copy_fetch, DIR/copy_write), which read and
+# write exactly 1 GiB per launch and so give the counters' byte scale.
+COUNTER_KERNELS = {
+    "gqa_split": ("gqa", r"gqa_split_kernel", "gqa_decode.hip",
+                  "GQA Llama-3-8B layer (B16, 32/8 heads, D128, 8192 tokens, paged 16, bf16): "
+                  "K+V 536870912 bytes"),
+    "mla_split": ("mla", r"mla_contig_kernel", "mla_decode.hip",
+                  "MLA DeepSeek-V3 shape (B32, H128, 576-wide latent, 16384 tokens, bf16): "
+                  "latent 603979776 bytes, 146028888064 flops"),
+    "sparse_mla_split": ("dsa", r"mla_split_kernel<true, true", "mla_decode.hip",
+                         "sparse MLA over top-2048 of 65536 (B8, H128, bf16): "
+                         "selected latent rows 18874368 bytes, 4563402752 flops"),
+    "indexer_bf16": ("dsa", r"indexer_kernel<\d+, false>", "indexer.hip",
+                     "DSA indexer (B8, 65536 tokens, 64 heads x 128, bf16 keys): "
+                     "134217728 key bytes"),
+    "indexer_fp8": ("dsa", r"indexer_kernel<\d+, true>", "indexer.hip",
+                    "DSA indexer (B8, 65536 tokens, 64 heads x 128, fp8 e4m3 keys): "
+                    "67108864 key bytes"),
+}
+COUNTER_PASSES = {
+    "fetch": "FETCH_SIZE",
+    "write": "WRITE_SIZE",
+    "mfma": "SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES SQ_INSTS_MFMA SQ_INSTS_VALU SQ_INSTS_LDS "
+            "SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE GRBM_GUI_ACTIVE",
+    "issue": "SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY SQ_WAIT_INST_LDS "
+             "SQ_ACTIVE_INST_LDS SQ_ACTIVE_INST_VALU SQ_INSTS_SALU",
+}
+
+
+def counter_record(kernel):
+    """The committed counter record of a kernel if it was taken on the current
+    kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_counters.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    src = os.path.join(ROOT, "decode_attention_kv_flash_amd", "csrc", source)
+    src = os.path.join(ROOT, "decode_attention_kv_flash_amd", "csrc", rec["source"])
     if rec.get("source_sha256") != sha256_of(src):
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec
+
+
+def counter_traffic(kernel):
+    """HBM bytes per launch from the committed counter record, or None."""
+    rec = counter_record(kernel)
+    return None if rec is None else rec["hbm_bytes_per_launch"]
+
+
+def counter_fields(kernel):
+    """Counter-measured fields for a workload record (None when stale)."""
+    rec = counter_record(kernel)
+    if rec is None:
+        return {"counters": None}
+    return {"counters": {k: rec[k] for k in ("hbm_bytes_per_launch", "fetch_bytes_per_launch",
+                                              "write_bytes_per_launch", "mfma_busy_frac",
+                                              "lds_bank_conflict_per_lds_inst")}}
+
+
+def _pmc_means(csv_path, pattern):
+    """Per-counter mean over the dispatches of kernels matching pattern (a
+    counter's per-dispatch value is the sum of its rows)."""
+    import csv
+    import re
+    per = {}
+    rx = re.compile(pattern)
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            if not rx.search(r["Kernel_Name"]):
+                continue
+            d = per.setdefault(r["Counter_Name"], {})
+            d[r["Dispatch_Id"]] = d.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    return {c: (sum(v.values()) / len(v), len(v)) for c, v in per.items()}
+
+
+def counter_summary(pmc_dir):
+    """Writes profiles/<kernel>_counters.json and a text summary per kernel
+    from the counter passes under pmc_dir."""
+    import glob
+    def csv_of(tag):
+        return glob.glob(os.path.join(pmc_dir, tag, "*counter_collection.csv"))[0]
+    copy_fetch = _pmc_means(csv_of("copy_fetch"), r"copyBuffer|copy_kernel|direct_copy")["FETCH_SIZE"][0]
+    copy_write = _pmc_means(csv_of("copy_write"), r"copyBuffer|copy_kernel|direct_copy")["WRITE_SIZE"][0]
+    fetch_scale = (1 << 30) / (copy_fetch * 1024)
+    write_scale = (1 << 30) / (copy_write * 1024)
+    cmd = ("cd /tmp && rocprofv3 --pmc {ctr} -d <out>/{tag} -o run --output-format csv -- "
+           "python3 <repo>/bench.py {args}")
+    wl_args = "--only {w} --steps 20 --warmup 5 --ramp-ms 50"
+    for name, (w, pattern, source, what) in COUNTER_KERNELS.items():
+        vals = {}
+        for p in COUNTER_PASSES:
+            try:
+                vals.update(_pmc_means(csv_of(f"{w}_{p}"), pattern))
+            except IndexError:
+                pass
+        if "FETCH_SIZE" not in vals:
+            log(f"[counters] no passes for {name}")
+            continue
+        v = {c: x for c, (x, _) in vals.items()}
+        n_disp = vals["FETCH_SIZE"][1]
+        fetch_b = v["FETCH_SIZE"] * 1024 * fetch_scale
+        write_b = v["WRITE_SIZE"] * 1024 * write_scale
+        rec = {
+            "kernel": name, "kernel_pattern": pattern, "workload": what,
+            "source": source,
+            "source_sha256": sha256_of(os.path.join(ROOT, "decode_attention_kv_flash_amd", "csrc", source)),
+            "dispatches": n_disp,
+            "fetch_kib_per_dispatch": round(v["FETCH_SIZE"], 1),
+            "write_kib_per_dispatch": round(v["WRITE_SIZE"], 1),
+            "copy_1GiB_fetch_kib": round(copy_fetch, 1), "copy_1GiB_write_kib": round(copy_write, 1),
+            "fetch_scale": round(fetch_scale, 4), "write_scale": round(write_scale, 4),
+            "fetch_bytes_per_launch": int(fetch_b), "write_bytes_per_launch": int(write_b),
+            "hbm_bytes_per_launch": int(fetch_b + write_b),
+            # MFMA pipes busy over all SIMDs (4 per CU) of the CUs the kernel occupied
+            "mfma_busy_frac": round(v["SQ_VALU_MFMA_BUSY_CYCLES"] / (4 * v["SQ_BUSY_CU_CYCLES"]), 4)
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in v else None,
+            "lds_bank_conflict_per_lds_inst": round(v["SQ_LDS_BANK_CONFLICT"] / max(v["SQ_INSTS_LDS"], 1), 4)
+            if "SQ_LDS_BANK_CONFLICT" in v else None,
+            "wave_cycle_fracs": {k: round(v[k] / v["SQ_WAVE_CYCLES"], 4)
+                                 for k in ("SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY",
+                                           "SQ_WAIT_INST_LDS", "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_VALU")
+                                 if k in v and "SQ_WAVE_CYCLES" in v},
+            "counters_per_dispatch": {k: round(x, 1) for k, x in sorted(v.items())},
+            "commands": {p: cmd.format(ctr=ctr, tag=f"{w}_{p}", args=wl_args.format(w=w))
+                         for p, ctr in COUNTER_PASSES.items()},
+        }
+        rec["commands"]["copy_fetch"] = cmd.format(ctr="FETCH_SIZE", tag="copy_fetch",
+                                                   args="--calibrate-copy --steps 5")
+        rec["commands"]["copy_write"] = cmd.format(ctr="WRITE_SIZE", tag="copy_write",
+                                                   args="--calibrate-copy --steps 5")
+        with open(os.path.join(ROOT, "profiles", f"{name}_counters.json"), "w") as f:
+            json.dump(rec, f, indent=1)
+            f.write("\n")
+        lines = [f"# {name} counters: {what}", "",
+                 "rocprofv3 --pmc, one counter set per run (passes below); values are means over the",
+                 f"{n_disp} dispatches of kernels matching /{pattern}/.  FETCH_SIZE and WRITE_SIZE are",
+                 "scaled by the same counters on a plain 1 GiB device copy (bench.py --calibrate-copy).", ""]
+        for p, c in rec["commands"].items():
+            lines.append(f"{p}: {c}")
+        lines += ["",
+                  f"FETCH_SIZE  {v['FETCH_SIZE']:14.1f} KiB/dispatch x {fetch_scale:.4f} = {int(fetch_b):13d} bytes",
+                  f"WRITE_SIZE  {v['WRITE_SIZE']:14.1f} KiB/dispatch x {write_scale:.4f} = {int(write_b):13d} bytes",
+                  f"HBM bytes per launch {int(fetch_b + write_b)}"]
+        if rec["mfma_busy_frac"] is not None:
+            lines.append(f"MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES / (4 x SQ_BUSY_CU_CYCLES)) {rec['mfma_busy_frac']:.4f}")
+        if rec["lds_bank_conflict_per_lds_inst"] is not None:
+            lines.append(f"LDS bank conflict cycles per LDS instruction {rec['lds_bank_conflict_per_lds_inst']:.4f}")
+        for k, x in rec["wave_cycle_fracs"].items():
+            lines.append(f"{k} / SQ_WAVE_CYCLES {x:.4f}")
+        lines += ["", "counters per dispatch:"]
+        lines += [f"  {k:28s} {x:16.1f}" for k, x in sorted(v.items())]
+        lines.append(f"\nkernel source {source} sha256 {rec['source_sha256']}")
+        with open(os.path.join(ROOT, "profiles", f"{name}_counters.txt"), "w") as f:
+            f.write("\n".join(lines) + "\n")
+        log(f"[counters] {name}: {int(fetch_b + write_b)} HBM bytes/launch, mfma busy {rec['mfma_busy_frac']}")
+
+
+# Algorithmic work per launch of the dominant kernels, for the kernel-trace
+# summaries: kernel-name pattern -> (bytes, flops or None).
+TRACE_WORK = {
+    "gqa": {r"gqa_split_kernel": (536870912, None)},
+    "swa": {},
+    "layouts": {r"gqa_split_kernel": (536870912, None)},
+    "mla": {r"mla_contig_kernel": (603979776, 146028888064)},
+    "dsa": {r"indexer_kernel<\d+, false>": (134217728, None),
+            r"indexer_kernel<\d+, true>": (67108864, None),
+            r"mla_split_kernel<true, true": (18874368, 4563402752)},
+    "quest": {},
+    "append": {},
+}
+
+
+def _short_name(name):
+    import re
+    n = re.sub(r"^void ", "", name)
+    n = re.sub(r"dattn::\(anonymous namespace\)::", "", n)
+    return re.sub(r"\((dattn::)?\w+Args\)$", "", n)
+
+
+def trace_summary(trace_dir, workload, steps, out_name, title):
+    """profiles/<out_name>.txt from a rocprofv3 --kernel-trace --stats run of
+    `bench.py --only <workload> --steps <steps>`: per kernel and grid, the
+    durations of the step and kernel passes (the 2 x steps dispatches before
+    the two per-call passes), which follow the warmup and the clock ramp."""
+    import csv
+    import glob
+    import re
+    path = glob.glob(os.path.join(trace_dir, "*kernel_trace.csv"))[0]
+    if workload == "quick":  # the headline workload as the full benchmark runs it
+        bench_args = f"--quick --steps {steps} --warmup 20 --no-cpu-baseline"
+        workload = "gqa"
+    else:
+        bench_args = f"--only {workload} --steps {steps} --warmup 20"
+    groups = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if "dattn::" not in r["Kernel_Name"]:
+                continue
+            key = (r["Kernel_Name"], (int(r["Grid_Size_X"]), int(r["Grid_Size_Y"]), int(r["Grid_Size_Z"])))
+            g = groups.setdefault(key, {"d": [], "row": r})
+            g["d"].append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    K = steps
+    lines = [f"# {title}", "",
+             "rocprofv3 kernel trace (--kernel-trace --stats) of one benchmark workload; per kernel",
+             f"and grid, durations over its step and kernel passes ({K} calls each, back to back,",
+             "after the warmup and the clock ramp; the per-call passes that follow are left out).",
+             f"command: cd /tmp && rocprofv3 --kernel-trace --stats -d <out> -o run --output-format csv -- "
+             f"python3 <repo>/bench.py {bench_args}", "",
+             f"{'kernel':52s} {'grid (threads)':>20s} {'wg':>5s} {'calls':>6s} {'avg us':>9s} {'min us':>9s} "
+             f"{'max us':>9s} {'vgpr':>5s} {'agpr':>5s} {'lds':>7s} {'scratch':>7s}"]
+    for (name, grid), g in sorted(groups.items(), key=lambda kv: kv[1]["d"][0][0]):
+        d = [x for _, x in sorted(g["d"])]
+        n = len(d)
+        # the tail of each group's dispatches is [step, kernel, cold, warm] x K
+        win = d[n - 4 * K: n - 2 * K] if n >= 4 * K else d
+        us = [x / 1e3 for x in win]
+        r = g["row"]
+        sn = _short_name(name)
+        lines.append(f"{sn[:52]:52s} {str(grid):>20s} {r['Workgroup_Size_X']:>5s} {len(us):6d} "
+                     f"{sum(us) / len(us):9.2f} {min(us):9.2f} {max(us):9.2f} {r['VGPR_Count']:>5s} "
+                     f"{r['Accum_VGPR_Count']:>5s} {r['LDS_Block_Size']:>7s} {r['Scratch_Size']:>7s}")
+        for pat, (nb, nf) in TRACE_WORK.get(workload, {}).items():
+            if re.search(pat, name):
+                avg = sum(us) / len(us)
+                lines.append(f"    algorithmic bytes {nb} -> {gbs(nb, avg):.1f} GB/s "
+                             f"({100 * gbs(nb, avg) / HBM_PEAK_GBS:.1f}% of 8 TB/s)")
+                if nf:
+                    lines.append(f"    algorithmic flops {nf} -> {tflops(nf, avg):.1f} TFLOP/s "
+                                 f"({100 * tflops(nf, avg) / BF16_PEAK_TFLOPS:.1f}% of 2.5 PFLOP/s bf16)")
+    with open(os.path.join(ROOT, "profiles", out_name + ".txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    log(f"[trace] wrote profiles/{out_name}.txt")
 
 
 class Timer:
@@ -428,12 +655,24 @@ def main():
     ap.add_argument("--ramp-ms", type=float, default=200.0,
                     help="wall time of calls before each timed region (clock ramp)")
     ap.add_argument("--quick", action="store_true", help="headline workload only")
-    ap.add_argument("--only", choices=["gqa", "swa", "mla", "dsa", "append", "quest", "read"],
+    ap.add_argument("--only", choices=["gqa", "swa", "layouts", "mla", "dsa", "append", "quest", "read"],
                     help="time one workload and print its record (for profiling runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="time a plain 1 GiB device copy (reference for HBM byte counters)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--counter-summary", metavar="DIR",
+                    help="write profiles/<kernel>_counters.{json,txt} from rocprofv3 counter passes in DIR")
+    ap.add_argument("--trace-summary", nargs=4, metavar=("DIR", "WORKLOAD", "NAME", "TITLE"),
+                    help="write profiles/NAME.txt from a rocprofv3 kernel trace in DIR of "
+                         "bench.py --only WORKLOAD --steps STEPS")
     args = ap.parse_args()
+    if args.trace_summary:
+        d, w, name, title = args.trace_summary
+        trace_summary(d, w, args.steps, name, title)
+        return
+    if args.counter_summary:
+        counter_summary(args.counter_summary)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} (WORLD_SIZE {world}) is not "
@@ -499,7 +738,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": counter_traffic("gqa_split", "gqa_decode.hip"),
+            "traffic": counter_traffic("gqa_split"),
             "algorithmic_bytes_per_launch": bytes2,
             "avg_launch_us": round(split_us, 2),
             "frac_of_read_ceiling": round(achieved / ceiling["GB/s"], 4),
@@ -508,6 +747,7 @@ def main():
         "clock_ramp_ms": args.ramp_ms,
         "workloads": {
             "gqa_llama3_8b": {"step_us": round(r2["wall_ms"] * 1e3, 2), "GB/s": round(value, 1),
+                              "split_kernel": counter_fields("gqa_split"),
                               "TFLOP/s": round(flops2 / (r2["wall_ms"] * 1e-3) / 1e12, 3),
                               "kernels_us": {k: v["avg_us"] for k, v in r2["kernels"].items()},
                               **stats(r2)},
@@ -568,24 +808,7 @@ def main():
         del x3, r3s
         torch.cuda.empty_cache()
 
-        # other head layouts at config 2's K/V bytes: 64 q / 8 KV heads at D128
-        # (eight heads per KV head), and D64 over twice the tokens
-        result["workloads"]["gqa_head_layouts"] = {}
-        for hq, d, s_len in ((64, 128, 8192), (64, 64, 16384), (32, 64, 16384)):
-            name = f"gqa_{hq}q8kv_d{d}_b16_s{s_len}_paged16"
-            log(f"[bench] generating {name}")
-            xh = wl.make_gqa(B=16, Hq=hq, Hkv=8, D=d, seq_lens=[s_len] * 16, dtype=torch.bfloat16,
-                             page_size=16, seed=3, name=name)
-            bh = xh.kv_bytes()
-            rh = bench_gqa(xh, timer, steps, warmup, torch, lib)
-            result["workloads"]["gqa_head_layouts"][name] = {
-                "step_us": round(rh["wall_ms"] * 1e3, 2),
-                "GB/s": round(bh / (rh["wall_ms"] * 1e-3) / 1e9, 1),
-                "split_kernel_GB/s": round(gbs(bh, rh["kernels"]["gqa_split"]["avg_us"]), 1),
-                "kv_bytes_per_step": bh,
-                "kernels_us": {k: v["avg_us"] for k, v in rh["kernels"].items()}, **stats(rh)}
-            del xh, rh
-            torch.cuda.empty_cache()
+        result["workloads"]["gqa_head_layouts"] = bench_layouts(timer, steps, warmup, torch, lib, wl)
 
         log("[bench] generating MLA config (B32, H128, latent 576, 16384 tokens)")
         m4 = wl.config4_mla()
@@ -604,6 +827,7 @@ def main():
             "split_kernel_TFLOP/s": round(tflops(f4, us4), 1),
             "mfma_frac_of_bf16_peak": round(tflops(f4, us4) / BF16_PEAK_TFLOPS, 4),
             "split_kernel_hbm_frac": round(gbs(b4, us4) / HBM_PEAK_GBS, 4),
+            "split_kernel": counter_fields("mla_split"),
             "copies": r4["copies"],
             "kernels_us": {k: v["avg_us"] for k, v in r4["kernels"].items()}, **stats(r4)}
         del m4, r4
@@ -633,12 +857,15 @@ def main():
             "topk_us": ku["topk_select"]["avg_us"],
             "sparse_mla_TFLOP/s": round(tflops(fs, ku["sparse_mla_split"]["avg_us"]), 2),
             "sparse_mla_GB/s": round(gbs(bs, ku["sparse_mla_split"]["avg_us"]), 1),
+            "sparse_mla_split": counter_fields("sparse_mla_split"),
+            "indexer": counter_fields("indexer_bf16"),
             "copies": r5["copies"],
             "kernels_us": {k: v["avg_us"] for k, v in ku.items()}, **stats(r5),
             "indexer_fp8": {
                 "indexer_us": r5["fp8"]["kernels"]["indexer_scores"]["avg_us"],
                 "indexer_GB/s": round(gbs(bi // 2, r5["fp8"]["kernels"]["indexer_scores"]["avg_us"]), 1),
                 "key_bytes_per_step": bi // 2,
+                "indexer": counter_fields("indexer_fp8"),
                 "indexer_topk_step_us": round(r5["fp8"]["wall_ms"] * 1e3, 2), **stats(r5["fp8"])}}
         del d5, r5
         torch.cuda.empty_cache()
@@ -727,6 +954,8 @@ def only(name, timer, steps, warmup, torch, lib, wl):
         r["kv_bytes_per_step"], r["flops_per_step"] = m.kv_bytes(), m.flops()
     elif name == "append":
         r = bench_append(timer, steps, warmup, torch, lib)
+    elif name == "layouts":
+        r = bench_layouts(timer, steps, warmup, torch, lib, wl)
     elif name == "quest":
         x = wl.config2_llama3_8b_gqa()
         r = bench_quest(x, timer, steps, warmup, torch, lib, 128)
@@ -743,6 +972,28 @@ def only(name, timer, steps, warmup, torch, lib, wl):
         r.pop(k, None)
     r["workload"] = name
     print(json.dumps(r), flush=True)
+
+
+def bench_layouts(timer, steps, warmup, torch, lib, wl):
+    """Other head layouts at config 2's K/V bytes: 64 q / 8 KV heads at D128
+    (eight heads per KV head), and D64 over twice the tokens."""
+    out = {}
+    for hq, d, s_len in ((64, 128, 8192), (64, 64, 16384), (32, 64, 16384)):
+        name = f"gqa_{hq}q8kv_d{d}_b16_s{s_len}_paged16"
+        log(f"[bench] generating {name}")
+        xh = wl.make_gqa(B=16, Hq=hq, Hkv=8, D=d, seq_lens=[s_len] * 16, dtype=torch.bfloat16,
+                         page_size=16, seed=3, name=name)
+        bh = xh.kv_bytes()
+        rh = bench_gqa(xh, timer, steps, warmup, torch, lib)
+        out[name] = {
+            "step_us": round(rh["wall_ms"] * 1e3, 2),
+            "GB/s": round(bh / (rh["wall_ms"] * 1e-3) / 1e9, 1),
+            "split_kernel_GB/s": round(gbs(bh, rh["kernels"]["gqa_split"]["avg_us"]), 1),
+            "kv_bytes_per_step": bh,
+            "kernels_us": {k: v["avg_us"] for k, v in rh["kernels"].items()}, **stats(rh)}
+        del xh, rh
+        torch.cuda.empty_cache()
+    return out
 
 
 def cpu_model():
