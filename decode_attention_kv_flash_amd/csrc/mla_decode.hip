@@ -199,9 +199,11 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_split_kernel(const MlaArgs a) 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l16 = lane & 15, g4 = lane >> 4, half = lane >> 5;
-  const int split = blockIdx.x;
-  const int b = blockIdx.z;
-  const int hw = blockIdx.y * (NW * kHeadsPerWave);   // the workgroup's first head
+  // grid (B, splits, head blocks): the sequence index fastest, so that the
+  // workgroups of one sequence share an XCD and its L2 (B a multiple of 8)
+  const int b = blockIdx.x;
+  const int split = blockIdx.y;
+  const int hw = blockIdx.z * (NW * kHeadsPerWave);   // the workgroup's first head
   const int h0 = hw + wave * kHeadsPerWave;           // this wave's score heads
   const int d0 = wave * (kDc / NW);                   // this wave's output dims
 
@@ -666,7 +668,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_split_kernel(const MlaArgs a) 
 // Within an iteration the first LDS reads after the barrier are the first
 // score operands (the P and value fragments follow), and the splits of one
 // (sequence, head block) are placed on one XCD so that its L2 serves their
-// shared query rows.
+// shared query rows (the grid has the sequence index fastest).
 constexpr int kT2 = 32;                       // tokens per tile
 constexpr int kT2Bytes = kT2 * kRowBytes;     // 36864
 constexpr int kT2Buffers = 4;
@@ -694,24 +696,17 @@ __global__ __launch_bounds__(256, 1) void mla_contig_kernel(const MlaArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int half = lane >> 5, lj = lane & 31, li = lane & 15, g = lane >> 4;
-  // workgroups reach the 8 XCDs round-robin by linear id; renumber them so
-  // that the splits of one (batch, head block) share an XCD, and its L2
-  // serves their common query rows
-  int lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
-  const int n_wg = gridDim.x * gridDim.y * gridDim.z;
-  if (n_wg % 8 == 0) lin = (lin % 8) * (n_wg / 8) + lin / 8;
-  const int split = lin % gridDim.x;
-  const int b = lin / (gridDim.x * gridDim.y);
-  const int hw = (lin / gridDim.x) % gridDim.y * 128;  // the workgroup's first head
+  // grid (B, splits, H / 128): workgroups reach the 8 XCDs round-robin by
+  // linear id, so with the sequence fastest the splits of one sequence share
+  // an XCD (B a multiple of 8), and its L2 serves their common query rows
+  const int b = blockIdx.x;
+  const int split = blockIdx.y;
+  const int hw = blockIdx.z * 128;       // the workgroup's first head
   const int h0 = hw + wave * 32;         // this wave's score heads
   const int d0 = wave * 128;             // this wave's output dims
 
-  const int N = max(0, min(a.seq_lens[b], a.S_max));
-  const int per = ((N + a.num_splits - 1) / a.num_splits + kT2 - 1) / kT2 * kT2;
-  const int f_begin = min(N, split * per);
-  const int n_tok = min(N, f_begin + per) - f_begin;
-  const int n_tiles = (n_tok + kT2 - 1) / kT2;
-
+  // the sequence length first, then the query rows while it is in flight
+  const int len = a.seq_lens[b];
   // Q^T fragments (B of the scores): lane holds head h0 + lj, dims 16 k + 8 half + [0, 8)
   bf16x8_t qf[kKS];
   {
@@ -719,6 +714,12 @@ __global__ __launch_bounds__(256, 1) void mla_contig_kernel(const MlaArgs a) {
 #pragma unroll
     for (int k = 0; k < kKS; ++k) qf[k] = *(const bf16x8_t*)(qrow + 16 * k);
   }
+  __builtin_amdgcn_sched_barrier(0);
+  const int N = max(0, min(len, a.S_max));
+  const int per = ((N + a.num_splits - 1) / a.num_splits + kT2 - 1) / kT2 * kT2;
+  const int f_begin = min(N, split * per);
+  const int n_tok = min(N, f_begin + per) - f_begin;
+  const int n_tiles = (n_tok + kT2 - 1) / kT2;
 
   const uint32_t tiles_base = lds_address(tiles);
   const uint32_t pbuf_base = lds_address(pbuf);
@@ -1022,7 +1023,7 @@ __global__ __launch_bounds__(256, 1) void mla_contig_kernel(const MlaArgs a) {
 
 template <bool SPARSE, bool TABLE, int NW>
 hipError_t launch_variant(const MlaArgs& a, hipStream_t s) {
-  dim3 grid(a.num_splits, a.H / (NW * kHeadsPerWave), a.B), block(64 * NW);
+  dim3 grid(a.B, a.num_splits, a.H / (NW * kHeadsPerWave)), block(64 * NW);
   launch_kernel(mla_split_kernel<SPARSE, TABLE, NW>, grid, block, s, a);
   return hipGetLastError();
 }
@@ -1040,7 +1041,7 @@ int mla_heads_per_workgroup(int H) { return H % 128 == 0 ? 128 : 64; }
 
 hipError_t launch_mla(const MlaArgs& a, hipStream_t s) {
   if (!a.idx && !a.page_table && a.heads_per_wg == 128 && a.H % 128 == 0) {
-    dim3 grid(a.num_splits, a.H / 128, a.B);
+    dim3 grid(a.B, a.num_splits, a.H / 128);
     launch_kernel(mla_contig_kernel, grid, dim3(256), s, a);
     return hipGetLastError();
   }
