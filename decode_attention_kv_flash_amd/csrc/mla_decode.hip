@@ -220,6 +220,32 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_split_kernel(const MlaArgs a) 
   const int n_tok = f_end - f_begin;
   int n_tiles = min((n_tok + kTile - 1) / kTile, kMaxTiles);
 
+  // TABLE: the source of each position of the split (a token index of the
+  // list, or a page of the table), for the first kPre positions of this
+  // thread; requested before the query rows so that the two round trips
+  // overlap.  -1: no token.
+  constexpr int kPre = 2;
+  // positions of the split plus one all-padding tile (none for an empty split,
+  // which reads nothing)
+  const int n_rows = TABLE && n_tiles > 0 ? (n_tiles + 1) * kTile : 0;
+  auto entry_src = [&](int i) -> int {
+    const int f = f_begin + i;
+    if constexpr (SPARSE) {
+      return f < f_end ? a.idx[(size_t)b * a.k_sel + f] : -1;
+    } else {
+      const int t = f < f_end ? f : f_end - 1;
+      return a.page_table[(size_t)b * a.max_pages + (t >> a.log2_page)];
+    }
+  };
+  int pre[kPre];
+  if constexpr (TABLE) {
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) {
+      const int i = (int)threadIdx.x + u * kThreads;
+      pre[u] = i < n_rows ? entry_src(i) : -1;
+    }
+  }
+
   // Q^T fragments (B operand of the 16x16x32 scores): for head group hh the
   // lane holds head h0 + 16 hh + l16, dims 32 ks + 8 g4 + [0, 8)
   bf16x8_t qf[kKSteps][2];
@@ -240,42 +266,55 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_split_kernel(const MlaArgs a) 
   // all-padding tile past it.  Flag kPad marks a position without a token;
   // its entry still names a row of finite data (a real row of the same
   // split), so that P = 0 times it stays 0.
+  // The barriers of the set-up wait for LDS only: the query rows stay in
+  // flight under the table's construction and the first copies.
   if constexpr (TABLE) {
     if (threadIdx.x < (kMaxTiles + 32) / 32) tile_pad[threadIdx.x] = 0u;
-    __syncthreads();
-    const int n_rows = (n_tiles + 1) * kTile;
-    for (int i = threadIdx.x; i < n_rows; i += kThreads) {
+    barrier_in_flight<63>();
+    int fv = 0x7fffffff;  // this thread's first position with a token (SPARSE)
+    auto place = [&](int i, int src) {
       const int f = f_begin + i;
       uint32_t e;
       if constexpr (SPARSE) {
-        const int t = f < f_end ? a.idx[(size_t)b * a.k_sel + f] : -1;
-        const bool ok = t >= 0 && t < a.S_max;
-        e = ok ? (uint32_t)b * (uint32_t)a.S_max + (uint32_t)t : kPad;
-        if (ok) atomicMin(&first_valid, i);
+        const bool ok = src >= 0 && src < a.S_max;
+        e = ok ? (uint32_t)b * (uint32_t)a.S_max + (uint32_t)src : kPad;
+        if (ok) fv = min(fv, i);
       } else {
         const bool ok = f < f_end;
         const int t = ok ? f : f_end - 1;
-        const int phys = a.page_table[(size_t)b * a.max_pages + (t >> a.log2_page)];
-        const uint32_t row = (uint32_t)phys * (uint32_t)a.page_size + (uint32_t)(t & (a.page_size - 1));
+        const uint32_t row = (uint32_t)src * (uint32_t)a.page_size + (uint32_t)(t & (a.page_size - 1));
         e = row | (ok ? 0u : kPad);
       }
       rows[i] = e;
       if (e & kPad) atomicOr(&tile_pad[(i / kTile) >> 5], 1u << ((i / kTile) & 31));
+    };
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) {
+      const int i = (int)threadIdx.x + u * kThreads;
+      if (i < n_rows) place(i, pre[u]);
     }
-    __syncthreads();
+    for (int i = (int)threadIdx.x + kPre * kThreads; i < n_rows; i += kThreads) place(i, entry_src(i));
     if constexpr (SPARSE) {
-      const int fv = first_valid;
-      if (fv == 0x7fffffff) {
+      // the workgroup's first position with a token: a minimum per wave,
+      // then one LDS atomic per wave
+#pragma unroll
+      for (int d = 32; d >= 1; d >>= 1) fv = min(fv, __shfl_xor(fv, d));
+      if (lane == 0 && fv != 0x7fffffff) atomicMin(&first_valid, fv);
+    }
+    barrier_in_flight<63>();
+    if constexpr (SPARSE) {
+      const int fvw = first_valid;
+      if (fvw == 0x7fffffff) {
         n_tiles = 0;  // nothing to attend in this split
       } else {
-        const uint32_t fb = rows[fv] | kPad;
+        const uint32_t fb = rows[fvw] | kPad;
         for (int i = threadIdx.x; i < n_rows; i += kThreads)
           if (rows[i] == kPad) rows[i] = fb;
-        __syncthreads();
+        barrier_in_flight<63>();
       }
     }
   } else {
-    __syncthreads();
+    barrier_in_flight<63>();
   }
 
   const uint32_t tiles_base = lds_address(tiles);
@@ -288,14 +327,17 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_split_kernel(const MlaArgs a) 
   // ---- tile copy: this wave's copy j fills slots kPerWave * wave + 64 j +
   // lane; slot q of a tile is row q / 72, stored chunk q % 72, i.e. logical
   // chunk (q % 72) ^ f(row).  The lane's (row, chunk) of each copy is fixed.
-  uint32_t rc[kCopies];  // row | logical chunk << 8
+  // row | logical chunk << 8 of copy j, two 16-bit entries per register
+  uint32_t rc2[(kCopies + 1) / 2];
 #pragma unroll
   for (int j = 0; j < kCopies; ++j) {
     const uint32_t q = (uint32_t)(kPerWave * wave + 64 * j + lane);
     const uint32_t r = q / kChunks, cs = q - r * kChunks;
     const uint32_t c = (cs & ~7u) | ((cs & 7u) ^ (uint32_t)swz((int)r));
-    rc[j] = r | (c << 8);
+    if (j % 2 == 0) rc2[j / 2] = r | (c << 8);
+    else rc2[j / 2] |= (r | (c << 8)) << 16;
   }
+  auto rc = [&](int j) -> uint32_t { return j % 2 == 0 ? rc2[j / 2] & 0xffffu : rc2[j / 2] >> 16; };
   const char* latent = (const char*)a.latent;
   // Per tile: the copies' sources.  TABLE: each lane's row from the table
   // (read ahead of the copies, so that no LDS wait lands among the operand
@@ -310,13 +352,13 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_split_kernel(const MlaArgs a) 
     if constexpr (TABLE) {
       const uint32_t* rt = rows + tix * kTile;
 #pragma unroll
-      for (int j = 0; j < kCopies; ++j) c.v[j] = rt[rc[j] & 0xff] & ~kPad;
+      for (int j = 0; j < kCopies; ++j) c.v[j] = rt[rc(j) & 0xff] & ~kPad;
       c.base = latent;
     } else {
       c.base = latent + ((size_t)b * a.S_max + f_begin + tix * kTile) * kRowBytes;
       const uint32_t last = (uint32_t)(min(kTile, n_tok - tix * kTile) - 1);
 #pragma unroll
-      for (int j = 0; j < kCopies; ++j) c.v[j] = min(rc[j] & 0xff, last) * kRowBytes + (rc[j] >> 8) * 16;
+      for (int j = 0; j < kCopies; ++j) c.v[j] = min(rc(j) & 0xff, last) * kRowBytes + (rc(j) >> 8) * 16;
     }
     return c;
   };
@@ -324,7 +366,7 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_split_kernel(const MlaArgs a) 
   auto copy = [&](int tix, int j, const CopySrc& c) {
     const uint32_t dst = buffer(tix) + 16u * (uint32_t)(kPerWave * wave) + 1024u * j;
     if (j == kCopies - 1 && lane >= kLastLanes) return;
-    if constexpr (TABLE) copy_to_lds_v(c.base + ((size_t)c.v[j] * kChunks + (rc[j] >> 8)) * 16, dst);
+    if constexpr (TABLE) copy_to_lds_v(c.base + ((size_t)c.v[j] * kChunks + (rc(j) >> 8)) * 16, dst);
     else copy_to_lds_sv(c.v[j], c.base, dst);
   };
   auto issue = [&](int tix) {
