@@ -148,6 +148,19 @@ struct MlaPlan {
 };
 MlaPlan plan_mla(int32_t B, int32_t H, int64_t max_tokens, int32_t req, bool sparse) {
   MlaPlan p{0, dattn::mla_heads_per_workgroup(H)};
+  // A sparse call with 128-head workgroups runs on the 32-row kernel when its
+  // splits hold at most kMlaSparseTile32Tokens positions: aim for one round of
+  // 256 workgroups with at least two 32-row tiles per split.
+  if (sparse && p.heads_per_wg == 128 && req == 0) {
+    const int64_t units = (int64_t)B * (H / 128);
+    const int64_t floor_n = (max_tokens + dattn::kMlaSparseTile32Tokens - 1) / dattn::kMlaSparseTile32Tokens;
+    int64_t n = (256 + units - 1) / units;
+    const int64_t cap = (max_tokens + 127) / 128;
+    if (n > cap) n = cap;
+    if (n < floor_n) n = floor_n;
+    if (n < 1) n = 1;
+    if (n <= kMlaMaxSplits) return MlaPlan{(int)n, 128};
+  }
   p.splits = plan_mla_splits(B, H, p.heads_per_wg, max_tokens, req);
   if (sparse && p.heads_per_wg == 128 && p.splits > 0 &&
       (int64_t)B * (H / 128) * p.splits < dattn::device_cu_count()) {

@@ -134,10 +134,18 @@ struct MlaArgs {
 // Tokens one MLA split may hold (its cache rows are tabled in LDS); the
 // planner picks at least ceil(tokens / kMlaMaxSplitTokens) splits.
 constexpr int kMlaMaxSplitTokens = 3840;
+// Positions a sparse split may hold to run on the 32-row MLA kernel (its
+// validity bitmap and row register per wave cover 8 tiles of 32).
+constexpr int kMlaSparseTile32Tokens = 256;
 // 128 query heads per workgroup when H allows it, else 64 (H % 64 == 0); a
 // call may take 64 when H allows 128 (MlaArgs::heads_per_wg).
 int mla_heads_per_workgroup(int H);
 hipError_t launch_mla(const MlaArgs& a, hipStream_t s);
+// Whether launch_mla runs the 32-row kernel (dense contiguous 128-head calls,
+// and sparse 128-head calls whose splits hold at most kMlaSparseTile32Tokens
+// positions of a cache with S_max * 1152 < 2^32).
+bool mla_uses_tile32(const MlaArgs& a);
+bool mla_sparse_on_tile32(const MlaArgs& a);
 
 struct IndexerArgs {
   const void* q;           // [B, Hi, 128] bf16 or fp8 e4m3

@@ -714,6 +714,8 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_split_kernel(const MlaArgs a) 
 constexpr int kT2 = 32;                       // tokens per tile
 constexpr int kT2Bytes = kT2 * kRowBytes;     // 36864
 constexpr int kT2Buffers = 4;
+constexpr int kSparseTiles = kMlaSparseTile32Tokens / kT2;  // tiles of a sparse split on this kernel
+static_assert(kSparseTiles == 8, "one row register per wave: 8 tiles x 8 rows = 64 lanes");
 constexpr int kT2Copies = kT2 * kChunks / 64 / 4;  // 9 wave copies per wave and tile
 constexpr int kP2Bytes = 2 * 4 * 64 * 16;     // P of one tile: 2 k-steps x 4 head groups x 64 lanes x 16 B
 static_assert(kT2Buffers * kT2Bytes + 2 * kP2Bytes <= 160 * 1024, "fits the LDS");
@@ -727,7 +729,8 @@ __device__ __forceinline__ int swz32(int r) {
   return ((m & 1) << 2) | (m >> 1);
 }
 
-__global__ __launch_bounds__(256, 1) void mla_contig_kernel(const MlaArgs a) {
+template <bool SPARSE>
+__global__ __launch_bounds__(256, 1) void mla_tile32_kernel(const MlaArgs a) {
   constexpr int kKS = kDq / 16;          // 36 score k-steps of 16 dims
   constexpr int kNT = kDc / 4 / 32;      // 4 output tiles of 32 dims per wave
   constexpr int kP1 = 4;                 // P.V MFMAs in the score phase (of 32)
@@ -747,8 +750,27 @@ __global__ __launch_bounds__(256, 1) void mla_contig_kernel(const MlaArgs a) {
   const int h0 = hw + wave * 32;         // this wave's score heads
   const int d0 = wave * 128;             // this wave's output dims
 
-  // the sequence length first, then the query rows while it is in flight
-  const int len = a.seq_lens[b];
+  // the split: positions [f_begin, f_begin + n_tok) of the sequence (or list)
+  int N, f_begin, n_tok;
+  auto place_split = [&](int len) {
+    N = SPARSE ? len : max(0, min(len, a.S_max));
+    const int per = ((N + a.num_splits - 1) / a.num_splits + kT2 - 1) / kT2 * kT2;
+    f_begin = min(N, split * per);
+    n_tok = min(N, f_begin + per) - f_begin;
+  };
+  // SPARSE: the split's list entries first (see below); dense: the sequence
+  // length; then the query rows while either is in flight
+  int len_raw = 0, cids = 0, lid[4] = {-1, -1, -1, -1};
+  if constexpr (SPARSE) {
+    place_split(a.k_sel);
+    const int32_t* list = a.idx + (size_t)b * a.k_sel + f_begin;
+    const int p = 32 * (lane >> 3) + 8 * wave + (lane & 7);
+    cids = p < n_tok ? list[p] : -1;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) lid[u] = 64 * u + lane < n_tok ? list[64 * u + lane] : -1;
+  } else {
+    len_raw = a.seq_lens[b];
+  }
   // Q^T fragments (B of the scores): lane holds head h0 + lj, dims 16 k + 8 half + [0, 8)
   bf16x8_t qf[kKS];
   {
@@ -757,15 +779,49 @@ __global__ __launch_bounds__(256, 1) void mla_contig_kernel(const MlaArgs a) {
     for (int k = 0; k < kKS; ++k) qf[k] = *(const bf16x8_t*)(qrow + 16 * k);
   }
   __builtin_amdgcn_sched_barrier(0);
-  const int N = max(0, min(len, a.S_max));
-  const int per = ((N + a.num_splits - 1) / a.num_splits + kT2 - 1) / kT2 * kT2;
-  const int f_begin = min(N, split * per);
-  const int n_tok = min(N, f_begin + per) - f_begin;
+  if constexpr (!SPARSE) place_split(len_raw);
   const int n_tiles = (n_tok + kT2 - 1) / kT2;
 
   const uint32_t tiles_base = lds_address(tiles);
   const uint32_t pbuf_base = lds_address(pbuf);
   auto buffer = [&](int tix) -> uint32_t { return tiles_base + (uint32_t)(tix & 3) * kT2Bytes; };
+
+  // SPARSE (a split of at most kSparseTiles tiles): the validity of each
+  // position of the split as a bitmap in scalar registers, and in one
+  // register per wave the cache rows its copies need: lane l holds position
+  // 32 (l / 8) + 8 wave + l % 8, i.e. row 8 wave + l % 8 of tile l / 8 (a
+  // wave's copies cover its rows 8 wave .. 8 wave + 7).  A position without
+  // a valid row is masked like a position past the split end and copies the
+  // split's first valid row instead (finite data whose P is 0), so every copy
+  // instruction is issued whole and the barriers' counts of copies in flight
+  // stay exact.
+  const int f_end = f_begin + n_tok;
+  (void)f_end;
+  auto valid_row = [&](int id) -> bool { return id >= 0 && id < a.S_max; };
+  // (the list entries were requested before the query rows, so waiting for
+  // them here leaves the query rows in flight)
+  uint64_t vb0 = 0, vb1 = 0, vb2 = 0, vb3 = 0;  // positions 0-63, .., 192-255
+  int fill = 0;
+  int n_tiles_run = n_tiles;
+  if constexpr (SPARSE) {
+    const int32_t* list = a.idx + (size_t)b * a.k_sel + f_begin;
+    vb0 = __ballot(valid_row(lid[0]));
+    vb1 = __ballot(valid_row(lid[1]));
+    vb2 = __ballot(valid_row(lid[2]));
+    vb3 = __ballot(valid_row(lid[3]));
+    const int first = vb0 ? __builtin_ctzll(vb0)
+                    : vb1 ? 64 + __builtin_ctzll(vb1)
+                    : vb2 ? 128 + __builtin_ctzll(vb2)
+                    : vb3 ? 192 + __builtin_ctzll(vb3) : -1;
+    if (first < 0) n_tiles_run = 0;  // no valid row: nothing to attend
+    else fill = list[first];
+  }
+  // SPARSE: positions of tile tix without a valid row (bit r: position r)
+  auto holes_of = [&](int tix) -> uint32_t {
+    if (tix >= kSparseTiles) return ~0u;
+    const uint64_t w = tix < 2 ? vb0 : tix < 4 ? vb1 : tix < 6 ? vb2 : vb3;
+    return ~(uint32_t)(w >> (32 * (tix & 1)));
+  };
 
   // ---- copies: wave copy j fills slots 576 wave + 64 j + lane of a tile;
   // slot q is row q / 72, stored chunk q % 72, logical chunk (q % 72) ^ f(row).
@@ -782,7 +838,7 @@ __global__ __launch_bounds__(256, 1) void mla_contig_kernel(const MlaArgs a) {
     else coff2[j / 2] |= off << 16;
   }
   auto coff = [&](int j) -> uint32_t { return j % 2 == 0 ? coff2[j / 2] & 0xffffu : coff2[j / 2] >> 16; };
-  const char* latent = (const char*)a.latent + ((size_t)b * a.S_max + f_begin) * kRowBytes;
+  const char* latent = (const char*)a.latent + ((size_t)b * a.S_max + (SPARSE ? 0 : f_begin)) * kRowBytes;
   auto tile_src = [&](int tix) -> const char* { return latent + (size_t)tix * kT2Bytes; };
   // source offset of copy j for tile tix (rows past the split end re-read its
   // last row: finite data whose P is 0)
@@ -795,7 +851,20 @@ __global__ __launch_bounds__(256, 1) void mla_contig_kernel(const MlaArgs a) {
   };
   // whole: the tile holds kT2 tokens of the split (no clamping)
   auto copy = [&](int tix, int j, bool whole) {
-    copy_to_lds_sv(copy_off(tix, j, whole), tile_src(tix), buffer(tix) + 16u * (uint32_t)(576 * wave) + 1024u * j);
+    const uint32_t dst = buffer(tix) + 16u * (uint32_t)(576 * wave) + 1024u * j;
+    if constexpr (SPARSE) {
+      // copy j covers slots 64 j .. 64 j + 63 of the wave's eight rows:
+      // row lo, and row lo + 1 from lane thr on
+      const int lo = 64 * j / kChunks, thr = kChunks * (lo + 1) - 64 * j;
+      const int r_lo = __builtin_amdgcn_readlane(cids, 8 * tix + lo);
+      const int r_hi = thr < 64 ? __builtin_amdgcn_readlane(cids, 8 * tix + lo + 1) : r_lo;
+      const bool up = lane >= thr;
+      const int rid = up ? r_hi : r_lo;
+      const uint32_t c16 = coff(j) - (uint32_t)(8 * wave + lo + (up ? 1 : 0)) * kRowBytes;
+      copy_to_lds_sv((uint32_t)(valid_row(rid) ? rid : fill) * kRowBytes + c16, latent, dst);
+    } else {
+      copy_to_lds_sv(copy_off(tix, j, whole), tile_src(tix), dst);
+    }
   };
   auto issue = [&](int tix) {
 #pragma unroll
@@ -826,7 +895,15 @@ __global__ __launch_bounds__(256, 1) void mla_contig_kernel(const MlaArgs a) {
   bool jump = false;
   auto xpiece = [&](f32x16_t& s, int tix, int k) {
     if (k == 0) {
-      if (__builtin_amdgcn_readfirstlane(tix * kT2 + kT2 > n_tok)) {  // positions past the split end
+      if constexpr (SPARSE) {
+        const uint32_t holes = holes_of(tix);
+        if (holes != 0u) {
+          const uint32_t hl = holes >> (4 * half);  // bit 8 (v / 4) + v % 4: token of s[v]
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            if ((hl >> (8 * (v / 4) + (v % 4))) & 1u) s[v] = NEG_INF;
+        }
+      } else if (__builtin_amdgcn_readfirstlane(tix * kT2 + kT2 > n_tok)) {  // positions past the split end
 #pragma unroll
         for (int v = 0; v < 16; ++v)
           if (tix * kT2 + 8 * (v / 4) + 4 * half + (v % 4) >= n_tok) s[v] = NEG_INF;
@@ -1009,7 +1086,7 @@ __global__ __launch_bounds__(256, 1) void mla_contig_kernel(const MlaArgs a) {
   // tile loops have no early exit, so the accumulators follow one path.
   f32x16_t s;
   bool vote = false;
-  while (n_tiles > 0) {
+  while (n_tiles_run > 0) {
     prime(s);
     bool again = false;
     // iterations that request a whole tile, the one that requests the
@@ -1081,10 +1158,23 @@ hipError_t launch_nw(const MlaArgs& a, hipStream_t s) {
 
 int mla_heads_per_workgroup(int H) { return H % 128 == 0 ? 128 : 64; }
 
+bool mla_sparse_on_tile32(const MlaArgs& a) {
+  if (!a.idx || a.heads_per_wg != 128 || a.H % 128 != 0 || a.num_splits < 1) return false;
+  const int64_t per = ((int64_t)a.k_sel + a.num_splits - 1) / a.num_splits;
+  return per <= (int64_t)kSparseTiles * kT2 && (int64_t)a.S_max * kRowBytes < (int64_t(1) << 32);
+}
+
+bool mla_uses_tile32(const MlaArgs& a) {
+  if (a.num_splits < 1) return false;
+  if (!a.idx && !a.page_table && a.heads_per_wg == 128 && a.H % 128 == 0) return true;
+  return mla_sparse_on_tile32(a);
+}
+
 hipError_t launch_mla(const MlaArgs& a, hipStream_t s) {
-  if (!a.idx && !a.page_table && a.heads_per_wg == 128 && a.H % 128 == 0) {
+  if (mla_uses_tile32(a)) {
     dim3 grid(a.B, a.num_splits, a.H / 128);
-    launch_kernel(mla_contig_kernel, grid, dim3(256), s, a);
+    if (a.idx) launch_kernel(mla_tile32_kernel<true>, grid, dim3(256), s, a);
+    else launch_kernel(mla_tile32_kernel<false>, grid, dim3(256), s, a);
     return hipGetLastError();
   }
   if (a.heads_per_wg == 128 && a.H % 128 == 0) return launch_nw<4>(a, s);

@@ -256,6 +256,26 @@ def test_sparse_mla_split_capacity(k_sel):
     assert_lse_close(glse, wlse, 1e-5, f"sparse k={k_sel}")
 
 
+@pytest.mark.parametrize("k_sel", [2048, 1000])
+def test_sparse_mla_128_heads_tile32_holes(k_sel):
+    """The automatic plan for 128 heads runs sparse MLA on the 32-row kernel
+    (splits of at most 256 positions).  Holes that empty whole 32-row tiles in
+    the middle of a split, a split whose only valid row is its last position,
+    repeated rows (counted twice), and a list length that is not a multiple of
+    32."""
+    lens = [9000, 7000, 3000, 5000]
+    m = wl.make_mla(B=4, H=128, seq_lens=lens, seed=64, name="sparse_tile32")
+    idx = wl.random_topk_indices(B=4, seq_lens=lens, k=k_sel, seed=65)
+    idx[0, 32:96] = -1          # two whole tiles
+    idx[1, 64:127] = -1         # all but the last position of a 64-position split
+    idx[2, 5::7] = -1           # scattered holes
+    idx[3, 10:20] = idx[3, 100:110]  # repeated rows
+    got, glse = run_sparse(m, idx, 0)
+    want, wlse = oracle.mla(m.q, m.latent, idx=idx, scale=m.scale)
+    assert_rows_close(got, want, TOL_BF16, f"sparse tile32 k={k_sel}")
+    assert_lse_close(glse, wlse, 1e-5, f"sparse tile32 k={k_sel}")
+
+
 def test_sparse_with_all_tokens_equals_dense():
     m = wl.make_mla(B=2, H=64, seq_lens=[256, 256], seed=54)
     idx = torch.arange(256, dtype=torch.int32).repeat(2, 1)
