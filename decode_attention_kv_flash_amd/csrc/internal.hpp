@@ -141,9 +141,10 @@ constexpr int kMlaSparseTile32Tokens = 256;
 // call may take 64 when H allows 128 (MlaArgs::heads_per_wg).
 int mla_heads_per_workgroup(int H);
 hipError_t launch_mla(const MlaArgs& a, hipStream_t s);
-// Whether launch_mla runs the 32-row kernel (dense contiguous 128-head calls,
-// and sparse 128-head calls whose splits hold at most kMlaSparseTile32Tokens
-// positions of a cache with S_max * 1152 < 2^32).
+// Whether launch_mla runs the 32-row kernel (dense contiguous 128-head calls;
+// sparse 128-head calls whose splits hold at most kMlaSparseTile32Tokens
+// positions of a cache with S_max * 1152 < 2^32; paged 128-head calls with
+// pages of at least 8 rows and at most 128 pages per split).
 bool mla_uses_tile32(const MlaArgs& a);
 bool mla_sparse_on_tile32(const MlaArgs& a);
 

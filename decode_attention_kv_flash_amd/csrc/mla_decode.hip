@@ -729,8 +729,14 @@ __device__ __forceinline__ int swz32(int r) {
   return ((m & 1) << 2) | (m >> 1);
 }
 
-template <bool SPARSE>
+// Where a tile's rows come from: a contiguous cache, a sparse list, or a
+// paged cache with pages of at least 8 rows.
+enum : int { kSrcContig = 0, kSrcSparse = 1, kSrcPaged = 2 };
+
+template <int SRC>
 __global__ __launch_bounds__(256, 1) void mla_tile32_kernel(const MlaArgs a) {
+  constexpr bool SPARSE = SRC == kSrcSparse;
+  constexpr bool PAGED = SRC == kSrcPaged;
   constexpr int kKS = kDq / 16;          // 36 score k-steps of 16 dims
   constexpr int kNT = kDc / 4 / 32;      // 4 output tiles of 32 dims per wave
   constexpr int kP1 = 4;                 // P.V MFMAs in the score phase (of 32)
@@ -753,7 +759,7 @@ __global__ __launch_bounds__(256, 1) void mla_tile32_kernel(const MlaArgs a) {
   // the split: positions [f_begin, f_begin + n_tok) of the sequence (or list)
   int N, f_begin, n_tok;
   auto place_split = [&](int len) {
-    N = SPARSE ? len : max(0, min(len, a.S_max));
+    N = SPARSE ? len : max(0, min(len, PAGED ? a.page_size * a.max_pages : a.S_max));
     const int per = ((N + a.num_splits - 1) / a.num_splits + kT2 - 1) / kT2 * kT2;
     f_begin = min(N, split * per);
     n_tok = min(N, f_begin + per) - f_begin;
@@ -761,7 +767,18 @@ __global__ __launch_bounds__(256, 1) void mla_tile32_kernel(const MlaArgs a) {
   // SPARSE: the split's list entries first (see below); dense: the sequence
   // length; then the query rows while either is in flight
   int len_raw = 0, cids = 0, lid[4] = {-1, -1, -1, -1};
-  if constexpr (SPARSE) {
+  // PAGED: the page-table entries of the split's pages (at most 128), lane l
+  // of pe[0] / pe[1] holding page first_page + l / + 64 + l; requested before
+  // the query rows, after the sequence length they depend on
+  int pe[2] = {0, 0}, first_page = 0;
+  if constexpr (PAGED) {
+    place_split(a.seq_lens[b]);
+    first_page = f_begin >> a.log2_page;
+    const int n_pages = n_tok > 0 ? ((f_begin + n_tok - 1) >> a.log2_page) - first_page + 1 : 0;
+    const int32_t* row = a.page_table + (size_t)b * a.max_pages + first_page;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) pe[u] = 64 * u + lane < n_pages ? row[64 * u + lane] : 0;
+  } else if constexpr (SPARSE) {
     place_split(a.k_sel);
     const int32_t* list = a.idx + (size_t)b * a.k_sel + f_begin;
     const int p = 32 * (lane >> 3) + 8 * wave + (lane & 7);
@@ -779,7 +796,7 @@ __global__ __launch_bounds__(256, 1) void mla_tile32_kernel(const MlaArgs a) {
     for (int k = 0; k < kKS; ++k) qf[k] = *(const bf16x8_t*)(qrow + 16 * k);
   }
   __builtin_amdgcn_sched_barrier(0);
-  if constexpr (!SPARSE) place_split(len_raw);
+  if constexpr (SRC == kSrcContig) place_split(len_raw);
   const int n_tiles = (n_tok + kT2 - 1) / kT2;
 
   const uint32_t tiles_base = lds_address(tiles);
@@ -838,7 +855,8 @@ __global__ __launch_bounds__(256, 1) void mla_tile32_kernel(const MlaArgs a) {
     else coff2[j / 2] |= off << 16;
   }
   auto coff = [&](int j) -> uint32_t { return j % 2 == 0 ? coff2[j / 2] & 0xffffu : coff2[j / 2] >> 16; };
-  const char* latent = (const char*)a.latent + ((size_t)b * a.S_max + (SPARSE ? 0 : f_begin)) * kRowBytes;
+  const char* latent = (const char*)a.latent + (SRC == kSrcContig ? ((size_t)b * a.S_max + f_begin) * kRowBytes
+                                                : SPARSE ? (size_t)b * a.S_max * kRowBytes : 0);
   auto tile_src = [&](int tix) -> const char* { return latent + (size_t)tix * kT2Bytes; };
   // source offset of copy j for tile tix (rows past the split end re-read its
   // last row: finite data whose P is 0)
@@ -862,6 +880,23 @@ __global__ __launch_bounds__(256, 1) void mla_tile32_kernel(const MlaArgs a) {
       const int rid = up ? r_hi : r_lo;
       const uint32_t c16 = coff(j) - (uint32_t)(8 * wave + lo + (up ? 1 : 0)) * kRowBytes;
       copy_to_lds_sv((uint32_t)(valid_row(rid) ? rid : fill) * kRowBytes + c16, latent, dst);
+    } else if constexpr (PAGED) {
+      // the wave's eight rows of the tile lie in one page (pages of >= 8
+      // rows, tiles at multiples of 32); rows past the split end re-read its
+      // last row, in the last row's page when the whole block is past it
+      const int p0 = min(tix * kT2 + 8 * wave, n_tok - 1);  // the block's first row, in the split
+      const int pos = f_begin + p0;
+      const int pg = (pos >> a.log2_page) - first_page;
+      const int phys = __builtin_amdgcn_readlane(pg < 64 ? pe[0] : pe[1], pg & 63);
+      const int64_t row0 = (int64_t)phys * a.page_size + (pos & (a.page_size - 1));
+      if (whole) {
+        copy_to_lds_sv(coff(j), latent + (row0 - 8 * wave) * kRowBytes, dst);
+      } else {
+        const uint32_t o = coff(j);
+        const uint32_t r = o / kRowBytes;  // tile row 8 wave + i
+        const uint32_t i = min(r - 8u * (uint32_t)wave, (uint32_t)(n_tok - 1 - p0));
+        copy_to_lds_sv(i * kRowBytes + (o - r * kRowBytes), latent + row0 * kRowBytes, dst);
+      }
     } else {
       copy_to_lds_sv(copy_off(tix, j, whole), tile_src(tix), dst);
     }
@@ -1164,17 +1199,28 @@ bool mla_sparse_on_tile32(const MlaArgs& a) {
   return per <= (int64_t)kSparseTiles * kT2 && (int64_t)a.S_max * kRowBytes < (int64_t(1) << 32);
 }
 
+// A paged call runs there when its pages hold at least 8 rows (a power of
+// two) and a split spans at most 128 pages.
+bool mla_paged_on_tile32(const MlaArgs& a) {
+  if (a.idx || !a.page_table || a.heads_per_wg != 128 || a.H % 128 != 0 || a.num_splits < 1) return false;
+  if (a.page_size < 8 || (a.page_size & (a.page_size - 1)) != 0) return false;
+  const int64_t cap = (int64_t)a.page_size * a.max_pages;
+  const int64_t per = ((cap + a.num_splits - 1) / a.num_splits + kT2 - 1) / kT2 * kT2;
+  return per / a.page_size + 2 <= 128;
+}
+
 bool mla_uses_tile32(const MlaArgs& a) {
   if (a.num_splits < 1) return false;
   if (!a.idx && !a.page_table && a.heads_per_wg == 128 && a.H % 128 == 0) return true;
-  return mla_sparse_on_tile32(a);
+  return mla_sparse_on_tile32(a) || mla_paged_on_tile32(a);
 }
 
 hipError_t launch_mla(const MlaArgs& a, hipStream_t s) {
   if (mla_uses_tile32(a)) {
     dim3 grid(a.B, a.num_splits, a.H / 128);
-    if (a.idx) launch_kernel(mla_tile32_kernel<true>, grid, dim3(256), s, a);
-    else launch_kernel(mla_tile32_kernel<false>, grid, dim3(256), s, a);
+    if (a.idx) launch_kernel(mla_tile32_kernel<kSrcSparse>, grid, dim3(256), s, a);
+    else if (a.page_table) launch_kernel(mla_tile32_kernel<kSrcPaged>, grid, dim3(256), s, a);
+    else launch_kernel(mla_tile32_kernel<kSrcContig>, grid, dim3(256), s, a);
     return hipGetLastError();
   }
   if (a.heads_per_wg == 128 && a.H % 128 == 0) return launch_nw<4>(a, s);

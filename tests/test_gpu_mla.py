@@ -70,6 +70,46 @@ def test_mla_paged_equals_contiguous():
     check(x, 2, page_table=pt, latent=cache)
 
 
+def _paged(x, P, seed):
+    """x's latent rows scattered over shuffled pages of P rows (two spare
+    pages, never referenced, at random places in the pool)."""
+    lens = x.seq_lens.tolist()
+    n_pages = [(L + P - 1) // P for L in lens]
+    total = sum(n_pages) + 2
+    perm = torch.randperm(total, generator=torch.Generator().manual_seed(seed))
+    pt = torch.zeros(x.B, max(max(n_pages), 1), dtype=torch.int32)
+    cache = torch.full((total, P, 576), 3.0, dtype=torch.bfloat16)
+    off = 0
+    for b, L in enumerate(lens):
+        for j in range(n_pages[b]):
+            phys = int(perm[off + j])
+            pt[b, j] = phys
+            t0, t1 = j * P, min(L, (j + 1) * P)
+            cache[phys, : t1 - t0] = x.latent[b, t0:t1]
+        off += n_pages[b]
+    return pt, cache
+
+
+@pytest.mark.parametrize("P", [4, 8, 16, 64])
+@pytest.mark.parametrize("splits", [0, 1, 3])
+def test_mla_paged_128_heads(P, splits):
+    """128 heads over pages of P rows: pages of 8 or more rows run the 32-row
+    kernel, whose paged tiles must match its contiguous ones bit for bit;
+    pages of 4 rows, and 2000 tokens in one split of 8-row pages (250 pages),
+    take the 64-row kernel."""
+    x = wl.make_mla(B=4, H=128, seq_lens=[1, 33, 517, 2000], seed=46, name=f"mla_paged_p{P}")
+    pt, cache = _paged(x, P, seed=P)
+    check(x, splits, page_table=pt, latent=cache)
+    # explicit splits: the 32-row kernel takes the call when a split spans at
+    # most 126 pages (its 32-row multiple of cache positions, plus two)
+    per = -(-(-(-P * pt.shape[1] // max(splits, 1)) // 32)) * 32
+    if P >= 8 and splits > 0 and per // P + 2 <= 128:
+        cont, clse = run_gpu(x, splits)
+        paged, plse = run_gpu(x, splits, page_table=pt, latent=cache)
+        assert torch.equal(cont, paged)
+        assert torch.equal(clse, plse)
+
+
 @pytest.fixture(scope="module")
 def cfg4():
     say("[mla] generating DeepSeek-V3-shaped MLA decode: B32 H128 576-wide latent 16384 tokens")
