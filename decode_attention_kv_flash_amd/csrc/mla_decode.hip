@@ -740,6 +740,8 @@ __global__ __launch_bounds__(256, 1) void mla_tile32_kernel(const MlaArgs a) {
   constexpr int kKS = kDq / 16;          // 36 score k-steps of 16 dims
   constexpr int kNT = kDc / 4 / 32;      // 4 output tiles of 32 dims per wave
   constexpr int kP1 = 4;                 // P.V MFMAs in the score phase (of 32)
+  constexpr int kDefer = 4;              // P.V MFMAs run after the barrier (of 32)
+  static_assert(kDefer % 4 == 0 && kDefer <= 8, "whole head-group rounds, two value fragments");
   const float NEG_INF = -__builtin_inff();
   __shared__ __attribute__((aligned(16))) char tiles[kT2Buffers * kT2Bytes];
   __shared__ __attribute__((aligned(16))) char pbuf[2][kP2Bytes];
@@ -924,9 +926,12 @@ __global__ __launch_bounds__(256, 1) void mla_tile32_kernel(const MlaArgs a) {
   // lane's share of the denominator
   float m_run = NEG_INF, m_seen = NEG_INF, l_run = 0.f;
 
-  // Softmax of one tile's scores s (tile tix) in pieces; piece k of 8.  Writes
-  // the tile's P (and this wave's vote) to pbuf[tix & 1].
-  float mxs, nmu;
+  // Softmax of one tile's scores s (tile tix) in kXSteps steps of a few VALU
+  // instructions each, one per P.V MFMA (a matrix-core instruction hides a
+  // handful).  Writes the tile's P (and this wave's vote) to pbuf[tix & 1].
+  constexpr int kXSteps = 16;
+  float m8a, m8b, mxs, mx, nmu;
+  uint4 pv;
   bool jump = false;
   auto xpiece = [&](f32x16_t& s, int tix, int k) {
     if (k == 0) {
@@ -943,30 +948,32 @@ __global__ __launch_bounds__(256, 1) void mla_tile32_kernel(const MlaArgs a) {
         for (int v = 0; v < 16; ++v)
           if (tix * kT2 + 8 * (v / 4) + 4 * half + (v % 4) >= n_tok) s[v] = NEG_INF;
       }
-      const float m8a = max3(s[0], s[1], max3(s[2], s[3], s[4]));
-      const float m8b = max3(s[5], s[6], max3(s[7], s[8], s[9]));
+      m8a = max3(s[0], s[1], max3(s[2], s[3], s[4]));
+    } else if (k == 1) {
+      m8b = max3(s[5], s[6], max3(s[7], s[8], s[9]));
+    } else if (k == 2) {
       const float m8c = max3(s[10], s[11], max3(s[12], s[13], max2(s[14], s[15])));
       mxs = max3(m8a, m8b, m8c);
-    } else if (k == 1) {
+    } else if (k == 3) {
       // lanes lj and lj + 32 hold the two halves of head lj's tokens
       const auto w = __builtin_amdgcn_permlane32_swap(__float_as_uint(mxs), __float_as_uint(mxs), false, false);
-      const float mx = max2(__uint_as_float(w[0]), __uint_as_float(w[1])) * a.scale_log2;
+      mx = max2(__uint_as_float(w[0]), __uint_as_float(w[1])) * a.scale_log2;
       m_seen = max2(m_seen, mx);
+    } else if (k == 4) {
       // a head's first scores set its reference (its O is still zero); a
       // later score past it by more than kTau asks for a restart
       jump = mx > m_run + kTau && m_run != NEG_INF;
       m_run = m_run == NEG_INF ? mx : m_run;
       nmu = m_run == NEG_INF ? 0.f : -m_run;
-    } else if (k >= 2 && k < 6) {
-      const int v0 = 4 * (k - 2);
-#pragma unroll
-      for (int v = v0; v < v0 + 4; ++v) s[v] = fast_exp2(__builtin_fmaf(s[v], a.scale_log2, nmu));
-      l_run += (s[v0] + s[v0 + 1]) + (s[v0 + 2] + s[v0 + 3]);
-    } else if (k == 6 || k == 7) {
-      // P of k-step ks = k - 6: tokens 16 ks + 8 (v / 4) + 4 half + v % 4 for
+    } else if ((k >= 5 && k < 9) || (k >= 10 && k < 14)) {
+      const int v0 = 2 * (k < 9 ? k - 5 : k - 6);
+      s[v0] = fast_exp2(__builtin_fmaf(s[v0], a.scale_log2, nmu));
+      s[v0 + 1] = fast_exp2(__builtin_fmaf(s[v0 + 1], a.scale_log2, nmu));
+      l_run += s[v0] + s[v0 + 1];
+    } else if (k == 9 || k == 14) {
+      // P of k-step ks: tokens 16 ks + 8 (v / 4) + 4 half + v % 4 for
       // v = 8 ks .. 8 ks + 7, in the 32x32x16 A layout
-      const int ks = k - 6;
-      uint4 pv;
+      const int ks = k == 14;
       pv.x = pack_bf16x2(s[8 * ks + 0], s[8 * ks + 1]);
       pv.y = pack_bf16x2(s[8 * ks + 2], s[8 * ks + 3]);
       pv.z = pack_bf16x2(s[8 * ks + 4], s[8 * ks + 5]);
@@ -976,6 +983,9 @@ __global__ __launch_bounds__(256, 1) void mla_tile32_kernel(const MlaArgs a) {
         const bool any = __ballot(jump) != 0;
         if (lane == 0) pv.x = (pv.x & 0xffff7fffu) | (any ? 0x8000u : 0u);
       }
+    }
+    if (k == 10 || k == 15) {
+      const int ks = k == 15;
       const uint32_t dst = pbuf_base + (uint32_t)(tix & 1) * kP2Bytes + 16u * (uint32_t)((ks * 4 + wave) * 64 + lane);
       *(lds_bf16x8*)(uintptr_t)dst = __builtin_bit_cast(bf16x8_t, pv);
     }
@@ -994,9 +1004,15 @@ __global__ __launch_bounds__(256, 1) void mla_tile32_kernel(const MlaArgs a) {
                  : "+a"(acc[hg * kNT + nt]) : "v"(pa[hg]), "v"(vr[nt & 1]));
   };
 
+  // P fragments of one k-step (head groups) and value fragments; the last
+  // kDefer P.V MFMAs of a tile keep theirs across the barrier
+  bf16x8_t pa[4], vr[2];
+  auto defer_mfma = [&](int i) { pv_mfma(32 - kDefer + i, pa, vr); };
+
   // The stream of iteration t: S(t + 1) || P.V(t) || softmax(t + 1) || copies of
   // t + 3: none (kCopy = 0), of a whole tile (1) or of the split's last,
-  // partial tile (2).
+  // partial tile (2).  It opens with the last kDefer P.V MFMAs of tile t - 1,
+  // whose operands are in registers, while the first LDS reads are in flight.
   auto stream = [&](auto copy_kind, int t, f32x16_t& s, bool& vote) {
     constexpr int kCopy = decltype(copy_kind)::value;
     const uint32_t sbuf = buffer(t + 1), vbuf = buffer(t);
@@ -1028,7 +1044,6 @@ __global__ __launch_bounds__(256, 1) void mla_tile32_kernel(const MlaArgs a) {
     auto pread = [&](int ks, int hg) -> bf16x8_t {
       return *(const lds_bf16x8*)(uintptr_t)(pin + 16u * (uint32_t)((ks * 4 + hg) * 64 + lane));
     };
-    bf16x8_t pa[4], vr[2];  // P fragments of one k-step (head groups), value fragments
     // value fragments: (ks, nt) for MFMAs 16 ks + 4 nt .. + 3, two in flight
     auto vload = [&](int u) {  // load the fragment MFMA u first needs
       const int ks = u >> 4, nt = (u >> 2) & 3;
@@ -1040,8 +1055,15 @@ __global__ __launch_bounds__(256, 1) void mla_tile32_kernel(const MlaArgs a) {
 #pragma unroll
     for (int j = 0; j < kRing; ++j) ar[j] = aread(j);
     __builtin_amdgcn_sched_barrier(0);
+    // each head group's P fragment is replaced once its last deferred use is issued
 #pragma unroll
-    for (int hg = 0; hg < 4; ++hg) pa[hg] = pread(0, hg);
+    for (int i = 0; i < kDefer; ++i) {
+      defer_mfma(i);
+      if (i >= kDefer - 4) pa[i % 4] = pread(0, i % 4);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int hg = kDefer; hg < 4; ++hg) pa[hg] = pread(0, hg);
     vload(0);
     vload(4);
     __builtin_amdgcn_sched_barrier(0);
@@ -1070,17 +1092,19 @@ __global__ __launch_bounds__(256, 1) void mla_tile32_kernel(const MlaArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    // phase 2: the remaining P.V MFMAs with the softmax of tile t + 1 between
-    // them (its first read of the scores comes two MFMAs after the last score
-    // MFMA, past the 18 wait states a 32x32 MFMA result needs)
+    // phase 2: the P.V MFMAs up to the deferred ones, with the softmax of
+    // tile t + 1 between them (its first read of the scores comes two MFMAs
+    // after the last score MFMA, past the 18 wait states a 32x32 MFMA result
+    // needs)
+    static_assert(2 + kXSteps <= 28 - kDefer, "the softmax fits the phase");
 #pragma unroll
-    for (int u = kP1; u < 32; ++u) {
+    for (int u = kP1; u < 32 - kDefer; ++u) {
       const int w = u - kP1;
       pv_mfma(u, pa, vr);
       if ((u & 3) == 3 && u + 5 < 32) vload(u + 5);
       // k-step 1's P fragment of a head group once k-step 0's last use is past
       if (u >= 12 && u < 16) pa[u - 12] = pread(1, u - 12);
-      if (w >= 2 && (w - 2) % 3 == 0 && (w - 2) / 3 < 8) xpiece(s, t + 1, (w - 2) / 3);
+      if (w >= 2 && w - 2 < kXSteps) xpiece(s, t + 1, w - 2);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -1111,7 +1135,7 @@ __global__ __launch_bounds__(256, 1) void mla_tile32_kernel(const MlaArgs a) {
     }
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s));
 #pragma unroll
-    for (int k = 0; k < 8; ++k) xpiece(s, 0, k);
+    for (int k = 0; k < kXSteps; ++k) xpiece(s, 0, k);
     if (first >= 3) barrier_in_flight<kT2Copies>();  // tile 1 complete; P(0) visible
     else barrier_in_flight<0>();
   };
@@ -1123,6 +1147,10 @@ __global__ __launch_bounds__(256, 1) void mla_tile32_kernel(const MlaArgs a) {
   bool vote = false;
   while (n_tiles_run > 0) {
     prime(s);
+    // the first iteration's deferred MFMAs have no tile before them: zero operands
+#pragma unroll
+    for (int hg = 0; hg < 4; ++hg) pa[hg] = bf16x8_t{};
+    vr[0] = vr[1] = bf16x8_t{};
     bool again = false;
     // iterations that request a whole tile, the one that requests the
     // split's partial last tile, then the tail
@@ -1144,6 +1172,8 @@ __global__ __launch_bounds__(256, 1) void mla_tile32_kernel(const MlaArgs a) {
       barrier_in_flight<0>();
       again |= vote;
     }
+#pragma unroll
+    for (int i = 0; i < kDefer; ++i) defer_mfma(i);
     if (!again) break;
     // some head's maximum jumped: redo the split with every head's reference
     // at the largest score it has seen (each restart raises a reference by
