@@ -72,6 +72,7 @@ constexpr int kKSteps = kDq / 32;                         // 18 score k-steps of
 constexpr int kNTiles = kDc / 32;                         // 16 output tiles of 32 dims
 constexpr int kRing = 3;                                  // LDS fragments in flight per operand
 constexpr float kTau = 64.0f;                             // reference-maximum slack (log2)
+constexpr float kTwoTau = 18446744073709551616.0f;         // 2^kTau
 constexpr uint32_t kPad = 0x80000000u;                    // row-table flag: no token here
 constexpr int kMaxTiles = kMlaMaxSplitTokens / kTile;
 constexpr int kRowTable = (kMaxTiles + 1) * kTile;  // plus one tile of padding
@@ -803,6 +804,8 @@ __global__ __launch_bounds__(256, 1) void mla_tile32_kernel(const MlaArgs a) {
 
   const uint32_t tiles_base = lds_address(tiles);
   const uint32_t pbuf_base = lds_address(pbuf);
+  // this lane's slot in a P buffer: reads and writes add uniform offsets
+  const uint32_t p_lane = pbuf_base + 16u * (uint32_t)lane;
   auto buffer = [&](int tix) -> uint32_t { return tiles_base + (uint32_t)(tix & 3) * kT2Bytes; };
 
   // SPARSE (a split of at most kSparseTiles tiles): the validity of each
@@ -926,14 +929,46 @@ __global__ __launch_bounds__(256, 1) void mla_tile32_kernel(const MlaArgs a) {
   // lane's share of the denominator
   float m_run = NEG_INF, m_seen = NEG_INF, l_run = 0.f;
 
-  // Softmax of one tile's scores s (tile tix) in kXSteps steps of a few VALU
-  // instructions each, one per P.V MFMA (a matrix-core instruction hides a
-  // handful).  Writes the tile's P (and this wave's vote) to pbuf[tix & 1].
-  constexpr int kXSteps = 16;
-  float m8a, m8b, mxs, mx, nmu;
+  // Softmax of one tile's scores s (tile tix) in steps of a few VALU
+  // instructions, one per P.V MFMA (a matrix-core instruction hides a
+  // handful).  Three kinds of pass use it:
+  //   full (kXSteps steps, the first tile of a pass): each head's maximum over
+  //     the tile becomes its reference unless it has one; a head left without
+  //     one (no score in the tile) votes;
+  //   lean (kXLean, every later tile): no maximum; a lane votes when its 16
+  //     probabilities sum past 2^kTau, which any score past the reference by
+  //     more than kTau makes them do;
+  //   max (kXMax): only each head's maximum, into m_seen.
+  // Full and lean write the tile's P, and the wave's vote in its k-step 1
+  // fragment, to pbuf[tix & 1].
+  constexpr int kFull = 0, kLean = 1, kMaxOnly = 2;
+  constexpr int kXSteps = 16, kXLean = 11, kXMax = 4;
+  float m8a, m8b, mxs, mx, nmu, tsum;
   uint4 pv;
   bool jump = false;
-  auto xpiece = [&](f32x16_t& s, int tix, int k) {
+  auto exp_pair = [&](f32x16_t& s, int v0) {
+    s[v0] = fast_exp2(__builtin_fmaf(s[v0], a.scale_log2, nmu));
+    s[v0 + 1] = fast_exp2(__builtin_fmaf(s[v0 + 1], a.scale_log2, nmu));
+  };
+  // P of k-step ks: tokens 16 ks + 8 (v / 4) + 4 half + v % 4 for v = 8 ks ..
+  // 8 ks + 7, in the 32x32x16 A layout; k-step 1 carries the vote on the sign
+  // bit of lane 0's first value
+  auto pack = [&](const f32x16_t& s, int ks) {
+    pv.x = pack_bf16x2(s[8 * ks + 0], s[8 * ks + 1]);
+    pv.y = pack_bf16x2(s[8 * ks + 2], s[8 * ks + 3]);
+    pv.z = pack_bf16x2(s[8 * ks + 4], s[8 * ks + 5]);
+    pv.w = pack_bf16x2(s[8 * ks + 6], s[8 * ks + 7]);
+    if (ks == 1) {
+      const bool any = __ballot(jump) != 0;
+      if (lane == 0) pv.x = (pv.x & 0xffff7fffu) | (any ? 0x8000u : 0u);
+    }
+  };
+  auto put = [&](int tix, int ks) {
+    const uint32_t dst = p_lane + (uint32_t)(tix & 1) * kP2Bytes + 1024u * (uint32_t)(ks * 4 + wave);
+    *(lds_bf16x8*)(uintptr_t)dst = __builtin_bit_cast(bf16x8_t, pv);
+  };
+  auto xpiece = [&](auto mode, f32x16_t& s, int tix, int k) {
+    constexpr int MODE = decltype(mode)::value;
     if (k == 0) {
       if constexpr (SPARSE) {
         const uint32_t holes = holes_of(tix);
@@ -948,53 +983,74 @@ __global__ __launch_bounds__(256, 1) void mla_tile32_kernel(const MlaArgs a) {
         for (int v = 0; v < 16; ++v)
           if (tix * kT2 + 8 * (v / 4) + 4 * half + (v % 4) >= n_tok) s[v] = NEG_INF;
       }
-      m8a = max3(s[0], s[1], max3(s[2], s[3], s[4]));
-    } else if (k == 1) {
-      m8b = max3(s[5], s[6], max3(s[7], s[8], s[9]));
-    } else if (k == 2) {
-      const float m8c = max3(s[10], s[11], max3(s[12], s[13], max2(s[14], s[15])));
-      mxs = max3(m8a, m8b, m8c);
-    } else if (k == 3) {
-      // lanes lj and lj + 32 hold the two halves of head lj's tokens
-      const auto w = __builtin_amdgcn_permlane32_swap(__float_as_uint(mxs), __float_as_uint(mxs), false, false);
-      mx = max2(__uint_as_float(w[0]), __uint_as_float(w[1])) * a.scale_log2;
-      m_seen = max2(m_seen, mx);
-    } else if (k == 4) {
-      // a head's first scores set its reference (its O is still zero); a
-      // later score past it by more than kTau asks for a restart
-      jump = mx > m_run + kTau && m_run != NEG_INF;
-      m_run = m_run == NEG_INF ? mx : m_run;
-      nmu = m_run == NEG_INF ? 0.f : -m_run;
-    } else if ((k >= 5 && k < 9) || (k >= 10 && k < 14)) {
-      const int v0 = 2 * (k < 9 ? k - 5 : k - 6);
-      s[v0] = fast_exp2(__builtin_fmaf(s[v0], a.scale_log2, nmu));
-      s[v0 + 1] = fast_exp2(__builtin_fmaf(s[v0 + 1], a.scale_log2, nmu));
-      l_run += s[v0] + s[v0 + 1];
-    } else if (k == 9 || k == 14) {
-      // P of k-step ks: tokens 16 ks + 8 (v / 4) + 4 half + v % 4 for
-      // v = 8 ks .. 8 ks + 7, in the 32x32x16 A layout
-      const int ks = k == 14;
-      pv.x = pack_bf16x2(s[8 * ks + 0], s[8 * ks + 1]);
-      pv.y = pack_bf16x2(s[8 * ks + 2], s[8 * ks + 3]);
-      pv.z = pack_bf16x2(s[8 * ks + 4], s[8 * ks + 5]);
-      pv.w = pack_bf16x2(s[8 * ks + 6], s[8 * ks + 7]);
-      if (ks == 0) {
-        // the vote: lane 0's first value carries the wave's sign bit
-        const bool any = __ballot(jump) != 0;
-        if (lane == 0) pv.x = (pv.x & 0xffff7fffu) | (any ? 0x8000u : 0u);
-      }
     }
-    if (k == 10 || k == 15) {
-      const int ks = k == 15;
-      const uint32_t dst = pbuf_base + (uint32_t)(tix & 1) * kP2Bytes + 16u * (uint32_t)((ks * 4 + wave) * 64 + lane);
-      *(lds_bf16x8*)(uintptr_t)dst = __builtin_bit_cast(bf16x8_t, pv);
+    if constexpr (MODE == kLean) {
+      // 1..8: exponentials of s[0..15] (k-step 0's P packed at 5, stored at
+      // 6); 9: the sum, the vote, k-step 1's P; 10: stored
+      if (k >= 1 && k <= 8) {
+        const int v0 = 2 * (k - 1);
+        exp_pair(s, v0);
+        const float two = s[v0] + s[v0 + 1];
+        tsum = k == 1 ? two : tsum + two;
+      }
+      if (k == 5) pack(s, 0);
+      if (k == 6) put(tix, 0);
+      if (k == 9) {
+        jump = tsum > kTwoTau;
+        l_run += tsum;
+        pack(s, 1);
+      }
+      if (k == 10) put(tix, 1);
+    } else {
+      if (k == 0) {
+        m8a = max3(s[0], s[1], max3(s[2], s[3], s[4]));
+      } else if (k == 1) {
+        m8b = max3(s[5], s[6], max3(s[7], s[8], s[9]));
+      } else if (k == 2) {
+        const float m8c = max3(s[10], s[11], max3(s[12], s[13], max2(s[14], s[15])));
+        mxs = max3(m8a, m8b, m8c);
+      } else if (k == 3) {
+        // lanes lj and lj + 32 hold the two halves of head lj's tokens
+        const auto w = __builtin_amdgcn_permlane32_swap(__float_as_uint(mxs), __float_as_uint(mxs), false, false);
+        mx = max2(__uint_as_float(w[0]), __uint_as_float(w[1])) * a.scale_log2;
+        if constexpr (MODE == kMaxOnly) m_seen = max2(m_seen, mx);
+      } else if constexpr (MODE == kFull) {
+        if (k == 4) {
+          m_run = m_run == NEG_INF ? mx : m_run;
+          jump = m_run == NEG_INF;
+          nmu = m_run == NEG_INF ? 0.f : -m_run;
+        } else if ((k >= 5 && k < 9) || (k >= 10 && k < 14)) {
+          const int v0 = 2 * (k < 9 ? k - 5 : k - 6);
+          exp_pair(s, v0);
+          l_run += s[v0] + s[v0 + 1];
+        } else if (k == 9) {
+          pack(s, 0);
+        } else if (k == 14) {
+          pack(s, 1);
+        }
+        if (k == 10) put(tix, 0);
+        if (k == 15) put(tix, 1);
+      }
     }
   };
 
   // Scores of the tile in buffer sbuf (36 MFMAs), optionally interleaved with
   // P.V MFMAs, copies and softmax pieces via the hook called at each k-step.
+  // this lane's parts of the operand addresses within a tile buffer, kept in
+  // registers except by the paged kernel (whose page entries take their place)
+  auto so_part = [&](int j) -> uint32_t { return lj * kRowBytes + 16 * ((2 * j + half) ^ sw_a); };
+  auto vo_part = [&](int j) -> uint32_t {
+    return (j < 2 ? rv : rv + 8) * kRowBytes + 16 * (16 * wave + ((4 * (j & 1) + cv) ^ (j < 2 ? sw_v0 : sw_v1))) +
+           8 * (li & 1);
+  };
+  uint32_t so_lane[4], vo_lane[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    so_lane[j] = PAGED ? 0u : so_part(j);
+    vo_lane[j] = PAGED ? 0u : vo_part(j);
+  }
   auto a_addr = [&](uint32_t sbuf, int j) -> uint32_t {  // chunk 2 k + half = 8 (k / 4) + (2 (k % 4) + half)
-    return sbuf + lj * kRowBytes + 16 * ((2 * j + half) ^ sw_a);
+    return sbuf + (PAGED ? so_part(j) : so_lane[j]);
   };
 
   // P.V MFMA u (0..31): k-step u / 16, output tile (u / 4) % 4, head group u % 4
@@ -1013,10 +1069,12 @@ __global__ __launch_bounds__(256, 1) void mla_tile32_kernel(const MlaArgs a) {
   // t + 3: none (kCopy = 0), of a whole tile (1) or of the split's last,
   // partial tile (2).  It opens with the last kDefer P.V MFMAs of tile t - 1,
   // whose operands are in registers, while the first LDS reads are in flight.
-  auto stream = [&](auto copy_kind, int t, f32x16_t& s, bool& vote) {
+  auto stream = [&](auto mode, auto copy_kind, int t, f32x16_t& s, bool& vote) {
+    constexpr int MODE = decltype(mode)::value;
+    constexpr bool PV = MODE != kMaxOnly;  // the max pass has no P.V
     constexpr int kCopy = decltype(copy_kind)::value;
     const uint32_t sbuf = buffer(t + 1), vbuf = buffer(t);
-    const uint32_t pin = pbuf_base + (uint32_t)(t & 1) * kP2Bytes;
+    const uint32_t pin = p_lane + (uint32_t)(t & 1) * kP2Bytes;
     uint32_t so[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -1026,8 +1084,8 @@ __global__ __launch_bounds__(256, 1) void mla_tile32_kernel(const MlaArgs a) {
     uint32_t vo[4];  // rows rv (+ 8), chunk groups 0 and 1 of the wave's 128 dims
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      vo[j] = vbuf + rv * kRowBytes + 16 * (16 * wave + ((4 * j + cv) ^ sw_v0)) + 8 * (li & 1);
-      vo[2 + j] = vbuf + (rv + 8) * kRowBytes + 16 * (16 * wave + ((4 * j + cv) ^ sw_v1)) + 8 * (li & 1);
+      vo[j] = vbuf + (PAGED ? vo_part(j) : vo_lane[j]);
+      vo[2 + j] = vbuf + (PAGED ? vo_part(2 + j) : vo_lane[2 + j]);
       asm volatile("" : "+v"(vo[j]), "+v"(vo[2 + j]));
     }
     auto aread = [&](int k) -> bf16x8_t {
@@ -1042,7 +1100,7 @@ __global__ __launch_bounds__(256, 1) void mla_tile32_kernel(const MlaArgs a) {
       return __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7);
     };
     auto pread = [&](int ks, int hg) -> bf16x8_t {
-      return *(const lds_bf16x8*)(uintptr_t)(pin + 16u * (uint32_t)((ks * 4 + hg) * 64 + lane));
+      return *(const lds_bf16x8*)(uintptr_t)(pin + 1024u * (uint32_t)(ks * 4 + hg));
     };
     // value fragments: (ks, nt) for MFMAs 16 ks + 4 nt .. + 3, two in flight
     auto vload = [&](int u) {  // load the fragment MFMA u first needs
@@ -1056,16 +1114,18 @@ __global__ __launch_bounds__(256, 1) void mla_tile32_kernel(const MlaArgs a) {
     for (int j = 0; j < kRing; ++j) ar[j] = aread(j);
     __builtin_amdgcn_sched_barrier(0);
     // each head group's P fragment is replaced once its last deferred use is issued
+    if constexpr (PV) {
 #pragma unroll
-    for (int i = 0; i < kDefer; ++i) {
-      defer_mfma(i);
-      if (i >= kDefer - 4) pa[i % 4] = pread(0, i % 4);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int i = 0; i < kDefer; ++i) {
+        defer_mfma(i);
+        if (i >= kDefer - 4) pa[i % 4] = pread(0, i % 4);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int hg = kDefer; hg < 4; ++hg) pa[hg] = pread(0, hg);
+      vload(0);
+      vload(4);
     }
-#pragma unroll
-    for (int hg = kDefer; hg < 4; ++hg) pa[hg] = pread(0, hg);
-    vload(0);
-    vload(4);
     __builtin_amdgcn_sched_barrier(0);
 
     // phase 1: the 36 score MFMAs, with P.V MFMAs 0 .. kP1 - 1 (at k = 3, 7,
@@ -1075,14 +1135,7 @@ __global__ __launch_bounds__(256, 1) void mla_tile32_kernel(const MlaArgs a) {
       if (k == 0) asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(ar[0]), "v"(qf[0]));
       else asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(ar[k % kRing]), "v"(qf[k]));
       if (k + kRing < kKS) ar[k % kRing] = aread(k + kRing);
-      // the vote in tile t's P: any wave's sign bit on lane 0's first value
-      // (read once the P fragments are in, for the first P.V MFMA)
-      if (k == 4) {
-        const uint32_t vote_bits = __builtin_bit_cast(uint4, pa[0]).x | __builtin_bit_cast(uint4, pa[1]).x |
-                                   __builtin_bit_cast(uint4, pa[2]).x | __builtin_bit_cast(uint4, pa[3]).x;
-        vote = (__builtin_amdgcn_readfirstlane(vote_bits) & 0x8000u) != 0;
-      }
-      if (k % 4 == 3 && k / 4 < kP1) {
+      if (PV && k % 4 == 3 && k / 4 < kP1) {
         const int u = k / 4;
         pv_mfma(u, pa, vr);
         if ((u & 3) == 3 && u + 5 < 32) vload(u + 5);
@@ -1100,18 +1153,28 @@ __global__ __launch_bounds__(256, 1) void mla_tile32_kernel(const MlaArgs a) {
 #pragma unroll
     for (int u = kP1; u < 32 - kDefer; ++u) {
       const int w = u - kP1;
-      pv_mfma(u, pa, vr);
-      if ((u & 3) == 3 && u + 5 < 32) vload(u + 5);
-      // k-step 1's P fragment of a head group once k-step 0's last use is past
-      if (u >= 12 && u < 16) pa[u - 12] = pread(1, u - 12);
-      if (w >= 2 && w - 2 < kXSteps) xpiece(s, t + 1, w - 2);
+      if constexpr (PV) {
+        pv_mfma(u, pa, vr);
+        if ((u & 3) == 3 && u + 5 < 32) vload(u + 5);
+        // k-step 1's P fragment of a head group once k-step 0's last use is past
+        if (u >= 12 && u < 16) pa[u - 12] = pread(1, u - 12);
+        // the vote in tile t's P: any wave's sign bit on lane 0's first value
+        // of k-step 1 (read once those fragments are in)
+        if (u == 20) {
+          const uint32_t vote_bits = __builtin_bit_cast(uint4, pa[0]).x | __builtin_bit_cast(uint4, pa[1]).x |
+                                     __builtin_bit_cast(uint4, pa[2]).x | __builtin_bit_cast(uint4, pa[3]).x;
+          vote = (__builtin_amdgcn_readfirstlane(vote_bits) & 0x8000u) != 0;
+        }
+      }
+      if (w >= 2 && w - 2 < (MODE == kLean ? kXLean : kXMax)) xpiece(mode, s, t + 1, w - 2);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
   // Prologue: tiles 0..2 requested; tile 0 scored, its softmax taken and its
-  // P in pbuf[0]; tile 1 complete.
-  auto prime = [&](f32x16_t& s) {
+  // P in pbuf[0] (the max pass: its maximum taken); tile 1 complete.
+  auto prime = [&](auto mode, f32x16_t& s) {
+    constexpr int MODE = decltype(mode)::value;
     const int first = min(n_tiles, 3);
     for (int t = 0; t < first; ++t) issue(t);
     if (first == 3) barrier_in_flight<2 * kT2Copies>();
@@ -1135,22 +1198,16 @@ __global__ __launch_bounds__(256, 1) void mla_tile32_kernel(const MlaArgs a) {
     }
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s));
 #pragma unroll
-    for (int k = 0; k < kXSteps; ++k) xpiece(s, 0, k);
+    for (int k = 0; k < (MODE == kFull ? kXSteps : kXMax); ++k) xpiece(mode, s, 0, k);
     if (first >= 3) barrier_in_flight<kT2Copies>();  // tile 1 complete; P(0) visible
     else barrier_in_flight<0>();
   };
 
-  // A pass runs every tile of the split; a vote seen on the way (a maximum
-  // jump) makes the whole pass run again with the raised references.  The
-  // tile loops have no early exit, so the accumulators follow one path.
+  // A pass runs every tile of the split.  The tile loops have no early exit,
+  // so the accumulators follow one path.
   f32x16_t s;
   bool vote = false;
-  while (n_tiles_run > 0) {
-    prime(s);
-    // the first iteration's deferred MFMAs have no tile before them: zero operands
-#pragma unroll
-    for (int hg = 0; hg < 4; ++hg) pa[hg] = bf16x8_t{};
-    vr[0] = vr[1] = bf16x8_t{};
+  auto tiles_after_first = [&](auto mode) -> bool {
     bool again = false;
     // iterations that request a whole tile, the one that requests the
     // split's partial last tile, then the tail
@@ -1158,31 +1215,48 @@ __global__ __launch_bounds__(256, 1) void mla_tile32_kernel(const MlaArgs a) {
     const int n_whole = min(n_copying, max(n_tok / kT2 - 3, 0));
     int t = 0;
     for (; t < n_whole; ++t) {
-      stream(std::integral_constant<int, 1>{}, t, s, vote);
+      stream(mode, std::integral_constant<int, 1>{}, t, s, vote);
       barrier_in_flight<kT2Copies>();  // tile t + 2 complete, tile t + 3 in flight
       again |= vote;
     }
     for (; t < n_copying; ++t) {
-      stream(std::integral_constant<int, 2>{}, t, s, vote);
+      stream(mode, std::integral_constant<int, 2>{}, t, s, vote);
       barrier_in_flight<kT2Copies>();
       again |= vote;
     }
     for (; t < n_tiles; ++t) {
-      stream(std::integral_constant<int, 0>{}, t, s, vote);
+      stream(mode, std::integral_constant<int, 0>{}, t, s, vote);
       barrier_in_flight<0>();
       again |= vote;
     }
+    return again;
+  };
+  // one pass, each head's reference its first tile's maximum unless set
+  auto attention_pass = [&]() -> bool {
+    prime(std::integral_constant<int, kFull>{}, s);
+    // the first iteration's deferred MFMAs have no tile before them: zero operands
+#pragma unroll
+    for (int hg = 0; hg < 4; ++hg) pa[hg] = bf16x8_t{};
+    vr[0] = vr[1] = bf16x8_t{};
+    const bool again = tiles_after_first(std::integral_constant<int, kLean>{});
 #pragma unroll
     for (int i = 0; i < kDefer; ++i) defer_mfma(i);
-    if (!again) break;
-    // some head's maximum jumped: redo the split with every head's reference
-    // at the largest score it has seen (each restart raises a reference by
-    // more than kTau; a jump needs an ordered comparison, so NaN scores never
-    // vote and restarts are few)
+    return again;
+  };
+  if (n_tiles_run > 0 && attention_pass()) {
+    // a vote: some head's score passed its reference by more than kTau, or a
+    // head had no score in its first tile.  A pass of scores alone finds
+    // every head's maximum over the split; with it as the reference the
+    // second attention pass has no jump (a jump needs an ordered comparison,
+    // so NaN scores never vote) and its vote is not read.
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::);  // in-flight MFMAs retire first
-    zero_acc();
+    m_seen = NEG_INF;
+    prime(std::integral_constant<int, kMaxOnly>{}, s);
+    (void)tiles_after_first(std::integral_constant<int, kMaxOnly>{});
     m_run = m_seen;
+    zero_acc();
     l_run = 0.f;
+    (void)attention_pass();
   }
   settle(acc);
 

@@ -261,13 +261,14 @@ def test_sparse_mla_128_heads_tile32_holes(k_sel):
     """The automatic plan for 128 heads runs sparse MLA on the 32-row kernel
     (splits of at most 256 positions).  Holes that empty whole 32-row tiles in
     the middle of a split, a split whose only valid row is its last position,
-    repeated rows (counted twice), and a list length that is not a multiple of
+    a split whose first tile has no valid row, repeated rows (counted twice), and a list length that is not a multiple of
     32."""
     lens = [9000, 7000, 3000, 5000]
     m = wl.make_mla(B=4, H=128, seq_lens=lens, seed=64, name="sparse_tile32")
     idx = wl.random_topk_indices(B=4, seq_lens=lens, k=k_sel, seed=65)
     idx[0, 32:96] = -1          # two whole tiles
     idx[1, 64:127] = -1         # all but the last position of a 64-position split
+    idx[1, 256:300] = -1        # a split whose first tile has no row
     idx[2, 5::7] = -1           # scattered holes
     idx[3, 10:20] = idx[3, 100:110]  # repeated rows
     got, glse = run_sparse(m, idx, 0)
