@@ -268,7 +268,8 @@ def test_sparse_mla_128_heads_tile32_holes(k_sel):
     idx = wl.random_topk_indices(B=4, seq_lens=lens, k=k_sel, seed=65)
     idx[0, 32:96] = -1          # two whole tiles
     idx[1, 64:127] = -1         # all but the last position of a 64-position split
-    idx[1, 256:300] = -1        # a split whose first tile has no row
+    idx[1, 256:300] = -1        # a split whose first tile has no row (splits of 128 or 256)
+    idx[1, 384:420] = -1        # the same for splits of 96, 128 or 192 positions
     idx[2, 5::7] = -1           # scattered holes
     idx[3, 10:20] = idx[3, 100:110]  # repeated rows
     got, glse = run_sparse(m, idx, 0)
