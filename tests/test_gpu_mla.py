@@ -90,7 +90,7 @@ def _paged(x, P, seed):
     return pt, cache
 
 
-@pytest.mark.parametrize("P", [4, 8, 16, 64])
+@pytest.mark.parametrize("P", [4, 8, 16, 64, 256])
 @pytest.mark.parametrize("splits", [0, 1, 3])
 def test_mla_paged_128_heads(P, splits):
     """128 heads over pages of P rows: pages of 8 or more rows run the 32-row
