@@ -132,6 +132,18 @@ def test_mla_score_jumps_restart_the_split():
     x.latent[1, 650] = (2.0 * q[1, 70]).to(torch.bfloat16)
     for splits in (1, 0):
         check(x, splits)
+    # the same jumps read through 16-row pages, and through a sparse list of
+    # every row (the 32-row kernel's paged and sparse tiles)
+    pt, cache = _paged(x, 16, seed=45)
+    for splits in (1, 3):
+        check(x, splits, page_table=pt, latent=cache)
+    idx = torch.stack([torch.arange(x.S_max, dtype=torch.int32)] * x.B)
+    idx[1, 700:] = -1
+    got, glse = api.sparse_mla_attn(dev(x.q), dev(x.latent), dev(idx), scale=x.scale)
+    torch.cuda.synchronize()
+    want, wlse = oracle.mla(x.q, x.latent, x.seq_lens, scale=x.scale)
+    assert_rows_close(got.float().cpu().reshape(-1, 512), want, TOL_BF16, "mla_spikes sparse")
+    assert_lse_close(glse.cpu().reshape(-1), wlse, 1e-5, "mla_spikes sparse")
 
 
 # A split holds at most 3840 tokens (120 tiles of 32 in its LDS row table).
