@@ -177,6 +177,21 @@ def test_topk_rows_within_one_chunk(n_distinct, k):
     assert torch.equal(got, want)
 
 
+@pytest.mark.parametrize("n_distinct", [None, 1, 3])
+@pytest.mark.parametrize("k", [1, 100, 511, 512])
+def test_topk_rows_of_512_blocks(n_distinct, k):
+    """S_max = 512 (the selection over the 16-token blocks of 8192 tokens, as
+    Quest makes it): ragged, empty, all-equal and k >= length rows."""
+    lens = [0, 1, 99, 100, 300, 511, 512]
+    say(f"[dsa] topk 512 lens={lens} k={k} n_distinct={n_distinct}")
+    s = wl.make_scores(B=len(lens), seq_lens=lens, n_distinct=n_distinct, seed=k + 13)
+    assert s.shape[1] == 512
+    sl = torch.tensor(lens, dtype=torch.int32)
+    got = api.dsa_topk(dev(s), dev(sl), k).cpu()
+    want = oracle.topk(s, sl, k)
+    assert torch.equal(got, want)
+
+
 def test_topk_ignores_workspace_contents():
     """The workspace holds no state between calls: garbage in it changes nothing."""
     lens = [9000, 20000, 5]
