@@ -97,7 +97,7 @@ def test_mla_paged_128_heads(P, splits):
     kernel, whose paged tiles must match its contiguous ones bit for bit;
     pages of 4 rows, and 2000 tokens in one split of 8-row pages (250 pages),
     take the 64-row kernel."""
-    x = wl.make_mla(B=4, H=128, seq_lens=[1, 33, 517, 2000], seed=46, name=f"mla_paged_p{P}")
+    x = wl.make_mla(B=5, H=128, seq_lens=[1, 33, 517, 2000, 0], seed=46, name=f"mla_paged_p{P}")
     pt, cache = _paged(x, P, seed=P)
     check(x, splits, page_table=pt, latent=cache)
     # explicit splits: the 32-row kernel takes the call when a split spans at
