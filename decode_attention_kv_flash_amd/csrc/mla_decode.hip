@@ -684,34 +684,37 @@ __global__ __launch_bounds__(64 * NW, 1) void mla_split_kernel(const MlaArgs a) 
 }
 
 // ---------------------------------------------------------------------------
-// The contiguous-cache kernel (dense MLA over [B, S_max, 576], 128 heads per
-// workgroup): tiles of 32 rows and 32x32x16 MFMAs throughout.  A 32x32x16
-// MFMA keeps the matrix core busy for 32 cycles, in which the wave can issue
-// about four other instructions; with 16x16x32 scores there is half that
-// room per instruction.  So here every k-step of the scores is one MFMA for
-// the wave's 32 heads, and the softmax, the operand reads and the copies fit
+// The 32-row kernel (128 heads per workgroup; rows from a contiguous cache
+// [B, S_max, 576], a sparse list, or a paged cache with pages of at least 8
+// rows): tiles of 32 rows and 32x32x16 MFMAs throughout.  A 32x32x16 MFMA
+// keeps the matrix core busy for 32 cycles, in which the wave can issue
+// a few other instructions; with 16x16x32 scores there is half that room per
+// instruction.  So here every k-step of the scores is one MFMA for the
+// wave's 32 heads, and the softmax, the operand reads and the copies fit
 // between the MFMAs.
 //
-// Per tile t the stream is: S(t + 1) interleaved with the first P.V MFMAs of
-// tile t, then the rest of P.V(t) interleaved with the softmax of tile t + 1
-// (its scores are complete by then), which sends P(t + 1) to the other waves
-// through LDS.  The S^T accumulator layout of the 32x32x16 MFMA (lane: head
-// lane % 32, tokens 8 (v / 4) + 4 (lane / 32) + v % 4) is the A layout P.V
-// needs for each 16-token k-step, with the token order permuted the same way
-// on the value's side, so P needs no shuffle.
+// Per tile t the stream is: the last P.V MFMAs of tile t - 1 (operands kept
+// in registers across the barrier) while the first score operands are read,
+// S(t + 1) interleaved with the first P.V MFMAs of tile t, then the rest of
+// P.V(t) interleaved with the softmax of tile t + 1 (its scores are complete
+// by then), which sends P(t + 1) to the other waves through LDS.  The S^T
+// accumulator layout of the 32x32x16 MFMA (lane: head lane % 32, tokens
+// 8 (v / 4) + 4 (lane / 32) + v % 4) is the A layout P.V needs for each
+// 16-token k-step, with the token order permuted the same way on the value's
+// side, so P needs no shuffle.
 //
 // LDS: four 36 KB tile buffers (tiles t (P.V), t + 1 (scores), t + 2 and
-// t + 3 in flight) and two 8 KB buffers of P: 160 KB, all of it.  The
-// restart vote therefore rides on P itself: probabilities are never negative,
-// so a wave that sees a maximum jump sets the sign bit of the first value of
-// its P fragment (head group w, lane 0); every wave reads that value back
-// with the fragment, finishes the pass over the split's tiles and runs it
-// again with the raised references.
+// t + 3 in flight) and two 8 KB buffers of P: 160 KB, all of it.  A wave's
+// vote (a score far above its head's reference, or a head without one)
+// therefore rides on P itself: probabilities are never negative, so the wave
+// sets the sign bit of lane 0's first value in its k-step-1 fragment, and
+// every wave reads that value back with the fragments.  A pass that saw a
+// vote is followed by a pass of scores alone (every head's maximum over the
+// split) and a second attention pass with those maxima as references.
 //
-// Within an iteration the first LDS reads after the barrier are the first
-// score operands (the P and value fragments follow), and the splits of one
-// (sequence, head block) are placed on one XCD so that its L2 serves their
-// shared query rows (the grid has the sequence index fastest).
+// The splits of one (sequence, head block) are placed on one XCD so that its
+// L2 serves their shared query rows (the grid has the sequence index
+// fastest).
 constexpr int kT2 = 32;                       // tokens per tile
 constexpr int kT2Bytes = kT2 * kRowBytes;     // 36864
 constexpr int kT2Buffers = 4;
