@@ -1132,7 +1132,8 @@ __global__ __launch_bounds__(256, 1) void mla_tile32_kernel(const MlaArgs a) {
     __builtin_amdgcn_sched_barrier(0);
 
     // phase 1: the 36 score MFMAs, with P.V MFMAs 0 .. kP1 - 1 (at k = 3, 7,
-    // 11, 15) and the copies (at k = 1, 5, .., 33)
+    // 11, 15) and the copies of tile t + 3 early, one after each of k = 1 .. 9
+    // (their lead over the barrier that waits for them is then longest)
 #pragma unroll
     for (int k = 0; k < kKS; ++k) {
       if (k == 0) asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(ar[0]), "v"(qf[0]));
@@ -1144,7 +1145,7 @@ __global__ __launch_bounds__(256, 1) void mla_tile32_kernel(const MlaArgs a) {
         if ((u & 3) == 3 && u + 5 < 32) vload(u + 5);
       }
       if constexpr (kCopy > 0) {
-        if (k % 4 == 1) copy(t + 3, k / 4, kCopy == 1);
+        if (k >= 1 && k <= kT2Copies) copy(t + 3, k - 1, kCopy == 1);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
