@@ -110,6 +110,24 @@ def test_mla_paged_128_heads(P, splits):
         assert torch.equal(clse, plse)
 
 
+@pytest.mark.parametrize("H", [192, 256])
+def test_mla_several_head_blocks(H):
+    """More heads than one workgroup holds: 256 heads run as two 128-head
+    blocks on the 32-row kernel, 192 as three 64-head blocks on the 16-row
+    one; contiguous, paged and sparse."""
+    x = wl.make_mla(B=3, H=H, seq_lens=[700, 1, 2100], seed=47, name=f"mla_h{H}")
+    for splits in (0, 3):
+        check(x, splits)
+    pt, cache = _paged(x, 16, seed=47)
+    check(x, 0, page_table=pt, latent=cache)
+    idx = wl.random_topk_indices(B=3, seq_lens=x.seq_lens.tolist(), k=512, seed=48)
+    got, glse = api.sparse_mla_attn(dev(x.q), dev(x.latent), dev(idx), scale=x.scale)
+    torch.cuda.synchronize()
+    want, wlse = oracle.mla(x.q, x.latent, idx=idx, scale=x.scale)
+    assert_rows_close(got.float().cpu().reshape(-1, 512), want, TOL_BF16, f"{x.name} sparse")
+    assert_lse_close(glse.cpu().reshape(-1), wlse, 1e-5, f"{x.name} sparse")
+
+
 @pytest.fixture(scope="module")
 def cfg4():
     say("[mla] generating DeepSeek-V3-shaped MLA decode: B32 H128 576-wide latent 16384 tokens")
