@@ -820,8 +820,6 @@ __global__ __launch_bounds__(256, 1) void mla_tile32_kernel(const MlaArgs a) {
   // split's first valid row instead (finite data whose P is 0), so every copy
   // instruction is issued whole and the barriers' counts of copies in flight
   // stay exact.
-  const int f_end = f_begin + n_tok;
-  (void)f_end;
   auto valid_row = [&](int id) -> bool { return id >= 0 && id < a.S_max; };
   // (the list entries were requested before the query rows, so waiting for
   // them here leaves the query rows in flight)
