@@ -192,6 +192,34 @@ def test_topk_rows_of_512_blocks(n_distinct, k):
     assert torch.equal(got, want)
 
 
+def _ordered_scores(order, lens, seed):
+    if order == "crowded":
+        return wl.make_scores(B=len(lens), seq_lens=lens, n_distinct=3, seed=seed)
+    if order == "many_ties":
+        return wl.make_scores(B=len(lens), seq_lens=lens, n_distinct=20000, seed=seed)
+    s = wl.make_scores(B=len(lens), seq_lens=lens, seed=seed)
+    if order in ("ascending", "descending"):
+        for b, L in enumerate(lens):
+            s[b, :L] = torch.sort(s[b, :L], descending=order == "descending").values
+    return s
+
+
+@pytest.mark.parametrize("order", ["random", "many_ties", "ascending", "descending", "crowded"])
+@pytest.mark.parametrize("k", [1, 2048, 8192, 8193])
+def test_topk_sorted_and_crowded_rows(order, k):
+    """Rows of up to 65536 tokens (32 chunks) in random order with or without
+    many ties, sorted either way (the taken keys sit in a few chunks, at the
+    start or the end of the row), and with three distinct values; lengths on
+    and off chunk boundaries, one more than k, equal to k, and empty."""
+    lens = [65536, 65535, 40000, 20481, 16385, 16384, 9000, k + 1, k, 0]
+    say(f"[dsa] topk sorted/crowded rows order={order} k={k}")
+    s = _ordered_scores(order, lens, seed=k + 17)
+    assert s.shape[1] == 65536
+    sl = torch.tensor(lens, dtype=torch.int32)
+    got = api.dsa_topk(dev(s), dev(sl), k).cpu()
+    assert torch.equal(got, oracle.topk(s, sl, k))
+
+
 def test_topk_ignores_workspace_contents():
     """The workspace holds no state between calls: garbage in it changes nothing."""
     lens = [9000, 20000, 5]
