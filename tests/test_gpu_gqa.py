@@ -141,6 +141,19 @@ def test_gqa_page_sizes(page_size):
     check_full(x)
 
 
+@pytest.mark.parametrize("page_size", [2, 8, 128, 256, 1024])
+@pytest.mark.parametrize("D", [64, 128])
+def test_window_and_sinks_on_small_and_large_pages(page_size, D):
+    """Pages of 2 and 8 tokens (several per 16-token step) and of 128 to 1024
+    (a window spanning one to eight pages, sinks and window in one page),
+    ragged lengths, 4 query heads per KV head, automatic and 3 splits."""
+    lens = [1, 300, 2049, 5000]
+    x = wl.make_gqa(B=4, Hq=16, Hkv=4, D=D, seq_lens=lens, page_size=page_size, window=1000, n_sink=4,
+                    sink_key_scale=4.0, seed=28 + page_size, name=f"swa_pages{page_size}_d{D}")
+    check_full(x, 0)
+    check_full(x, 3)
+
+
 @pytest.mark.parametrize("window,n_sink,lens", [
     (64, 4, [1, 4, 60, 64, 65, 68, 69, 1000]),   # window >= L, sinks inside / overlapping / apart
     (16, 0, [15, 16, 17, 500]),
