@@ -59,3 +59,45 @@ def test_mla_on_side_stream():
     for out, lse in outs:
         assert_rows_close(out.float().cpu().reshape(-1, 512), want, TOL_BF16, m.name)
         assert_lse_close(lse.cpu(), wlse, 1e-5, m.name)
+
+
+def test_calls_from_two_host_threads():
+    """Two host threads, each with its own stream, call the library at once
+    (the C calls release the GIL): every result equals the single-threaded one."""
+    import threading
+    x = wl.make_gqa(B=4, Hq=32, Hkv=8, D=128, seq_lens=[3000, 17, 4096, 1000], dtype=torch.bfloat16,
+                    seed=95, name="gqa_threads")
+    m = wl.make_mla(B=2, H=128, seq_lens=[2500, 700], seed=96, name="mla_threads")
+    say("[streams] two host threads, GQA and MLA")
+    q, kc, vc, sl, pt = x.q.cuda(), x.k_cache.cuda(), x.v_cache.cuda(), x.seq_lens.cuda(), x.page_table.cuda()
+    mq, lat, msl = m.q.cuda(), m.latent.cuda(), m.seq_lens.cuda()
+    ref_g, _ = api.decode_attn_gqa(q, kc, vc, sl, pt, scale=x.scale)
+    ref_m, _ = api.decode_attn_mla(mq, lat, msl, scale=m.scale)
+    torch.cuda.synchronize()
+    results, errors = {}, []
+
+    def worker(tid):
+        try:
+            s = torch.cuda.Stream()
+            outs = []
+            with torch.cuda.stream(s):
+                for _ in range(20):
+                    if tid == 0:
+                        outs.append(api.decode_attn_gqa(q, kc, vc, sl, pt, scale=x.scale, stream=s)[0])
+                    else:
+                        outs.append(api.decode_attn_mla(mq, lat, msl, scale=m.scale, stream=s)[0])
+            s.synchronize()
+            results[tid] = outs
+        except Exception as e:  # reported below
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    assert all(torch.equal(o, ref_g) for o in results[0])
+    assert all(torch.equal(o, ref_m) for o in results[1])
+    want, _ = oracle.gqa(x.q, x.k, x.v, x.seq_lens, scale=x.scale)
+    assert_rows_close(ref_g.float().cpu().reshape(-1, x.D), want, TOL_BF16, x.name)
