@@ -251,6 +251,22 @@ def test_config2_split_invariance(cfg2):
     assert oracle.rel_err_rows(a, b) <= 2 * TOL_BF16
 
 
+@pytest.mark.parametrize("window,n_sink", [(0, 0), (8192, 4)])
+def test_gqa_long_context_sampled(window, n_sink):
+    """Sequences of 131072 and 70001 tokens (Llama-3-8B heads, 16-token
+    pages in a random order): many splits per (sequence, KV head); full
+    attention, and an 8192-token window with 4 sinks."""
+    x = wl.make_gqa(B=2, Hq=32, Hkv=8, D=128, seq_lens=[131072, 70001], window=window, n_sink=n_sink,
+                    sink_key_scale=4.0 if n_sink else 1.0, seed=29, name=f"gqa_long_w{window}")
+    say(f"[gqa] {x.name} lens={x.seq_lens.tolist()} window={window} sinks={n_sink}")
+    got, glse = run_gpu(x)
+    rows = rows_sample(x.B * x.Hq, 24, seed=6)
+    want, wlse = oracle.gqa(x.q, x.k, x.v, x.seq_lens, window=window, n_sink=n_sink, scale=x.scale,
+                            rows=rows)
+    assert_rows_close(got[rows], want, TOL_BF16, x.name)
+    assert_lse_close(glse[rows], wlse, 1e-5, x.name)
+
+
 @pytest.fixture(scope="module")
 def cfg3():
     say("[swa] generating window 4096 + 4 sinks: B32 32/8 heads D128 lens U[4096,32768] paged16")

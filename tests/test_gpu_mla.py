@@ -140,6 +140,15 @@ def test_config4_full_size_sampled(cfg4):
     check(x, 0, rows=rows)
 
 
+@pytest.mark.parametrize("splits", [0, 35])
+def test_mla_long_context_sampled(splits):
+    """Sequences of 131072 and 100000 tokens: the automatic plan (many splits
+    per sequence for two sequences), and the fewest splits the 3840-token
+    split capacity allows (35), on sampled rows."""
+    x = wl.make_mla(B=2, H=128, seq_lens=[131072, 100000], seed=48, name="mla_long")
+    check(x, splits, rows=rows_sample(x.B * x.H, 16, seed=5))
+
+
 def test_mla_score_jumps_restart_the_split():
     """Scores far above the first ones of a split (more than 2^64 apart in
     exp2 units): rows whose latent is a multiple of one head's query."""
