@@ -114,20 +114,26 @@ int64_t gqa_slots(bool bf16, int D, int G, bool paged, int page_size) {
   return (int64_t)per * cus;
 }
 
-// MLA workgroups (hpw = 128 or 64 heads each, 127 KB of LDS) run one per CU:
-// aim for one full wave of 256 workgroups with splits of at least 128
-// tokens; a split holds at most kMlaMaxSplitTokens tokens, which sets a
-// floor on the count (a request below it is raised).  0 when the count would
-// exceed kMlaMaxSplits.
-int plan_mla_splits(int32_t B, int32_t H, int hpw, int64_t max_tokens, int32_t req) {
+// MLA workgroups (hpw = 128 or 64 heads each, up to 160 KB of LDS) run one
+// per CU: aim for at most one round of them (the count rounded down: 258
+// workgroups on 256 CUs, 6 x 128 heads x 16384 tokens, took 73.5 us per
+// call against 52.1 us for 222), with splits of at least min_tokens tokens.
+// Dense calls take 320: below that each workgroup's 256 KB of partials and
+// their combine cost more than the extra workgroups buy (128 heads x 16384
+// tokens, 1 / 2 / 4 sequences: 36.2 / 39.2 / 43.8 us per call against
+// 40.3 / 43.5 / 48.6 us with 128-token splits).  A split holds at most
+// kMlaMaxSplitTokens tokens, which sets a floor on the count (a request
+// below it is raised).  0 when the count would exceed kMlaMaxSplits.
+constexpr int kMlaDenseMinSplitTokens = 320;
+int plan_mla_splits(int32_t B, int32_t H, int hpw, int64_t max_tokens, int32_t req, int min_tokens) {
   const int64_t floor_n = (max_tokens + dattn::kMlaMaxSplitTokens - 1) / dattn::kMlaMaxSplitTokens;
   int64_t n;
   if (req > 0) {
     n = req;
   } else {
     const int64_t units = (int64_t)B * (H / hpw);
-    const int64_t want = (256 + units - 1) / units;
-    const int64_t cap = (max_tokens + 127) / 128;
+    const int64_t want = std::max<int64_t>(1, dattn::device_cu_count() / units);
+    const int64_t cap = (max_tokens + min_tokens - 1) / min_tokens;
     n = want < cap ? want : cap;
   }
   if (n < floor_n) n = floor_n;
@@ -154,17 +160,18 @@ MlaPlan plan_mla(int32_t B, int32_t H, int64_t max_tokens, int32_t req, bool spa
   if (sparse && p.heads_per_wg == 128 && req == 0) {
     const int64_t units = (int64_t)B * (H / 128);
     const int64_t floor_n = (max_tokens + dattn::kMlaSparseTile32Tokens - 1) / dattn::kMlaSparseTile32Tokens;
-    int64_t n = (256 + units - 1) / units;
+    int64_t n = std::max<int64_t>(1, dattn::device_cu_count() / units);
     const int64_t cap = (max_tokens + 127) / 128;
     if (n > cap) n = cap;
     if (n < floor_n) n = floor_n;
     if (n < 1) n = 1;
     if (n <= kMlaMaxSplits) return MlaPlan{(int)n, 128};
   }
-  p.splits = plan_mla_splits(B, H, p.heads_per_wg, max_tokens, req);
+  const int min_tokens = sparse ? 128 : kMlaDenseMinSplitTokens;
+  p.splits = plan_mla_splits(B, H, p.heads_per_wg, max_tokens, req, min_tokens);
   if (sparse && p.heads_per_wg == 128 && p.splits > 0 &&
       (int64_t)B * (H / 128) * p.splits < dattn::device_cu_count()) {
-    const int s64 = plan_mla_splits(B, H, 64, max_tokens, req);
+    const int s64 = plan_mla_splits(B, H, 64, max_tokens, req, min_tokens);
     if (s64 > 0) p = MlaPlan{s64, 64};
   }
   return p;
