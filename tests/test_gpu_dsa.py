@@ -137,6 +137,15 @@ def test_indexer_hands_the_select_its_first_level(fp8):
         assert torch.equal(sc[b, :n].double(), want[b, :n].double())
 
 
+def test_indexer_six_rows_of_65536():
+    """6 rows: 42 token ranges of 1568 tokens per row (one round of 252
+    workgroups; the ranges are not the select's chunks, so the select counts
+    its own first level), ragged lengths; scores and selection bit-exact."""
+    x = wl.make_dsa(B=6, seq_lens=[65536, 60000, 65536, 1000, 65536, 33333], Hi=64, topk=2048, H=64, seed=64,
+                    name="dsa_six_rows")
+    check_indexer(x, 2048)
+
+
 @pytest.mark.parametrize("n_distinct", [None, 3, 50])
 @pytest.mark.parametrize("k", [1, 100, 2048])
 def test_topk_alone(n_distinct, k):
