@@ -184,6 +184,53 @@ size_t mla_workspace(int64_t rows, int splits) {
          2 * align256((size_t)rows * splits * sizeof(float));
 }
 
+// Balanced splits for a dense call whose split count the library plans
+// (MlaArgs::flat_target): 128-head workgroups on the 32-row kernel, at most
+// kMlaFlatMaxB sequences, pages of at least 32 rows (items of up to 3840
+// tokens then span at most 122 pages).  Items aim at one per CU and head
+// block, of at least kMlaDenseMinSplitTokens tokens.  With one sequence
+// several times longer than the rest, equal split counts per sequence left
+// most CUs idle while its splits ran.
+struct MlaFlat {
+  int target = 0, slots = 0;
+};
+MlaFlat plan_mla_flat(int32_t B, int32_t H, int64_t cap, int32_t req, int32_t page_size, bool paged) {
+  MlaFlat f;
+  if (req != 0 || B > dattn::kMlaFlatMaxB || H % 128 != 0) return f;
+  if (paged && (page_size < 32 || !pow2(page_size))) return f;
+  const int64_t target = std::max<int64_t>(1, dattn::device_cu_count() / (H / 128));
+  const int64_t by_cap = (B * cap + dattn::kMlaMaxSplitTokens - 1) / dattn::kMlaMaxSplitTokens;
+  const int64_t slots = (std::max(target, by_cap) + B + 7) / 8 * 8;
+  if (slots * H > (int64_t(1) << 31) / 512) return f;
+  f.target = (int)target;
+  f.slots = (int)slots;
+  return f;
+}
+
+// Items per sequence of a balanced plan when every sequence holds `cap`
+// tokens: the same chunk search as the kernel's, on the host.  The combine
+// loads those rows first (the split grid's layout) and keeps them when the
+// item table agrees.
+int mla_flat_full_items(int32_t B, int64_t cap, int target, int min_tok, int max_tok) {
+  constexpr int kTile = 32;
+  const int64_t tot = (int64_t)B * cap;
+  int chunk = (int)std::max<int64_t>((tot + target - 1) / target, min_tok);
+  chunk = std::min((chunk + kTile - 1) / kTile * kTile, max_tok);
+  auto per_of = [&](int c) { return (int)((cap + c - 1) / c); };
+  int items = B * per_of(chunk);
+  for (int it = 0; it < 8 && items > target && chunk < max_tok; ++it) {
+    const int grow = std::max(kTile, (int)((int64_t)chunk * (items - target) / target));
+    chunk = std::min((chunk + grow + kTile - 1) / kTile * kTile, max_tok);
+    items = B * per_of(chunk);
+  }
+  return per_of(chunk);
+}
+
+// [partials of slots * H rows | item table B x 2]
+size_t mla_flat_workspace(const MlaFlat& f, int32_t B, int32_t H) {
+  return mla_workspace((int64_t)f.slots * H, 1) + align256((size_t)B * 2 * sizeof(int32_t));
+}
+
 // Upper bound on the tokens one sequence attends: the cache capacity
 // page_size * max_pages (contiguous: max_pages = 1), cut by window + sinks.
 int64_t gqa_max_tokens(int32_t page_size, int32_t max_pages, int32_t window, int32_t n_sink) {
@@ -640,23 +687,35 @@ size_t decode_attn_mla_workspace(int32_t B, int32_t H, int32_t d_latent, int32_t
                                  int32_t num_splits) {
   if (B < 1 || H < 64 || H % 64 != 0 || d_latent < 1 || S_max < 1 || num_splits < 0) return 0;
   const int splits = plan_mla(B, H, S_max, num_splits, false).splits;
-  return splits > 0 ? mla_workspace((int64_t)B * H, splits) : 0;
+  if (splits < 1) return 0;
+  // enough for either plan: a paged call with small pages keeps the split grid
+  const size_t split_bytes = mla_workspace((int64_t)B * H, splits);
+  const MlaFlat f = plan_mla_flat(B, H, S_max, num_splits, 32, false);
+  return f.target > 0 ? std::max(split_bytes, mla_flat_workspace(f, B, H)) : split_bytes;
 }
 
 // The split kernel always writes unnormalised partials; the combine divides
 // (also for one split) and writes bf16 out and the natural-log lse.
 static int run_mla(dattn::MlaArgs& a, int splits, float* lse, uint16_t* out, void* workspace,
                    hipStream_t s, const char* name) {
-  const size_t rs = (size_t)a.B * a.H * splits;
-  a.num_splits = splits;
+  const bool flat = a.flat_target > 0;
+  const size_t rs = flat ? (size_t)a.flat_slots * a.H : (size_t)a.B * a.H * splits;
+  a.num_splits = flat ? 1 : splits;
   a.out = out;
   a.lse = lse;
   a.part_o = (float*)workspace;
   a.part_lse = (float*)((char*)workspace + align256(rs * 512 * sizeof(float)));
   a.part_l = (float*)((char*)a.part_lse + align256(rs * sizeof(float)));
+  if (flat) a.flat_table = (int32_t*)((char*)a.part_l + align256(rs * sizeof(float)));
   int rc = launch(name, s, [&] { return dattn::launch_mla(a, s); });
   if (rc) return rc;
   dattn::CombineArgs c{a.part_o, a.part_lse, a.part_l, out, lse, a.B * a.H, splits, 512, 1};
+  if (flat) {
+    c.items = a.flat_table;
+    c.heads = a.H;
+    c.splits = mla_flat_full_items(a.B, a.page_table ? (int64_t)a.page_size * a.max_pages : a.S_max,
+                                   a.flat_target, a.flat_min, a.flat_max);
+  }
   return launch("lse_combine", s, [&] { return dattn::launch_combine(c, s); });
 }
 
@@ -682,8 +741,9 @@ int decode_attn_mla(const void* q_absorbed, const void* latent_cache, const int3
   const int splits = plan.splits;
   if (splits < 1) return fail(DATTN_EUNSUPPORTED, "decode_attn_mla: %lld tokens need more than %d splits",
                               (long long)max_tokens, kMlaMaxSplits);
-  if ((rc = check_workspace(workspace, workspace_bytes, mla_workspace((int64_t)B * H, splits))))
-    return rc;
+  const MlaFlat flat = plan_mla_flat(B, H, max_tokens, num_splits, page_size, page_table != nullptr);
+  const size_t need = flat.target > 0 ? mla_flat_workspace(flat, B, H) : mla_workspace((int64_t)B * H, splits);
+  if ((rc = check_workspace(workspace, workspace_bytes, need))) return rc;
   if (debug_on()) {
     const void* caches[] = {latent_cache};
     const int64_t pb = (int64_t)page_size * (d_latent + d_rope) * 2;
@@ -705,6 +765,12 @@ int decode_attn_mla(const void* q_absorbed, const void* latent_cache, const int3
   a.max_pages = page_table ? max_pages : 1;
   const float sc = scale > 0.f ? scale : 1.0f / std::sqrt(192.0f);
   a.scale_log2 = sc * 1.4426950408889634f;
+  if (flat.target > 0) {
+    a.flat_target = flat.target;
+    a.flat_slots = flat.slots;
+    a.flat_min = kMlaDenseMinSplitTokens;
+    a.flat_max = dattn::kMlaMaxSplitTokens;
+  }
   return run_mla(a, splits, lse, (uint16_t*)out, workspace, (hipStream_t)stream, "mla_split");
 }
 

@@ -830,15 +830,20 @@ __global__ __launch_bounds__(kCombineThreads) void lse_combine_kernel(const Comb
   const size_t e = (size_t)blockIdx.x * kCombineThreads + threadIdx.x;
   if (e >= (size_t)a.rows * D4) return;
   const int row = (int)(e / D4), d = 4 * (int)(e % D4);
-  const int S = a.splits;
-  const float* pl = a.part_lse + (size_t)row * S;
-  const float* ps = a.part_l ? a.part_l + (size_t)row * S : nullptr;
-  const float4* po = (const float4*)(a.part_o + (size_t)row * S * a.D + d);
-  float M = NEG_INF, wsum = 0.f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int j0 = 0; j0 < S; j0 += kCombineChunk) {
-    float x[kCombineChunk], l[kCombineChunk];
-    float4 v[kCombineChunk];
+  // this row's partials: entries base .. base + S - 1
+  int S = a.splits;
+  size_t base = (size_t)row * S;
+  const float* pl;
+  const float* ps;
+  const float4* po;
+  auto at = [&](size_t bs) {
+    pl = a.part_lse + bs;
+    ps = a.part_l ? a.part_l + bs : nullptr;
+    po = (const float4*)(a.part_o + bs * a.D + d);
+  };
+  float x[kCombineChunk], l[kCombineChunk];
+  float4 v[kCombineChunk];
+  auto load = [&](int j0) {
 #pragma unroll
     for (int u = 0; u < kCombineChunk; ++u) {
       const bool in = j0 + u < S;
@@ -846,6 +851,28 @@ __global__ __launch_bounds__(kCombineThreads) void lse_combine_kernel(const Comb
       v[u] = in ? po[(size_t)(j0 + u) * D4] : make_float4(0.f, 0.f, 0.f, 0.f);
       l[u] = ps && in ? ps[j0 + u] : 1.f;
     }
+  };
+  at(base);
+  load(0);
+  if (a.items) {
+    // sequence b's items own rows first * heads .. + count * heads,
+    // head-major.  The first loads above went to row * splits: where a plan
+    // of full-length sequences (splits items each) puts them, the same
+    // layout as the split grid; they are redone elsewhere.
+    const int b = row / a.heads, h = row - b * a.heads;
+    const int n = a.items[2 * b + 1];
+    const size_t tb = (size_t)a.items[2 * b] * a.heads + (size_t)h * n;
+    if (n != S || tb != base) {
+      S = n;
+      base = tb;
+      at(base);
+      load(0);
+    }
+  }
+  float M = NEG_INF, wsum = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j0 = 0; j0 < S; j0 += kCombineChunk) {
+    if (j0 > 0) load(j0);
     float Mc = M;
 #pragma unroll
     for (int u = 0; u < kCombineChunk; ++u) Mc = fmaxf(Mc, x[u]);
@@ -918,7 +945,7 @@ int gqa_blocks_per_cu(bool bf16, int D, int G, bool paged, int page_size) {
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
-  if (a.splits > kMaxCombineSplits) return hipErrorInvalidValue;
+  if (!a.items && a.splits > kMaxCombineSplits) return hipErrorInvalidValue;
   if (a.D % 4 != 0) return hipErrorInvalidValue;
   const size_t total = (size_t)a.rows * (a.D / 4);
   const unsigned blocks = (unsigned)((total + kCombineThreads - 1) / kCombineThreads);

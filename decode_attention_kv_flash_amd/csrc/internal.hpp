@@ -110,6 +110,13 @@ struct CombineArgs {
   // nullptr, or a sink logit per head (natural log) for row r: sink[r % sink_heads]
   const float* sink = nullptr;
   int32_t sink_heads = 1;
+  // nullptr, or the item table of a balanced MLA call ([B][2]: first item,
+  // item count of sequence b): row r = b * heads + h then merges the partials
+  // of rows first * heads + h * count + j, j < count.  `splits` is then the
+  // item count per sequence a plan of full-length sequences makes (rows
+  // r * splits + j: loaded before the table is read, and kept when it agrees).
+  const int32_t* items = nullptr;
+  int32_t heads = 1;
 };
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
@@ -129,7 +136,19 @@ struct MlaArgs {
   int32_t B, H, S_max, page_size, log2_page, max_pages, num_splits;
   int32_t heads_per_wg;     // 128 (four waves) or 64 (two waves) query heads per workgroup
   float scale_log2;
+  // Balanced splits (flat_target > 0; dense 128-head calls on the 32-row
+  // kernel whose split count the library plans): every sequence is cut into
+  // items of `chunk` tokens, chunk = the total tokens / flat_target rounded up
+  // to whole 32-row tiles and held within [flat_min, flat_max], so that long
+  // and short sequences make items of about equal work.  Sequence b's items
+  // (first f, count n) write rows f * H + h * n + j; flat_table [B][2] gets
+  // each sequence's f and n.  The grid holds flat_slots items (a multiple of 8, at least
+  // the items any lengths within the cache can make).
+  int32_t flat_target = 0, flat_min = 0, flat_max = 0, flat_slots = 0;
+  int32_t* flat_table = nullptr;
 };
+// Sequences a balanced MLA call plans for (8 lengths per lane of one wave).
+constexpr int kMlaFlatMaxB = 512;
 
 // Tokens one MLA split may hold (its cache rows are tabled in LDS); the
 // planner picks at least ceil(tokens / kMlaMaxSplitTokens) splits.

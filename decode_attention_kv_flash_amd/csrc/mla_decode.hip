@@ -733,6 +733,111 @@ __device__ __forceinline__ int swz32(int r) {
   return ((m & 1) << 2) | (m >> 1);
 }
 
+// Balanced splits: this workgroup's item, its sequence b and token range
+// [f_begin, f_begin + n_tok) of the sequence's N tokens, and where its
+// partials go (rows pbase + h * pstride: a sequence's items own a block of
+// n_b * H rows, head-major, so the combine reads each head's partials in one
+// run).  The chunk is the smallest multiple of 32 tokens, within [flat_min,
+// flat_max], that cuts the sequences into at most flat_target items (one
+// round of workgroups; item counts round up per sequence, so T / target
+// alone can overshoot by up to B).  Grid slots reach the 8 XCDs round-robin;
+// with n items, slot k holds item (k % 8) * ceil(n / 8) + k / 8, so each XCD
+// runs ceil(n / 8) consecutive items, mostly of a few sequences whose query
+// rows its L2 then serves.  Every wave plans alike from all B lengths (8 per
+// lane); wave 0 of slot 0 writes the item table.
+
+// the chunk for total tokens `tot`, given the item count of a chunk
+template <typename F>
+__device__ __forceinline__ int flat_chunk(const MlaArgs& a, int64_t tot, const F& items_of, int& items) {
+  int chunk = (int)max((tot + a.flat_target - 1) / a.flat_target, (int64_t)a.flat_min);
+  chunk = min((chunk + kT2 - 1) / kT2 * kT2, a.flat_max);
+  items = items_of(chunk);
+  for (int it = 0; it < 8 && items > a.flat_target && chunk < a.flat_max; ++it) {
+    // grow by the share of items over the target (at least a tile)
+    const int grow = max(kT2, (int)((int64_t)chunk * (items - a.flat_target) / a.flat_target));
+    chunk = min((chunk + grow + kT2 - 1) / kT2 * kT2, a.flat_max);
+    items = items_of(chunk);
+  }
+  return chunk;
+}
+
+// The sequence this slot's item belongs to if every sequence held `cap`
+// tokens (scalar; no loads), or -1: a guess to load query rows early.
+__device__ __forceinline__ int flat_guess(const MlaArgs& a, int cap) {
+  int items, per = 1;
+  (void)flat_chunk(a, (int64_t)a.B * cap, [&](int c) { per = (cap + c - 1) / c; return a.B * per; }, items);
+  const int k = blockIdx.x, run = (items + 7) >> 3;
+  const int item = (k & 7) * run + (k >> 3);
+  return (k >> 3) < run && item < items && per > 0 ? item / per : -1;
+}
+
+__device__ __forceinline__ void flat_lengths(const MlaArgs& a, int cap, int (&L)[8]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int bb = 64 * u + lane;
+    L[u] = bb < a.B ? min(max(a.seq_lens[bb], 0), cap) : 0;
+  }
+}
+
+__device__ __forceinline__ bool flat_place(const MlaArgs& a, const int (&L)[8], bool write_table, int& b, int& N,
+                                           int& f_begin, int& n_tok, size_t& pbase, size_t& pstride) {
+  const int lane = threadIdx.x & 63;
+  int tot = 0;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) tot += L[u];
+  tot = __builtin_amdgcn_readfirstlane(__ockl_wfred_add_i32(tot));
+  int n[8];
+  auto items_of = [&](int c) {
+    int s = 0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      n[u] = 64 * u < a.B ? (L[u] + c - 1) / c : 0;
+      s += n[u];
+    }
+    return __builtin_amdgcn_readfirstlane(__ockl_wfred_add_i32(s));
+  };
+  int items;
+  const int chunk = flat_chunk(a, tot, items_of, items);
+  const int k = blockIdx.x, run = (items + 7) >> 3;
+  const int item = (k & 7) * run + (k >> 3);
+  const bool live = (k >> 3) < run && item < items;
+  int running = 0, fb = -1, fj = 0, fl = 0, fo = 0, fn = 0;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    if (64 * u >= a.B) break;
+    int inc = n[u];
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(inc, d);
+      if (lane >= d) inc += y;
+    }
+    const int excl = running + inc - n[u];
+    if (write_table && 64 * u + lane < a.B) {
+      a.flat_table[2 * (64 * u + lane)] = excl;
+      a.flat_table[2 * (64 * u + lane) + 1] = n[u];
+    }
+    const uint64_t m = __ballot(live && item >= excl && item < excl + n[u]);
+    if (m) {
+      const int src = __ffsll((long long)m) - 1;
+      fb = 64 * u + src;
+      fo = __builtin_amdgcn_readlane(excl, src);
+      fn = __builtin_amdgcn_readlane(n[u], src);
+      fj = item - fo;
+      fl = __builtin_amdgcn_readlane(L[u], src);
+    }
+    running += __builtin_amdgcn_readlane(inc, 63);
+  }
+  if (fb < 0) return false;
+  b = fb;
+  N = fl;
+  f_begin = fj * chunk;
+  n_tok = min(chunk, N - f_begin);
+  pbase = (size_t)fo * a.H + fj;
+  pstride = (size_t)fn;
+  return true;
+}
+
 // Where a tile's rows come from: a contiguous cache, a sparse list, or a
 // paged cache with pages of at least 8 rows.
 enum : int { kSrcContig = 0, kSrcSparse = 1, kSrcPaged = 2 };
@@ -753,17 +858,41 @@ __global__ __launch_bounds__(256, 1) void mla_tile32_kernel(const MlaArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int half = lane >> 5, lj = lane & 31, li = lane & 15, g = lane >> 4;
-  // grid (B, splits, H / 128): workgroups reach the 8 XCDs round-robin by
-  // linear id, so with the sequence fastest the splits of one sequence share
-  // an XCD (B a multiple of 8), and its L2 serves their common query rows
-  const int b = blockIdx.x;
-  const int split = blockIdx.y;
   const int hw = blockIdx.z * 128;       // the workgroup's first head
   const int h0 = hw + wave * 32;         // this wave's score heads
   const int d0 = wave * 128;             // this wave's output dims
 
-  // the split: positions [f_begin, f_begin + n_tok) of the sequence (or list)
-  int N, f_begin, n_tok;
+  // the split: positions [f_begin, f_begin + n_tok) of the sequence (or
+  // list); its partials go to rows pbase + h * pstride.  Grid (B, splits,
+  // H / 128): workgroups reach the 8 XCDs round-robin by linear id, so with
+  // the sequence fastest the splits of one sequence share an XCD (B a
+  // multiple of 8), and its L2 serves their common query rows.  Balanced
+  // splits: grid (slots, 1, H / 128), placed by flat_place.
+  const bool flat = !SPARSE && a.flat_target > 0;
+  int b = blockIdx.x, split = blockIdx.y;
+  int N = 0, f_begin = 0, n_tok = 0;
+  size_t pbase = (size_t)b * a.H * a.num_splits + split, pstride = (size_t)a.num_splits;
+  // Q^T fragments (B of the scores): lane holds head h0 + lj, dims 16 k + 8 half + [0, 8)
+  bf16x8_t qf[kKS];
+  int bq = -1;  // the sequence whose query rows qf holds
+  auto load_q = [&](int bs) {
+    const uint16_t* qrow = a.q + ((size_t)bs * a.H + h0 + lj) * kDq + 8 * half;
+#pragma unroll
+    for (int k = 0; k < kKS; ++k) qf[k] = *(const bf16x8_t*)(qrow + 16 * k);
+    bq = bs;
+  };
+  if (flat) {
+    // the lengths first, then the query rows of the full-length guess while
+    // they are in flight (right for full-length batches; reloaded otherwise)
+    const int cap = PAGED ? a.page_size * a.max_pages : a.S_max;
+    int L8[8];
+    flat_lengths(a, cap, L8);
+    const int guess = flat_guess(a, cap);
+    if (guess >= 0) load_q(guess);
+    if (!flat_place(a, L8, blockIdx.x == 0 && blockIdx.z == 0 && wave == 0, b, N, f_begin, n_tok, pbase,
+                    pstride))
+      return;
+  }
   auto place_split = [&](int len) {
     N = SPARSE ? len : max(0, min(len, PAGED ? a.page_size * a.max_pages : a.S_max));
     const int per = ((N + a.num_splits - 1) / a.num_splits + kT2 - 1) / kT2 * kT2;
@@ -778,7 +907,7 @@ __global__ __launch_bounds__(256, 1) void mla_tile32_kernel(const MlaArgs a) {
   // the query rows, after the sequence length they depend on
   int pe[2] = {0, 0}, first_page = 0;
   if constexpr (PAGED) {
-    place_split(a.seq_lens[b]);
+    if (!flat) place_split(a.seq_lens[b]);
     first_page = f_begin >> a.log2_page;
     const int n_pages = n_tok > 0 ? ((f_begin + n_tok - 1) >> a.log2_page) - first_page + 1 : 0;
     const int32_t* row = a.page_table + (size_t)b * a.max_pages + first_page;
@@ -792,17 +921,13 @@ __global__ __launch_bounds__(256, 1) void mla_tile32_kernel(const MlaArgs a) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) lid[u] = 64 * u + lane < n_tok ? list[64 * u + lane] : -1;
   } else {
-    len_raw = a.seq_lens[b];
+    if (!flat) len_raw = a.seq_lens[b];
   }
-  // Q^T fragments (B of the scores): lane holds head h0 + lj, dims 16 k + 8 half + [0, 8)
-  bf16x8_t qf[kKS];
-  {
-    const uint16_t* qrow = a.q + ((size_t)b * a.H + h0 + lj) * kDq + 8 * half;
-#pragma unroll
-    for (int k = 0; k < kKS; ++k) qf[k] = *(const bf16x8_t*)(qrow + 16 * k);
-  }
+  if (bq != b) load_q(b);
   __builtin_amdgcn_sched_barrier(0);
-  if constexpr (SRC == kSrcContig) place_split(len_raw);
+  if constexpr (SRC == kSrcContig) {
+    if (!flat) place_split(len_raw);
+  }
   const int n_tiles = (n_tok + kT2 - 1) / kT2;
 
   const uint32_t tiles_base = lds_address(tiles);
@@ -1268,19 +1393,18 @@ __global__ __launch_bounds__(256, 1) void mla_tile32_kernel(const MlaArgs a) {
   settle(acc);
 
   // unnormalised partials: O (relative to m_run), m_run and l per head
-  const size_t roww = (size_t)b * a.H + hw;
 #pragma unroll
   for (int hg = 0; hg < 4; ++hg)
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
       for (int v = 0; v < 16; ++v)
-        a.part_o[((roww + 32 * hg + 8 * (v / 4) + 4 * half + (v % 4)) * a.num_splits + split) * kDc + d0 +
+        a.part_o[(pbase + (size_t)(hw + 32 * hg + 8 * (v / 4) + 4 * half + (v % 4)) * pstride) * kDc + d0 +
                  32 * nt + lj] = acc[hg * kNT + nt][v];
   const auto w = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
   const float l_tot = __uint_as_float(w[0]) + __uint_as_float(w[1]);
   if (half == 0) {
-    const size_t r = ((size_t)b * a.H + h0 + lj) * a.num_splits + split;
+    const size_t r = pbase + (size_t)(h0 + lj) * pstride;
     a.part_lse[r] = l_tot > 0.f ? m_run : NEG_INF;
     a.part_l[r] = l_tot;
   }
@@ -1321,6 +1445,7 @@ bool mla_paged_on_tile32(const MlaArgs& a) {
 }
 
 bool mla_uses_tile32(const MlaArgs& a) {
+  if (a.flat_target > 0) return true;  // the planner took the 32-row kernel's limits
   if (a.num_splits < 1) return false;
   if (!a.idx && !a.page_table && a.heads_per_wg == 128 && a.H % 128 == 0) return true;
   return mla_sparse_on_tile32(a) || mla_paged_on_tile32(a);
@@ -1328,7 +1453,7 @@ bool mla_uses_tile32(const MlaArgs& a) {
 
 hipError_t launch_mla(const MlaArgs& a, hipStream_t s) {
   if (mla_uses_tile32(a)) {
-    dim3 grid(a.B, a.num_splits, a.H / 128);
+    const dim3 grid = a.flat_target > 0 ? dim3(a.flat_slots, 1, a.H / 128) : dim3(a.B, a.num_splits, a.H / 128);
     if (a.idx) launch_kernel(mla_tile32_kernel<kSrcSparse>, grid, dim3(256), s, a);
     else if (a.page_table) launch_kernel(mla_tile32_kernel<kSrcPaged>, grid, dim3(256), s, a);
     else launch_kernel(mla_tile32_kernel<kSrcContig>, grid, dim3(256), s, a);

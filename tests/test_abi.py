@@ -115,16 +115,18 @@ def test_mla_and_sparse_validation():
 
 
 def test_mla_plan_stays_in_one_round_of_workgroups():
-    """The dense MLA split count, read back from the workspace size (rows x
-    splits x (512 + 2) fp32), on the 256-CU default the library assumes
-    without a device: at most one workgroup per CU for every batch size (a
-    count rounded up gave 258 workgroups at 6 sequences), splits of at least
-    320 tokens, and never more than the 3840-token split capacity allows."""
+    """The MLA split grid, read back from the workspace size (rows x splits x
+    (512 + 2) fp32) of 64-head calls, which always take it, on the 256-CU
+    default the library assumes without a device: at most one workgroup per
+    CU for every batch size (a count rounded up gave 258 workgroups at 6
+    sequences), splits of at least 320 tokens, and never more than the
+    3840-token split capacity allows.  128-head calls reserve room for
+    balanced items too: one per CU plus one per sequence."""
     L = api.lib()
     S = 16384
     for B in list(range(1, 65)) + [96, 128, 255, 256, 300]:
-        rows = B * 128
-        nb = L.decode_attn_mla_workspace(B, 128, 512, S, 0)
+        rows = B * 64
+        nb = L.decode_attn_mla_workspace(B, 64, 512, S, 0)
         assert nb % (rows * 2056) == 0
         splits = nb // (rows * 2056)
         assert splits >= (S + 3839) // 3840
@@ -134,7 +136,9 @@ def test_mla_plan_stays_in_one_round_of_workgroups():
     # 8 to 32 sequences of 16384 tokens keep 256 / B splits; 64 take the 5
     # that the split capacity needs
     for B, want in ((8, 32), (16, 16), (32, 8), (64, 5)):
-        assert L.decode_attn_mla_workspace(B, 128, 512, S, 0) == B * 128 * 2056 * want
+        assert L.decode_attn_mla_workspace(B, 64, 512, S, 0) == B * 64 * 2056 * want
+    for B in (1, 6, 32, 512):
+        assert L.decode_attn_mla_workspace(B, 128, 512, S, 0) >= (256 + B) * 128 * 2056
 
 
 def test_dsa_validation():

@@ -140,6 +140,40 @@ def test_config4_full_size_sampled(cfg4):
     check(x, 0, rows=rows)
 
 
+# --- balanced splits: the library's own plan for 128-head calls cuts every
+# sequence into items of about equal token counts (at most 3840 each)
+
+@pytest.mark.parametrize("P", [0, 32, 64, 256])
+def test_mla_balanced_items_on_skewed_lengths(P):
+    """One long sequence among short and empty ones (the long one takes many
+    items, the short ones one each, the empty one none), contiguous and
+    paged with 32-, 64- and 256-row pages; sampled rows of every sequence."""
+    lens = [40000, 1, 0, 5000, 33, 2047, 320, 321]
+    x = wl.make_mla(B=len(lens), H=128, seq_lens=lens, seed=49, name=f"mla_skew_p{P}")
+    rows = sorted(set(rows_sample(x.B * x.H, 40, seed=7) + [128 * b + 5 for b in range(x.B)]))
+    if P == 0:
+        check(x, 0, rows=rows)
+    else:
+        pt, cache = _paged(x, P, seed=P)
+        check(x, 0, rows=rows, page_table=pt, latent=cache)
+    got, lse = run_gpu(x)
+    assert torch.all(got[256:384] == 0) and torch.all(torch.isinf(lse[256:384]))  # the empty sequence
+
+
+def test_mla_balanced_items_all_empty_and_many_sequences():
+    """Every sequence empty (no item at all: the combine writes zeros and
+    -inf); 300 short sequences (one item each, more items than CUs); and 513
+    sequences, past the balanced plan's 512, on the split grid."""
+    x = wl.make_mla(B=4, H=128, seq_lens=[0, 0, 0, 0], seed=50, name="mla_all_empty")
+    got, lse = run_gpu(x)
+    assert torch.all(got == 0) and torch.all(torch.isinf(lse))
+    for B in (300, 513):
+        g = torch.Generator().manual_seed(B)
+        lens = torch.randint(0, 60, (B,), generator=g).tolist()
+        x = wl.make_mla(B=B, H=128, seq_lens=lens, seed=51, name=f"mla_{B}_short")
+        check(x, 0, rows=rows_sample(x.B * x.H, 48, seed=B))
+
+
 @pytest.mark.parametrize("splits", [0, 35])
 def test_mla_long_context_sampled(splits):
     """Sequences of 131072 and 100000 tokens: the automatic plan (many splits
