@@ -91,10 +91,10 @@ COUNTER_KERNELS = {
     "gqa_split": ("gqa", r"gqa_split_kernel", "gqa_decode.hip",
                   "GQA Llama-3-8B layer (B16, 32/8 heads, D128, 8192 tokens, paged 16, bf16): "
                   "K+V 536870912 bytes"),
-    "mla_split": ("mla", r"mla_tile32_kernel<0>", "mla_decode.hip",
+    "mla_split": ("mla", r"mla_tile32_kernel<0(, (true|false))?>", "mla_decode.hip",
                   "MLA DeepSeek-V3 shape (B32, H128, 576-wide latent, 16384 tokens, bf16): "
                   "latent 603979776 bytes, 146028888064 flops"),
-    "sparse_mla_split": ("dsa", r"mla_tile32_kernel<1>", "mla_decode.hip",
+    "sparse_mla_split": ("dsa", r"mla_tile32_kernel<1(, (true|false))?>", "mla_decode.hip",
                          "sparse MLA over top-2048 of 65536 (B8, H128, bf16): "
                          "selected latent rows 18874368 bytes, 4563402752 flops"),
     "indexer_bf16": ("dsa", r"indexer_kernel<\d+, false>", "indexer.hip",
@@ -248,10 +248,10 @@ TRACE_WORK = {
     "gqa": {r"gqa_split_kernel": (536870912, None)},
     "swa": {},
     "layouts": {r"gqa_split_kernel": (536870912, None)},
-    "mla": {r"mla_tile32_kernel<0>": (603979776, 146028888064)},
+    "mla": {r"mla_tile32_kernel<0(, (true|false))?>": (603979776, 146028888064)},
     "dsa": {r"indexer_kernel<\d+, false>": (134217728, None),
             r"indexer_kernel<\d+, true>": (67108864, None),
-            r"mla_tile32_kernel<1>": (18874368, 4563402752)},
+            r"mla_tile32_kernel<1(, (true|false))?>": (18874368, 4563402752)},
     "quest": {},
     "append": {},
 }

@@ -136,8 +136,8 @@ struct MlaArgs {
   int32_t B, H, S_max, page_size, log2_page, max_pages, num_splits;
   int32_t heads_per_wg;     // 128 (four waves) or 64 (two waves) query heads per workgroup
   float scale_log2;
-  // Balanced splits (flat_target > 0; dense 128-head calls on the 32-row
-  // kernel whose split count the library plans): every sequence is cut into
+  // Balanced splits (flat_target > 0; dense 128-head calls over a contiguous
+  // cache whose split count the library plans): every sequence is cut into
   // items of `chunk` tokens, chunk = the total tokens / flat_target rounded up
   // to whole 32-row tiles and held within [flat_min, flat_max], so that long
   // and short sequences make items of about equal work.  Sequence b's items

@@ -842,7 +842,9 @@ __device__ __forceinline__ bool flat_place(const MlaArgs& a, const int (&L)[8], 
 // paged cache with pages of at least 8 rows.
 enum : int { kSrcContig = 0, kSrcSparse = 1, kSrcPaged = 2 };
 
-template <int SRC>
+// FLAT: balanced items (flat_place) instead of the (B, splits) grid; a
+// template parameter, so that the split-grid instances keep their own code.
+template <int SRC, bool FLAT = false>
 __global__ __launch_bounds__(256, 1) void mla_tile32_kernel(const MlaArgs a) {
   constexpr bool SPARSE = SRC == kSrcSparse;
   constexpr bool PAGED = SRC == kSrcPaged;
@@ -868,7 +870,8 @@ __global__ __launch_bounds__(256, 1) void mla_tile32_kernel(const MlaArgs a) {
   // the sequence fastest the splits of one sequence share an XCD (B a
   // multiple of 8), and its L2 serves their common query rows.  Balanced
   // splits: grid (slots, 1, H / 128), placed by flat_place.
-  const bool flat = !SPARSE && a.flat_target > 0;
+  constexpr bool flat = FLAT;
+  static_assert(!FLAT || SRC == kSrcContig, "paged caches and sparse lists keep the split grid");
   int b = blockIdx.x, split = blockIdx.y;
   int N = 0, f_begin = 0, n_tok = 0;
   size_t pbase = (size_t)b * a.H * a.num_splits + split, pstride = (size_t)a.num_splits;
@@ -881,7 +884,7 @@ __global__ __launch_bounds__(256, 1) void mla_tile32_kernel(const MlaArgs a) {
     for (int k = 0; k < kKS; ++k) qf[k] = *(const bf16x8_t*)(qrow + 16 * k);
     bq = bs;
   };
-  if (flat) {
+  if constexpr (flat) {
     // the lengths first, then the query rows of the full-length guess while
     // they are in flight (right for full-length batches; reloaded otherwise)
     const int cap = PAGED ? a.page_size * a.max_pages : a.S_max;
@@ -1454,8 +1457,10 @@ bool mla_uses_tile32(const MlaArgs& a) {
 hipError_t launch_mla(const MlaArgs& a, hipStream_t s) {
   if (mla_uses_tile32(a)) {
     const dim3 grid = a.flat_target > 0 ? dim3(a.flat_slots, 1, a.H / 128) : dim3(a.B, a.num_splits, a.H / 128);
+    const bool flat = a.flat_target > 0;
     if (a.idx) launch_kernel(mla_tile32_kernel<kSrcSparse>, grid, dim3(256), s, a);
     else if (a.page_table) launch_kernel(mla_tile32_kernel<kSrcPaged>, grid, dim3(256), s, a);
+    else if (flat) launch_kernel(mla_tile32_kernel<kSrcContig, true>, grid, dim3(256), s, a);
     else launch_kernel(mla_tile32_kernel<kSrcContig>, grid, dim3(256), s, a);
     return hipGetLastError();
   }

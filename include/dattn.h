@@ -305,11 +305,11 @@ DATTN_EXPORT size_t decode_attn_quest_workspace(int32_t B, int32_t Hq, int32_t H
  *   num_splits   0 = automatic; a split holds at most 3840 tokens, so a
  *                smaller count is raised to ceil(S_max / 3840) (at most 256).
  *                Automatic with H a multiple of 128, B <= 512 and a
- *                contiguous cache or pages of at least 32 rows cuts every
- *                sequence into items of about equal tokens from the actual
- *                seq_lens (long sequences take more, empty ones none), so
- *                that ragged batches keep every CU busy; otherwise every
- *                sequence gets the same number of splits.
+ *                contiguous cache cuts every sequence into items of about
+ *                equal tokens from the actual seq_lens (long sequences take
+ *                more, empty ones none), so that ragged batches keep every
+ *                CU busy; otherwise (and for paged caches) every sequence
+ *                gets the same number of splits.
  *   workspace    decode_attn_mla_workspace bytes (never 0: the splits' partial
  *                results always go through it)
  * The cache must hold fewer than 2^31 rows (B * S_max contiguous, num_pages *

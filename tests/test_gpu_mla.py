@@ -145,9 +145,10 @@ def test_config4_full_size_sampled(cfg4):
 
 @pytest.mark.parametrize("P", [0, 32, 64, 256])
 def test_mla_balanced_items_on_skewed_lengths(P):
-    """One long sequence among short and empty ones (the long one takes many
-    items, the short ones one each, the empty one none), contiguous and
-    paged with 32-, 64- and 256-row pages; sampled rows of every sequence."""
+    """One long sequence among short and empty ones: contiguous, balanced
+    items (the long one takes many, the short ones one each, the empty one
+    none); paged with 32-, 64- and 256-row pages, equal splits per
+    sequence; sampled rows of every sequence."""
     lens = [40000, 1, 0, 5000, 33, 2047, 320, 321]
     x = wl.make_mla(B=len(lens), H=128, seq_lens=lens, seed=49, name=f"mla_skew_p{P}")
     rows = sorted(set(rows_sample(x.B * x.H, 40, seed=7) + [128 * b + 5 for b in range(x.B)]))
