@@ -175,6 +175,17 @@ def test_mla_balanced_items_all_empty_and_many_sequences():
         check(x, 0, rows=rows_sample(x.B * x.H, 48, seed=B))
 
 
+def test_mla_balanced_items_in_several_rounds():
+    """512 sequences (the balanced plan's limit) of up to 4000 tokens: items
+    are capped at 3840 tokens, so there are about four items per CU and the
+    grid runs several rounds; sampled rows against the oracle."""
+    g = torch.Generator().manual_seed(512)
+    lens = torch.randint(3000, 4001, (512,), generator=g).tolist()
+    lens[7], lens[300] = 3840, 3841  # one item exactly, and one token over
+    x = wl.make_mla(B=512, H=128, seq_lens=lens, seed=52, name="mla_512_rounds")
+    check(x, 0, rows=sorted(set(rows_sample(x.B * x.H, 40, seed=9) + [7 * 128 + 3, 300 * 128 + 100])))
+
+
 @pytest.mark.parametrize("splits", [0, 35])
 def test_mla_long_context_sampled(splits):
     """Sequences of 131072 and 100000 tokens: the automatic plan (many splits
