@@ -195,9 +195,8 @@ size_t mla_workspace(int64_t rows, int splits) {
 struct MlaFlat {
   int target = 0, slots = 0;
 };
-MlaFlat plan_mla_flat(int32_t B, int32_t H, int64_t cap, int32_t req, int32_t page_size, bool paged) {
+MlaFlat plan_mla_flat(int32_t B, int32_t H, int64_t cap, int32_t req, bool paged) {
   MlaFlat f;
-  (void)page_size;
   if (req != 0 || B > dattn::kMlaFlatMaxB || H % 128 != 0 || paged) return f;
   const int64_t target = std::max<int64_t>(1, dattn::device_cu_count() / (H / 128));
   const int64_t by_cap = (B * cap + dattn::kMlaMaxSplitTokens - 1) / dattn::kMlaMaxSplitTokens;
@@ -691,7 +690,7 @@ size_t decode_attn_mla_workspace(int32_t B, int32_t H, int32_t d_latent, int32_t
   if (splits < 1) return 0;
   // enough for either plan: a paged call keeps the split grid
   const size_t split_bytes = mla_workspace((int64_t)B * H, splits);
-  const MlaFlat f = plan_mla_flat(B, H, S_max, num_splits, 32, false);
+  const MlaFlat f = plan_mla_flat(B, H, S_max, num_splits, false);
   return f.target > 0 ? std::max(split_bytes, mla_flat_workspace(f, B, H)) : split_bytes;
 }
 
@@ -742,7 +741,7 @@ int decode_attn_mla(const void* q_absorbed, const void* latent_cache, const int3
   const int splits = plan.splits;
   if (splits < 1) return fail(DATTN_EUNSUPPORTED, "decode_attn_mla: %lld tokens need more than %d splits",
                               (long long)max_tokens, kMlaMaxSplits);
-  const MlaFlat flat = plan_mla_flat(B, H, max_tokens, num_splits, page_size, page_table != nullptr);
+  const MlaFlat flat = plan_mla_flat(B, H, max_tokens, num_splits, page_table != nullptr);
   const size_t need = flat.target > 0 ? mla_flat_workspace(flat, B, H) : mla_workspace((int64_t)B * H, splits);
   if ((rc = check_workspace(workspace, workspace_bytes, need))) return rc;
   if (debug_on()) {
