@@ -175,6 +175,23 @@ def test_mla_balanced_items_all_empty_and_many_sequences():
         check(x, 0, rows=rows_sample(x.B * x.H, 48, seed=B))
 
 
+def test_mla_balanced_items_without_lse_and_reused_workspace():
+    """A balanced call without lse writes the same output; a workspace reused
+    by a call with other lengths (a different item table) holds no state."""
+    x = wl.make_mla(B=5, H=128, seq_lens=[9000, 5, 0, 3000, 700], seed=53, name="mla_nolse")
+    y = wl.make_mla(B=5, H=128, seq_lens=[100, 9000, 4000, 0, 1], seed=54, name="mla_nolse2")
+    nbytes = api.lib().decode_attn_mla_workspace(5, 128, 512, max(x.S_max, y.S_max), 0)
+    ws = torch.full((nbytes,), 0x7F, dtype=torch.uint8, device="cuda")
+    for m in (x, y):
+        ref, _ = api.decode_attn_mla(dev(m.q), dev(m.latent), dev(m.seq_lens), scale=m.scale, workspace=ws)
+        got, lse = api.decode_attn_mla(dev(m.q), dev(m.latent), dev(m.seq_lens), scale=m.scale, want_lse=False,
+                                       workspace=ws)
+        torch.cuda.synchronize()
+        assert lse is None and torch.equal(got, ref)
+        want, _ = oracle.mla(m.q, m.latent, m.seq_lens, scale=m.scale)
+        assert_rows_close(got.float().cpu().reshape(-1, 512), want, TOL_BF16, m.name)
+
+
 def test_mla_balanced_items_in_several_rounds():
     """512 sequences (the balanced plan's limit) of up to 4000 tokens: items
     are capped at 3840 tokens, so there are about four items per CU and the
